@@ -1,0 +1,216 @@
+"""CPU oracle for paged attention over a quantized KV cache, the MXFP4 paged MQA
+logits and the KV insert.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The GPU library
+(``paged_attention_quantized_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc into
+``liboracle.so``); this module only marshals numpy arrays through ctypes.
+Every function's docstring names the passage of the pages it follows; the C
+source carries the same citations.
+
+Parity-pin status: every function here is pinned by tests under ``-m "not gpu"``
+(see tests/test_oracle_*.py); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+KV_F16, KV_BF16, KV_E4M3, KV_INT8, KV_INT4 = 0, 1, 2, 3, 4
+SCALE_NONE, SCALE_PER_TENSOR, SCALE_PER_CHANNEL = 0, 1, 2
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (ISO C11, no FP contraction)."""
+    subprocess.run(["gcc", *CFLAGS, src, "-o", out, "-lm"], check=True)
+    return out
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load liboracle.so, building it first if it is not there."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_f16_to_f32.restype = f32
+    lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_to_f32.restype = f32
+    lib.orc_f64_to_f16.argtypes = [ctypes.c_double]
+    lib.orc_f64_to_f16.restype = ctypes.c_uint16
+    lib.orc_f32_to_bf16.argtypes = [f32]
+    lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+    lib.orc_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_to_f32.restype = f32
+    lib.orc_f32_to_e4m3.argtypes = [f32]
+    lib.orc_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.orc_round_clamp.argtypes = [f32, i32]
+    lib.orc_round_clamp.restype = i32
+    lib.orc_int4_value.argtypes = [i32]
+    lib.orc_int4_value.restype = i32
+    lib.orc_e2m1_to_f32.argtypes = [ctypes.c_uint8]
+    lib.orc_e2m1_to_f32.restype = f32
+    lib.orc_ue8m0_to_f32.argtypes = [ctypes.c_uint8]
+    lib.orc_ue8m0_to_f32.restype = f32
+    lib.orc_dequantize.argtypes = [i32, P, i64, P, i32, i64, P]
+    lib.orc_dequantize.restype = None
+    lib.orc_paged_attn.argtypes = [P, P, P, P, i32, P, i32, P, i32, P, P,
+                                   i32, i32, i32, i32, i32, i32, i64, i32, f32, i32]
+    lib.orc_paged_attn.restype = i32
+    lib.orc_mqa_logits.argtypes = [P, i64, P, P, P, P, P, P,
+                                   i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.orc_mqa_logits.restype = i32
+    lib.orc_kv_insert.argtypes = [P, P, i32, P, P, i32, P, i64, i64,
+                                  i32, i32, i32, i64, P, i32, P, i32]
+    lib.orc_kv_insert.restype = i32
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _bits16(a):
+    """fp16 / bf16 arrays may arrive as float16 or as raw uint16 bits."""
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# codecs (vectorised over numpy arrays by calling the scalar C routines)
+# ---------------------------------------------------------------------------
+
+def e4m3_to_f32(codes, lib=None):
+    lib = lib or load()
+    return np.array([lib.orc_e4m3_to_f32(int(c)) for c in np.ravel(codes)],
+                    dtype=np.float32).reshape(np.shape(codes))
+
+
+def f32_to_e4m3(x, lib=None):
+    lib = lib or load()
+    return np.array([lib.orc_f32_to_e4m3(float(v)) for v in np.ravel(np.float32(x))],
+                    dtype=np.uint8).reshape(np.shape(x))
+
+
+def f64_to_f16(x, lib=None):
+    lib = lib or load()
+    return np.array([lib.orc_f64_to_f16(float(v)) for v in np.ravel(x)],
+                    dtype=np.uint16).reshape(np.shape(x)).view(np.float16)
+
+
+def dequantize(kind, codes, n, scale=None, mode=SCALE_NONE, channels=1, lib=None):
+    """Element-wise dequantization of a flat code array: fp32(code) * fp32(scale)."""
+    lib = lib or load()
+    codes = np.ascontiguousarray(codes).view(np.uint8)
+    scale = _c(scale if scale is not None else np.ones(1, np.float32), np.float32)
+    out = np.empty(n, np.float32)
+    lib.orc_dequantize(kind, _ptr(codes), n, _ptr(scale), mode, channels, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the three operations
+# ---------------------------------------------------------------------------
+
+def paged_attn(q, k_cache, v_cache, kv_kind, block_table, context_lens, *,
+               k_scale=None, k_scale_mode=SCALE_NONE, v_scale=None, v_scale_mode=SCALE_NONE,
+               num_kv_heads, head_dim, block_size, softmax_scale, causal=True, lib=None):
+    """Reference paged attention (see orc_paged_attn in oracle.c).
+
+    q: [B, next_n, Hq, D] fp16 (or its uint16 bits); caches: uint8/fp16 arrays of shape
+    [num_blocks, block_size, Hkv, D_bytes]. Returns float64 [B, next_n, Hq, D].
+    """
+    lib = lib or load()
+    q16 = _bits16(q)
+    B, next_n, Hq, D = q16.shape
+    assert D == head_dim
+    kc = np.ascontiguousarray(k_cache).view(np.uint8)
+    vc = np.ascontiguousarray(v_cache).view(np.uint8)
+    num_blocks = k_cache.shape[0]
+    bt = _c(block_table, np.int32)
+    cl = _c(context_lens, np.int32)
+    ks = _c(k_scale if k_scale is not None else np.ones(1, np.float32), np.float32)
+    vs = _c(v_scale if v_scale is not None else np.ones(1, np.float32), np.float32)
+    out = np.empty((B, next_n, Hq, D), np.float64)
+    rc = lib.orc_paged_attn(_ptr(out), _ptr(q16), _ptr(kc), _ptr(vc), kv_kind,
+                            _ptr(ks), k_scale_mode, _ptr(vs), v_scale_mode, _ptr(bt), _ptr(cl),
+                            B, next_n, Hq, num_kv_heads, D, block_size, num_blocks,
+                            bt.shape[1], float(softmax_scale), int(causal))
+    if rc != 0:
+        raise ValueError(f"orc_paged_attn failed with code {rc}")
+    return out
+
+
+def mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len, *,
+               sf_vec_size=32, out_rows=None, out_row_stride=None, lib=None):
+    """Reference MXFP4 paged MQA logits (see orc_mqa_logits in oracle.c).
+
+    q: uint8 [B, next_n, H, D/2]; sf_q: int32 [B, next_n, H]; kv_fused: uint8
+    [num_blocks, bs, 1, D/2 + D/sf_vec]; weights: fp32 [B*next_n, H].
+    Returns fp32 [B*next_n, max_context_len] (or [out_rows, out_row_stride]).
+    """
+    lib = lib or load()
+    q = np.ascontiguousarray(q, np.uint8)
+    B, next_n, H, Dh = q.shape
+    D = Dh * 2
+    bs = kv_fused.shape[1]
+    bt = _c(block_table, np.int32)
+    cl = _c(context_lens, np.int32)
+    sfq = _c(sf_q, np.int32)
+    w = _c(weights, np.float32)
+    kv = np.ascontiguousarray(kv_fused, np.uint8)
+    stride = out_row_stride or max_context_len
+    rows = out_rows or B * next_n
+    out = np.full((rows, stride), np.nan, np.float32)
+    rc = lib.orc_mqa_logits(_ptr(out), stride, _ptr(q), _ptr(sfq), _ptr(kv), _ptr(w), _ptr(cl),
+                            _ptr(bt), B, next_n, H, D, bs, bt.shape[1], max_context_len,
+                            sf_vec_size)
+    if rc != 0:
+        raise ValueError(f"orc_mqa_logits failed with code {rc}")
+    return out
+
+
+def kv_insert(k_cache, v_cache, kv_kind, k, v, slot_mapping, *, k_scale=None,
+              k_scale_mode=SCALE_NONE, v_scale=None, v_scale_mode=SCALE_NONE, in_is_bf16=False,
+              block_size, lib=None):
+    """Reference KV insert (see orc_kv_insert in oracle.c). Writes the caches in place."""
+    lib = lib or load()
+    assert k_cache.flags["C_CONTIGUOUS"] and v_cache.flags["C_CONTIGUOUS"]
+    k16, v16 = _bits16(k), _bits16(v)
+    T, Hkv, D = k16.shape
+    sm = _c(slot_mapping, np.int64)
+    ks = _c(k_scale if k_scale is not None else np.ones(1, np.float32), np.float32)
+    vs = _c(v_scale if v_scale is not None else np.ones(1, np.float32), np.float32)
+    rc = lib.orc_kv_insert(k_cache.ctypes.data, v_cache.ctypes.data, kv_kind, _ptr(k16),
+                           _ptr(v16), int(in_is_bf16), _ptr(sm), T, sm.shape[0], Hkv, D,
+                           block_size, k_cache.shape[0], _ptr(ks), k_scale_mode, _ptr(vs),
+                           v_scale_mode)
+    if rc != 0:
+        raise ValueError(f"orc_kv_insert failed with code {rc}")

@@ -1,0 +1,440 @@
+/*
+ * oracle.c -- plain CPU reference for paged attention over a quantized,
+ * block-table-indexed KV cache, the MXFP4 paged MQA logits, and the KV insert.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. The GPU library shares no code,
+ * header, table or helper with it, and neither links the other.
+ *
+ * It is deliberately slow and literal: every value is decoded from its bit
+ * fields by the format's definition, every token is looked up through the
+ * block table one at a time, and sums run in ascending index order.
+ *
+ * Precision. A dequantized cache value is fp32(code) * fp32(scale), one fp32
+ * rounding, which is what the per-channel scale page ("Normalize the
+ * PER_CHANNEL K scale folded into Q for paged XQA", Description) calls the
+ * portable FP32 product. Attention sums (q.k, the softmax denominator and the
+ * weighted sum of V) are accumulated in double, so the reference error is far
+ * below the fp16 output tolerance. The MQA logits follow the fp32 contract of
+ * the fp4_paged_mqa_logits API page (float32 weights and output): per-head
+ * dot products in fp32, then an fmaf chain over heads in ascending order.
+ *
+ * Sources (each function cites the passage it follows):
+ *  [P1] "Stop grouped-page4 null-block padding from leaking E4M3 NaN"
+ *  [P2] "Normalize the PER_CHANNEL K scale folded into Q for paged XQA"
+ *  [P4] "DeepSeek-V4.1 Q pad + fused KV insert" (the KV-only insert path)
+ *  [P5] "flashinfer.fp4_paged_mqa_logits" API documentation
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_KV_F16 0
+#define ORC_KV_BF16 1
+#define ORC_KV_E4M3 2
+#define ORC_KV_INT8 3
+#define ORC_KV_INT4 4
+
+#define ORC_SCALE_NONE 0
+#define ORC_SCALE_PER_TENSOR 1
+#define ORC_SCALE_PER_CHANNEL 2
+
+/* ------------------------------------------------------------------ */
+/* Scalar codecs                                                       */
+/* ------------------------------------------------------------------ */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+float orc_f16_to_f32(uint16_t h) {
+  int s = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp(1024.0 + f, e - 25);
+  return (float)(s ? -v : v);
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+float orc_bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Round a double to binary16, round-to-nearest-even, overflow to infinity. */
+uint16_t orc_f64_to_f16(double x) {
+  if (isnan(x)) return 0x7E00;
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  int e2;
+  frexp(a, &e2);          /* a lies in [2^(e2-1), 2^e2) */
+  int lead = e2 - 1;
+  if (lead < -14) lead = -14; /* subnormal range: spacing 2^-24 */
+  double quantum = ldexp(1.0, lead - 10);
+  double r = nearbyint(a / quantum) * quantum; /* default rounding mode: ties to even */
+  if (r > 65504.0) return sign | 0x7C00;
+  if (r < ldexp(1.0, -14)) return sign | (uint16_t)(r / ldexp(1.0, -24));
+  int er;
+  frexp(r, &er);
+  int exp_field = er - 1 + 15;
+  double frac = r / ldexp(1.0, er - 1) - 1.0; /* in [0, 1) */
+  return sign | (uint16_t)(exp_field << 10) | (uint16_t)(frac * 1024.0);
+}
+
+/* Round a float to bfloat16, round-to-nearest-even (NaN kept quiet). */
+uint16_t orc_f32_to_bf16(float x) {
+  if (isnan(x)) return 0x7FC0;
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  uint32_t keep = u >> 16, rest = u & 0xFFFF;
+  if (rest > 0x8000 || (rest == 0x8000 && (keep & 1))) keep += 1;
+  return (uint16_t)keep;
+}
+
+/* OCP FP8 E4M3 ("FN"): 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinity; 0x7F and 0xFF are NaN [P1, Root cause: NaN bytes 0x7F/0xFF];
+ * largest finite magnitude 448 (code 0x7E). */
+float orc_e4m3_to_f32(uint8_t c) {
+  int s = (c >> 7) & 1;
+  int e = (c >> 3) & 15;
+  int m = c & 7;
+  float v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexpf((float)m, -9); /* (m/8) * 2^-6 */
+  else
+    v = ldexpf(8.0f + (float)m, e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+/* Nearest E4M3 code, ties to the even code, saturating to +-448; NaN -> 0x7F.
+ * Found by scanning all finite non-negative codes: slow and obviously right. */
+uint8_t orc_f32_to_e4m3(float x) {
+  if (isnan(x)) return 0x7F;
+  uint8_t sign = signbit(x) ? 0x80 : 0;
+  double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E;
+  int best = 0;
+  double bestd = a;
+  for (int c = 1; c <= 0x7E; ++c) {
+    double d = fabs((double)orc_e4m3_to_f32((uint8_t)c) - a);
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return sign | (uint8_t)best;
+}
+
+/* Signed INT8 and INT4 codes: symmetric round-to-nearest-even with clamps
+ * +-127 and +-7, the "/127" and "/7" scale ranges of [P2, Description]. */
+int orc_round_clamp(float y, int lim) {
+  if (isnan(y)) return 0;
+  float r = nearbyintf(y);
+  if (r > (float)lim) r = (float)lim;
+  if (r < (float)-lim) r = (float)-lim;
+  return (int)r;
+}
+
+/* INT4 nibble (two's complement, 4 bits) -> integer in [-8, 7]. */
+int orc_int4_value(int nib) { return nib >= 8 ? nib - 16 : nib; }
+
+/* OCP E2M1 (FP4): 1 sign, 2 exponent (bias 1), 1 mantissa bit. */
+float orc_e2m1_to_f32(uint8_t nib) {
+  int s = (nib >> 3) & 1;
+  int e = (nib >> 1) & 3;
+  int m = nib & 1;
+  float v = (e == 0) ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+  return s ? -v : v;
+}
+
+/* OCP UE8M0 scale factor: 2^(e - 127); 0xFF is NaN. */
+float orc_ue8m0_to_f32(uint8_t e) {
+  if (e == 0xFF) return NAN;
+  return ldexpf(1.0f, (int)e - 127);
+}
+
+/* ------------------------------------------------------------------ */
+/* Paged KV element access                                             */
+/* ------------------------------------------------------------------ */
+
+static int elem_bits(int kind) {
+  if (kind == ORC_KV_F16 || kind == ORC_KV_BF16) return 16;
+  if (kind == ORC_KV_INT4) return 4;
+  return 8;
+}
+
+/* Code value of element (slot, head, d) of physical block blk, as a float.
+ * The cache is [num_blocks, block_size, kv_heads, head_dim] [P5, kv_fused /
+ * block_table parameters]; INT4 keeps element 2j in the low nibble. */
+static float cache_code(const uint8_t* cache, int kind, int64_t blk, int slot, int hk, int d,
+                        int bs, int Hkv, int D) {
+  int64_t row = (blk * bs + slot) * Hkv + hk;
+  int64_t row_bytes = (int64_t)D * elem_bits(kind) / 8;
+  const uint8_t* p = cache + row * row_bytes;
+  if (kind == ORC_KV_F16) {
+    uint16_t h;
+    memcpy(&h, p + 2 * d, 2);
+    return orc_f16_to_f32(h);
+  }
+  if (kind == ORC_KV_BF16) {
+    uint16_t h;
+    memcpy(&h, p + 2 * d, 2);
+    return orc_bf16_to_f32(h);
+  }
+  if (kind == ORC_KV_E4M3) return orc_e4m3_to_f32(p[d]);
+  if (kind == ORC_KV_INT8) return (float)(int8_t)p[d];
+  {
+    uint8_t byte = p[d / 2];
+    int nib = (d % 2 == 0) ? (byte & 15) : (byte >> 4);
+    return (float)orc_int4_value(nib);
+  }
+}
+
+static float scale_of(const float* scale, int mode, int hk, int d, int D) {
+  if (mode == ORC_SCALE_PER_TENSOR) return scale[0];
+  if (mode == ORC_SCALE_PER_CHANNEL) return scale[hk * D + d];
+  return 1.0f;
+}
+
+/* Dequantized value: fp32(code) * fp32(scale), one rounding [P2, Description:
+ * the portable kernel keeps the q*k_scale product in FP32]. */
+static float deq(const uint8_t* cache, int kind, const float* scale, int mode, int64_t blk,
+                 int slot, int hk, int d, int bs, int Hkv, int D) {
+  return cache_code(cache, kind, blk, slot, hk, d, bs, Hkv, D) * scale_of(scale, mode, hk, d, D);
+}
+
+/* Element-wise decode of a flat code array (the dequantization probe):
+ * element i uses scale[i % channels] per channel, scale[0] per tensor. */
+void orc_dequantize(int kind, const uint8_t* codes, int64_t n, const float* scale, int mode,
+                    int64_t channels, float* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    float code;
+    if (kind == ORC_KV_E4M3)
+      code = orc_e4m3_to_f32(codes[i]);
+    else if (kind == ORC_KV_INT8)
+      code = (float)(int8_t)codes[i];
+    else if (kind == ORC_KV_INT4) {
+      uint8_t byte = codes[i / 2];
+      code = (float)orc_int4_value((i % 2 == 0) ? (byte & 15) : (byte >> 4));
+    } else {
+      uint16_t h;
+      memcpy(&h, codes + 2 * i, 2);
+      code = (kind == ORC_KV_F16) ? orc_f16_to_f32(h) : orc_bf16_to_f32(h);
+    }
+    float s = 1.0f;
+    if (mode == ORC_SCALE_PER_TENSOR) s = scale[0];
+    if (mode == ORC_SCALE_PER_CHANNEL) s = scale[i % channels];
+    out[i] = code * s;
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Paged attention                                                     */
+/* ------------------------------------------------------------------ */
+
+/*
+ * out[b, i, h, :] = softmax(softmax_scale * q[b,i,h,:] . K_t) @ V_t over the
+ * visible tokens t of sequence b, dequantize first [P2, Description: portable
+ * path], read through block_table [P5, block_table parameter].
+ *
+ * Readings where the pages are silent:
+ *  - q and out are [B, next_n, Hq, D]; query head h reads KV head
+ *    h / (Hq / Hkv) (contiguous groups).
+ *  - Query row i sits at absolute position L_b - next_n + i; with causal set
+ *    it sees tokens t <= that position, otherwise all t < L_b.
+ *  - No visible token: the output row is +0.
+ *  - Tokens that are not visible are never read, so the null block (physical
+ *    block 0 [P1, Root cause]) and tail slots cannot influence the result. A
+ *    visible token mapped to block 0 is a harness error (returns -1).
+ *
+ * Scores, softmax and the weighted sum are accumulated in double; `out` is
+ * the double result (the caller rounds to its output dtype).
+ */
+int orc_paged_attn(double* out, const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                   int kv_kind, const float* k_scale, int k_scale_mode, const float* v_scale,
+                   int v_scale_mode, const int32_t* block_table, const int32_t* context_lens, int B,
+                   int next_n, int Hq, int Hkv, int D, int bs, int64_t num_blocks, int max_blocks,
+                   float softmax_scale, int causal) {
+  int group = Hq / Hkv;
+  int max_len = max_blocks * bs;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+  int rc = 0;
+  for (int b = 0; b < B; ++b) {
+    int L = context_lens[b];
+    for (int i = 0; i < next_n; ++i) {
+      int pos = L - next_n + i;
+      int nvis = L;
+      if (causal && pos + 1 < nvis) nvis = pos + 1;
+      if (nvis < 0) nvis = 0;
+      if (nvis > max_len) { rc = -2; goto done; }
+      for (int h = 0; h < Hq; ++h) {
+        int hk = h / group;
+        const uint16_t* qrow = q + (((int64_t)b * next_n + i) * Hq + h) * D;
+        double* orow = out + (((int64_t)b * next_n + i) * Hq + h) * D;
+        for (int d = 0; d < D; ++d) orow[d] = 0.0;
+        if (nvis == 0) continue;
+        double m = -INFINITY;
+        for (int t = 0; t < nvis; ++t) {
+          int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
+          int slot = t % bs;
+          if (blk <= 0 || blk >= num_blocks) { rc = -1; goto done; }
+          double acc = 0.0;
+          for (int d = 0; d < D; ++d) {
+            float kv = deq(k_cache, kv_kind, k_scale, k_scale_mode, blk, slot, hk, d, bs, Hkv, D);
+            acc += (double)orc_f16_to_f32(qrow[d]) * (double)kv;
+          }
+          s[t] = (double)softmax_scale * acc;
+          if (s[t] > m) m = s[t];
+        }
+        double l = 0.0;
+        for (int t = 0; t < nvis; ++t) {
+          s[t] = exp(s[t] - m);
+          l += s[t];
+        }
+        for (int t = 0; t < nvis; ++t) {
+          int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
+          int slot = t % bs;
+          for (int d = 0; d < D; ++d) {
+            float vv = deq(v_cache, kv_kind, v_scale, v_scale_mode, blk, slot, hk, d, bs, Hkv, D);
+            orow[d] += s[t] * (double)vv;
+          }
+        }
+        for (int d = 0; d < D; ++d) orow[d] /= l;
+      }
+    }
+  }
+done:
+  free(s);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 paged MQA logits [P5]                                         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * out[b*next_n + i, t] = sum over heads h (ascending, fp32 fmaf chain from +0)
+ *   of weights[b*next_n + i, h] * S_h, with
+ *   S_h = sum over d (ascending, fp32) of deq(q[b,i,h,d]) * deq(k_t[d]),
+ * for t < context_lens[b]; -inf for context_lens[b] <= t < max_context_len.
+ *
+ * Layouts from the API page: q [B, next_n, H, D/2] two E2M1 per byte; sf_q
+ * [B, next_n, H] int32 holding D/sf_vec UE8M0 bytes; kv_fused
+ * [num_blocks, bs, 1, D/2 + D/sf_vec] where each block stores all tokens' FP4
+ * data first and then all tokens' scale bytes in token order; weights
+ * [B*next_n, H] fp32. Readings: element 2j is the low nibble; byte g of the
+ * int32 (bits 8g..8g+7) scales elements [g*sf_vec, (g+1)*sf_vec); there is no
+ * activation between the dot product and the weight.
+ */
+int orc_mqa_logits(float* out, int64_t out_row_stride, const uint8_t* q, const int32_t* sf_q,
+                   const uint8_t* kv_fused, const float* weights, const int32_t* context_lens,
+                   const int32_t* block_table, int B, int next_n, int H, int D, int bs,
+                   int max_blocks, int max_context_len, int sf_vec) {
+  int row_bytes = D / 2 + D / sf_vec;
+  for (int b = 0; b < B; ++b) {
+    int L = context_lens[b];
+    if (L > max_context_len || L > max_blocks * bs) return -2;
+    for (int i = 0; i < next_n; ++i) {
+      int64_t r = (int64_t)b * next_n + i;
+      float* orow = out + r * out_row_stride;
+      for (int t = 0; t < L; ++t) {
+        int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
+        int slot = t % bs;
+        const uint8_t* base = kv_fused + blk * (int64_t)bs * row_bytes;
+        const uint8_t* kdata = base + (int64_t)slot * (D / 2);
+        const uint8_t* ksf = base + (int64_t)bs * (D / 2) + (int64_t)slot * (D / sf_vec);
+        float acc = 0.0f;
+        for (int h = 0; h < H; ++h) {
+          const uint8_t* qd = q + (r * H + h) * (D / 2);
+          uint32_t qsf = (uint32_t)sf_q[r * H + h];
+          float sh = 0.0f;
+          for (int d = 0; d < D; ++d) {
+            int g = d / sf_vec;
+            uint8_t qb = qd[d / 2], kb = kdata[d / 2];
+            float qv = orc_e2m1_to_f32((d % 2 == 0) ? (qb & 15) : (qb >> 4)) *
+                       orc_ue8m0_to_f32((uint8_t)((qsf >> (8 * g)) & 0xFF));
+            float kv = orc_e2m1_to_f32((d % 2 == 0) ? (kb & 15) : (kb >> 4)) *
+                       orc_ue8m0_to_f32(ksf[g]);
+            sh += qv * kv;
+          }
+          acc = fmaf(weights[r * H + h], sh, acc);
+        }
+        orow[t] = acc;
+      }
+      for (int t = L; t < max_context_len; ++t) orow[t] = -INFINITY;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* KV insert [P4]                                                      */
+/* ------------------------------------------------------------------ */
+
+static float in_value(const uint16_t* x, int in_is_bf16, int64_t idx) {
+  return in_is_bf16 ? orc_bf16_to_f32(x[idx]) : orc_f16_to_f32(x[idx]);
+}
+
+static void store_code(uint8_t* cache, int kind, int64_t blk, int off, int hk, int d, int bs,
+                       int Hkv, int D, float x, float scale, uint16_t raw_bits) {
+  int64_t row = (blk * bs + off) * Hkv + hk;
+  int64_t row_bytes = (int64_t)D * elem_bits(kind) / 8;
+  uint8_t* p = cache + row * row_bytes;
+  if (kind == ORC_KV_F16 || kind == ORC_KV_BF16) {
+    memcpy(p + 2 * d, &raw_bits, 2);
+    return;
+  }
+  float y = x / scale; /* IEEE fp32 division */
+  if (kind == ORC_KV_E4M3) {
+    p[d] = orc_f32_to_e4m3(y);
+  } else if (kind == ORC_KV_INT8) {
+    p[d] = (uint8_t)(int8_t)orc_round_clamp(y, 127);
+  } else {
+    int nib = orc_round_clamp(y, 7) & 15;
+    if (d % 2 == 0)
+      p[d / 2] = (uint8_t)((p[d / 2] & 0xF0) | nib);
+    else
+      p[d / 2] = (uint8_t)((p[d / 2] & 0x0F) | (nib << 4));
+  }
+}
+
+/*
+ * Write rows k[i], v[i] ([T, Hkv, D]) of new tokens into the paged caches at
+ * slot_mapping[i] (block = slot / bs, offset = slot % bs). Rows with
+ * i >= num_slots or slot < 0 have no slot and are skipped, as the KV-only
+ * insert skips padding rows that have no slot [P4, Design]. Codes: E4M3
+ * nearest-even saturating, INT8/INT4 nearest-even clamped to +-127 / +-7,
+ * computed from x / scale in fp32. F16/BF16 caches store the input bits
+ * unchanged and require the matching input dtype.
+ */
+int orc_kv_insert(uint8_t* k_cache, uint8_t* v_cache, int kv_kind, const uint16_t* k,
+                  const uint16_t* v, int in_is_bf16, const int64_t* slot_mapping, int64_t T,
+                  int64_t num_slots, int Hkv, int D, int bs, int64_t num_blocks,
+                  const float* k_scale, int k_scale_mode, const float* v_scale, int v_scale_mode) {
+  for (int64_t i = 0; i < T; ++i) {
+    if (i >= num_slots) continue;
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    int64_t blk = slot / bs;
+    int off = (int)(slot % bs);
+    if (blk >= num_blocks) return -1;
+    for (int hk = 0; hk < Hkv; ++hk) {
+      for (int d = 0; d < D; ++d) {
+        int64_t idx = (i * Hkv + hk) * D + d;
+        store_code(k_cache, kv_kind, blk, off, hk, d, bs, Hkv, D, in_value(k, in_is_bf16, idx),
+                   scale_of(k_scale, k_scale_mode, hk, d, D), k[idx]);
+        store_code(v_cache, kv_kind, blk, off, hk, d, bs, Hkv, D, in_value(v, in_is_bf16, idx),
+                   scale_of(v_scale, v_scale_mode, hk, d, D), v[idx]);
+      }
+    }
+  }
+  return 0;
+}

@@ -1,0 +1,98 @@
+"""Planted mistakes: each mutation below is a plausible slip in the oracle (a
+dropped term, a wrong sign, index, bias or rounding rule, a transposed
+operand). The test copies oracle.c, applies one mutation, builds the copy on
+the CPU and runs the pins against it; at least one pin must fail. This shows
+the pins constrain every part of the oracle rather than restating it.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import test_oracle_attn, test_oracle_insert, test_oracle_logits
+
+
+def pin_codec_e4m3(lib):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_to_f32(codes, lib)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    vals = ref[:0x7E].astype(np.float64)
+    x = np.concatenate([((vals[:-1] + vals[1:]) / 2), np.linspace(-460, 460, 3001)]).astype(
+        np.float32)
+    enc = oracle.f32_to_e4m3(x, lib)
+    want = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(enc, want.numpy())
+
+
+def pin_codec_round(lib):
+    y = [2.5, 3.5, -2.5, 0.5, 1.5, 126.5, 200.0, -9.0]
+    for lim in (127, 7):
+        assert [lib.orc_round_clamp(v, lim) for v in y] == \
+            np.clip(np.rint(np.float32(y)), -lim, lim).astype(int).tolist()
+
+
+PINS = ([pin_codec_e4m3, pin_codec_round] + test_oracle_attn.ALL_PINS +
+        test_oracle_logits.ALL_PINS + test_oracle_insert.ALL_PINS)
+
+MUTATIONS = {
+    "gqa_head_map": ("int hk = h / group;", "int hk = h % Hkv;"),
+    "causal_off_by_one": ("if (causal && pos + 1 < nvis) nvis = pos + 1;",
+                          "if (causal && pos < nvis) nvis = pos;"),
+    "softmax_sign": ("s[t] = exp(s[t] - m);", "s[t] = exp(m - s[t]);"),
+    "dropped_normalizer": ("for (int d = 0; d < D; ++d) orow[d] /= l;", ""),
+    "dropped_softmax_scale": ("s[t] = (double)softmax_scale * acc;", "s[t] = acc;"),
+    # reads the [Hkv, D] scale as [D, Hkv]; every per-channel pin uses Hkv = 2, so it stays
+    # in bounds
+    "per_channel_transposed": ("if (mode == ORC_SCALE_PER_CHANNEL) return scale[hk * D + d];",
+                               "if (mode == ORC_SCALE_PER_CHANNEL) return scale[d * 2 + hk];"),
+    "e4m3_bias": ("v = ldexpf(8.0f + (float)m, e - 10);", "v = ldexpf(8.0f + (float)m, e - 9);"),
+    "e4m3_ties_up": ("(d == bestd && (c & 1) == 0)", "(d == bestd)"),
+    "int4_nibble_order": ("int nib = (d % 2 == 0) ? (byte & 15) : (byte >> 4);\n    return",
+                          "int nib = (d % 2 == 0) ? (byte >> 4) : (byte & 15);\n    return"),
+    "v_slot_index": ("int slot = t % bs;\n          for (int d = 0; d < D; ++d) {\n"
+                     "            float vv",
+                     "int slot = (t + 1) % bs;\n          for (int d = 0; d < D; ++d) {\n"
+                     "            float vv"),
+    "f16_exponent": ("v = ldexp(1024.0 + f, e - 25);", "v = ldexp(1024.0 + f, e - 24);"),
+    "int_round_away": ("float r = nearbyintf(y);", "float r = roundf(y);"),
+    "logits_weight_row": ("acc = fmaf(weights[r * H + h], sh, acc);",
+                          "acc = fmaf(weights[h], sh, acc);"),
+    "logits_sf_offset": ("const uint8_t* ksf = base + (int64_t)bs * (D / 2) + "
+                         "(int64_t)slot * (D / sf_vec);",
+                         "const uint8_t* ksf = base + (int64_t)slot * (D / sf_vec);"),
+    "logits_tail_zero": ("orow[t] = -INFINITY;", "orow[t] = 0.0f;"),
+    "logits_q_scale_byte": ("((qsf >> (8 * g)) & 0xFF)", "((qsf >> (8 * (3 - g))) & 0xFF)"),
+    "insert_offset": ("int off = (int)(slot % bs);", "int off = (int)(slot % bs) ^ 1;"),
+}
+
+
+def test_unmutated_passes_all_pins(orc):
+    for pin in PINS:
+        pin(orc)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / "oracle_mut.c"
+    path.write_text(src.replace(old, new))
+    so = str(tmp_path / "liboracle_mut.so")
+    subprocess.run(["gcc", *oracle.CFLAGS, str(path), "-o", so, "-lm"], check=True)
+    lib = oracle.load(so)
+    failures = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(lib)
+        except (AssertionError, ValueError):  # ValueError: the oracle rejected its input
+            failures.append(pin.__name__)
+            break
+    assert failures, f"no pin caught the planted mistake {name}"
