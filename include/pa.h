@@ -1,0 +1,266 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged attention over a quantized, block-table
+ * indexed KV cache, MXFP4 paged MQA logits, and the paged KV insert, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers inside the argument structs, `workspace` and the buffers of
+ *    pa_dequantize are DEVICE memory owned by the caller. The structs
+ *    themselves are host memory and are only read during the call.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on it: no allocation, no free, no host synchronisation,
+ *    no read of device data by the host. Calls may be captured into a HIP
+ *    graph.
+ *  - Errors are returned as pa_status; nothing is enqueued when a call
+ *    returns an error. pa_last_error() gives a message for the calling
+ *    thread's last non-OK status.
+ *  - Host-side checks (shapes, kinds, sizes) always run. Conditions that
+ *    depend on device data (context lengths within max_context_len, block
+ *    ids within num_blocks) are the caller's preconditions, as on the
+ *    fp4_paged_mqa_logits API page (block_table / max_context_len
+ *    parameters): violating them is undefined behaviour.
+ *
+ * Sources (titles of the pages these operations come from):
+ *  [NULLPAD] "Stop grouped-page4 null-block padding from leaking E4M3 NaN"
+ *  [FOLD]    "Normalize the PER_CHANNEL K scale folded into Q for paged XQA"
+ *  [RELOC]   "Stabilize QSA page4 order under KV relocation"
+ *  [INSERT]  "DeepSeek-V4.1 Q pad + fused KV insert" (the KV-only insert path)
+ *  [FP4API]  "flashinfer.fp4_paged_mqa_logits" API documentation
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* a null pointer, a negative or inconsistent size */
+  PA_ERR_UNSUPPORTED = 2,  /* valid, but a shape/kind this build has no kernel for */
+  PA_ERR_PRECONDITION = 3, /* a documented precondition checked on the host failed */
+  PA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than *_workspace_size() */
+  PA_ERR_HIP = 5           /* a HIP launch failed */
+} pa_status;
+
+typedef enum { PA_DT_F16 = 0, PA_DT_BF16 = 1, PA_DT_F32 = 2 } pa_dtype;
+
+/* KV cache element kinds. E4M3 is OCP FP8 E4M3FN (bytes 0x7F/0xFF are NaN,
+ * largest finite 448) [NULLPAD, Root cause]. INT8 is two's complement. INT4
+ * packs two signed nibbles per byte, element 2j in the low nibble [FOLD,
+ * Description: INT4 scale max|K|/7, INT8 max|K|/127]. */
+typedef enum {
+  PA_KV_F16 = 0,
+  PA_KV_BF16 = 1,
+  PA_KV_E4M3 = 2,
+  PA_KV_INT8 = 3,
+  PA_KV_INT4 = 4
+} pa_kv_kind;
+
+/* Scale of a cache plane: none (codes are values), one fp32 for the whole
+ * tensor, or one fp32 per channel with shape [num_kv_heads, head_dim]
+ * [FOLD, Cost: "1024 floats at H256"]. A dequantized value is
+ * fp32(code) * scale. */
+typedef enum {
+  PA_SCALE_NONE = 0,
+  PA_SCALE_PER_TENSOR = 1,
+  PA_SCALE_PER_CHANNEL = 2
+} pa_scale_mode;
+
+/* ------------------------------------------------------------------------ */
+/* paged_attn_fwd                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * out[b, i, h, :] = softmax(softmax_scale * q[b,i,h,:] . K_t) V_t over the
+ * tokens t visible to query row i of sequence b, with K_t, V_t read through
+ * block_table and dequantized. Decode is next_n = 1; multi-row verify /
+ * short prefill is next_n > 1, where row i sits at position
+ * context_lens[b] - next_n + i and, with `causal`, sees tokens t <= that
+ * position.
+ *
+ * Layouts (all row-major, device memory):
+ *   q, out       [batch, next_n, num_q_heads, head_dim]  fp16 (q_dtype = PA_DT_F16)
+ *   k_cache,
+ *   v_cache      [num_blocks, block_size, num_kv_heads, row_bytes], row_bytes =
+ *                head_dim * 2 (F16/BF16), head_dim (E4M3/INT8), head_dim / 2 (INT4)
+ *   k_scale,
+ *   v_scale      NULL (PA_SCALE_NONE), [1] or [num_kv_heads, head_dim] fp32
+ *   block_table  [batch, max_blocks_per_seq] int32, physical block ids in
+ *                logical order [FP4API, block_table parameter]
+ *   context_lens [batch] int32, each in [0, max_context_len]
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Guarantees:
+ *  - Only blocks holding visible tokens are read. Block 0 serves as the null
+ *    block for table padding and is never read through padding entries;
+ *    tail slots past a sequence's length are neutralised by select, so NaN
+ *    bytes there cannot reach the output [NULLPAD, Fix].
+ *  - A PER_CHANNEL K scale is folded into q as q * (k_scale / max|k_scale|)
+ *    and max|k_scale| is applied to the scores once [FOLD, Approach]; no
+ *    fp16 overflow can turn into inf * 0.
+ *  - The reduction over tokens runs in logical token order and its split
+ *    points depend only on shapes, so the output is bit-identical under any
+ *    physical relocation of pages [RELOC, Summary].
+ *  - A row with no visible token outputs +0.
+ *
+ * softmax_scale: 0 selects 1/sqrt(head_dim); otherwise it must be > 0.
+ * Supported: head_dim 64/128/256 (INT4: 128/256), block_size 16/32,
+ * num_q_heads / num_kv_heads * next_n <= 64, q_dtype F16; KV kinds F16, E4M3,
+ * INT8, INT4. Workspace: paged_attn_workspace_size(a) bytes, 256-byte aligned.
+ */
+typedef struct pa_attn_args {
+  void* out;
+  const void* q;
+  pa_dtype q_dtype;
+  const void* k_cache;
+  const void* v_cache;
+  pa_kv_kind kv_kind;
+  const float* k_scale;
+  pa_scale_mode k_scale_mode;
+  const float* v_scale;
+  pa_scale_mode v_scale_mode;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int32_t max_context_len;
+  int32_t batch;
+  int32_t next_n;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  float softmax_scale;
+  int32_t causal;
+} pa_attn_args;
+
+size_t paged_attn_workspace_size(const pa_attn_args* a);
+pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Test probe of the planner: writes the page-entry list the attention kernel
+ * walks. Work units are (b, split); entries of unit (b, s) are
+ * entries[((b * nsplit + s) * entries_per_unit + e) * 3 + {0,1,2}] =
+ * {physical block, logical block, token mask}, in ascending logical order,
+ * padded to a multiple of 8 with {0, logical block, 0} null entries
+ * (mask 0 = never read). `info` is HOST memory (may be NULL when entries is
+ * not) and receives {split_tokens, nsplit, entries_per_unit, 0}. Needs
+ * max_entries >= batch * nsplit * entries_per_unit; call with entries = NULL
+ * to get info only.
+ */
+pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t max_entries, int32_t* info,
+                  void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* paged_mqa_logits [FP4API]                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * out[b*next_n + i, t] = sum over heads h (ascending, fp32 fma chain) of
+ *   weights[b*next_n + i, h] * (q[b,i,h,:] . k_t) with both operands MXFP4
+ *   (E2M1 values, one UE8M0 scale per sf_vec_size elements), for
+ *   t < context_lens[b]; -inf for context_lens[b] <= t < max_context_len.
+ * Rows >= batch*next_n and columns >= max_context_len are not written.
+ *
+ * Layouts:
+ *   out       [>= batch*next_n, out_row_stride] fp32, out_row_stride >= max_context_len
+ *   q         [batch, next_n, num_heads, head_dim/2] uint8, element 2j in the low nibble
+ *   sf_q      [batch, next_n, num_heads] int32, byte g scales elements [32g, 32g+32)
+ *   kv_fused  [num_blocks, block_size, 1, head_dim/2 + head_dim/sf_vec_size] uint8; each
+ *             block holds [block_size * head_dim/2 FP4 bytes][block_size * head_dim/32 SF
+ *             bytes], token order
+ *   weights   [batch*next_n, num_heads] fp32
+ *   block_table [batch, max_blocks_per_seq] int32 with max_blocks_per_seq >=
+ *             round_up(max_context_len, 128) / block_size (checked on the host)
+ * Supported: head_dim 128, sf_vec_size 32, block_size 64, num_heads a multiple of 16
+ * up to 64, next_n 1..4. Workspace: none (pass NULL, 0).
+ */
+typedef struct pa_logits_args {
+  float* out;
+  int64_t out_row_stride;
+  const uint8_t* q;
+  const int32_t* sf_q;
+  const uint8_t* kv_fused;
+  const float* weights;
+  const int32_t* context_lens;
+  const int32_t* block_table;
+  int32_t batch;
+  int32_t next_n;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int32_t max_context_len;
+  int32_t sf_vec_size;
+} pa_logits_args;
+
+size_t paged_mqa_logits_workspace_size(const pa_logits_args* a);
+pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* kv_insert [INSERT]                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For each token row i < num_tokens with i < num_slots and slot_mapping[i] >= 0:
+ * k_cache[slot / block_size, slot % block_size, hk, :] = Q(k[i, hk, :] / k_scale)
+ * and likewise for v. Rows without a slot (i >= num_slots, or slot < 0) are
+ * skipped and their destination bytes are left untouched [INSERT, Design: the
+ * KV-only mode skips DP-padding rows that have no slot].
+ * Q: E4M3 round-to-nearest-even saturating to +-448; INT8 / INT4 round to
+ * nearest even clamped to +-127 / +-7; x / scale is an IEEE fp32 division.
+ * F16 caches take fp16 input bits unchanged (scale mode NONE).
+ *
+ * Layouts: k, v [num_tokens, num_kv_heads, head_dim] fp16 (in_dtype PA_DT_F16);
+ * slot_mapping [num_slots] int64; caches and scales as for paged_attn_fwd.
+ * Precondition: every slot < num_blocks * block_size.
+ */
+typedef struct pa_insert_args {
+  void* k_cache;
+  void* v_cache;
+  pa_kv_kind kv_kind;
+  const void* k;
+  const void* v;
+  pa_dtype in_dtype;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t num_slots;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int64_t num_blocks;
+  const float* k_scale;
+  pa_scale_mode k_scale_mode;
+  const float* v_scale;
+  pa_scale_mode v_scale_mode;
+} pa_insert_args;
+
+pa_status kv_insert(const pa_insert_args* a, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* probes and errors                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Test probe of the cache codecs used by paged_attn_fwd: out[i] =
+ * fp32(code_i) * scale, scale = scale[0] (PER_TENSOR), scale[i % channels]
+ * (PER_CHANNEL) or 1 (NONE). `n` counts elements (INT4: two per byte).
+ */
+pa_status pa_dequantize(pa_kv_kind kind, const void* codes, int64_t n, const float* scale,
+                        pa_scale_mode mode, int64_t channels, float* out, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,258 @@
+"""Python binding of libpa.so, the gfx950 paged-attention library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/pa.h. Tensors are torch tensors on the GPU (torch provides
+device memory and the current stream); their data pointers are passed through.
+There is no fallback: if libpa.so is missing, load() raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "load", "paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
+    "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "PaError",
+    "KV_F16", "KV_BF16", "KV_E4M3", "KV_INT8", "KV_INT4",
+    "SCALE_NONE", "SCALE_PER_TENSOR", "SCALE_PER_CHANNEL",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+DT_F16, DT_BF16, DT_F32 = 0, 1, 2
+KV_F16, KV_BF16, KV_E4M3, KV_INT8, KV_INT4 = 0, 1, 2, 3, 4
+SCALE_NONE, SCALE_PER_TENSOR, SCALE_PER_CHANNEL = 0, 1, 2
+STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
+          3: "PA_ERR_PRECONDITION", 4: "PA_ERR_WORKSPACE", 5: "PA_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("out", _vp), ("q", _vp), ("q_dtype", _i32), ("k_cache", _vp), ("v_cache", _vp),
+                ("kv_kind", _i32), ("k_scale", _vp), ("k_scale_mode", _i32), ("v_scale", _vp),
+                ("v_scale_mode", _i32), ("block_table", _vp), ("context_lens", _vp),
+                ("max_context_len", _i32), ("batch", _i32), ("next_n", _i32),
+                ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
+                ("block_size", _i32), ("max_blocks_per_seq", _i32), ("num_blocks", _i64),
+                ("softmax_scale", _f32), ("causal", _i32)]
+
+
+class LogitsArgs(ctypes.Structure):
+    _fields_ = [("out", _vp), ("out_row_stride", _i64), ("q", _vp), ("sf_q", _vp),
+                ("kv_fused", _vp), ("weights", _vp), ("context_lens", _vp), ("block_table", _vp),
+                ("batch", _i32), ("next_n", _i32), ("num_heads", _i32), ("head_dim", _i32),
+                ("block_size", _i32), ("max_blocks_per_seq", _i32), ("num_blocks", _i64),
+                ("max_context_len", _i32), ("sf_vec_size", _i32)]
+
+
+class InsertArgs(ctypes.Structure):
+    _fields_ = [("k_cache", _vp), ("v_cache", _vp), ("kv_kind", _i32), ("k", _vp), ("v", _vp),
+                ("in_dtype", _i32), ("slot_mapping", _vp), ("num_tokens", _i64),
+                ("num_slots", _i64), ("num_kv_heads", _i32), ("head_dim", _i32),
+                ("block_size", _i32), ("num_blocks", _i64), ("k_scale", _vp),
+                ("k_scale_mode", _i32), ("v_scale", _vp), ("v_scale_mode", _i32)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
+           "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "pa_last_error"]
+
+
+def load(path: str | None = None):
+    """Load libpa.so (raises if it was not built: there is no fallback path)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError(f"{p} not found: build it with `python -m paged_attention_quantized_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.paged_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t, _vp]
+    lib.paged_attn_fwd.restype = _i32
+    lib.paged_attn_workspace_size.argtypes = [ctypes.POINTER(AttnArgs)]
+    lib.paged_attn_workspace_size.restype = ctypes.c_size_t
+    lib.pa_plan.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i64, _vp, _vp]
+    lib.pa_plan.restype = _i32
+    lib.paged_mqa_logits.argtypes = [ctypes.POINTER(LogitsArgs), _vp, ctypes.c_size_t, _vp]
+    lib.paged_mqa_logits.restype = _i32
+    lib.paged_mqa_logits_workspace_size.argtypes = [ctypes.POINTER(LogitsArgs)]
+    lib.paged_mqa_logits_workspace_size.restype = ctypes.c_size_t
+    lib.kv_insert.argtypes = [ctypes.POINTER(InsertArgs), _vp]
+    lib.kv_insert.restype = _i32
+    lib.pa_dequantize.argtypes = [_i32, _vp, _i64, _vp, _i32, _i64, _vp, _vp]
+    lib.pa_dequantize.restype = _i32
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise PaError(status, load().pa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _mode(scale, mode):
+    if mode is not None:
+        return mode
+    if scale is None:
+        return SCALE_NONE
+    return SCALE_PER_TENSOR if scale.numel() == 1 else SCALE_PER_CHANNEL
+
+
+# ---------------------------------------------------------------------------
+# paged attention
+# ---------------------------------------------------------------------------
+
+def _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len, kv_kind,
+               k_scale, v_scale, k_scale_mode, v_scale_mode, softmax_scale, causal):
+    B, next_n, Hq, D = q.shape
+    return AttnArgs(out=_ptr(out), q=_ptr(q), q_dtype=DT_F16, k_cache=_ptr(k_cache),
+                    v_cache=_ptr(v_cache), kv_kind=kv_kind, k_scale=_ptr(k_scale),
+                    k_scale_mode=_mode(k_scale, k_scale_mode), v_scale=_ptr(v_scale),
+                    v_scale_mode=_mode(v_scale, v_scale_mode), block_table=_ptr(block_table),
+                    context_lens=_ptr(context_lens), max_context_len=int(max_context_len),
+                    batch=B, next_n=next_n, num_q_heads=Hq, num_kv_heads=k_cache.shape[2],
+                    head_dim=D, block_size=k_cache.shape[1],
+                    max_blocks_per_seq=block_table.shape[1], num_blocks=k_cache.shape[0],
+                    softmax_scale=float(softmax_scale), causal=int(bool(causal)))
+
+
+def paged_attn_workspace_size(q, k_cache, block_table, max_context_len, kv_kind,
+                              k_scale_mode=SCALE_NONE, v_scale_mode=SCALE_NONE):
+    a = _attn_args(None, q, k_cache, k_cache, block_table, None, max_context_len, kv_kind, None,
+                   None, k_scale_mode, v_scale_mode, 0.0, True)
+    return load().paged_attn_workspace_size(ctypes.byref(a))
+
+
+def paged_attn_fwd(out, q, k_cache, v_cache, block_table, context_lens, max_context_len, *,
+                   kv_kind, k_scale=None, v_scale=None, k_scale_mode=None, v_scale_mode=None,
+                   softmax_scale=0.0, causal=True, workspace=None, stream=None):
+    """out[B, next_n, Hq, D] fp16 <- paged attention (see paged_attn_fwd in include/pa.h).
+
+    q fp16 [B, next_n, Hq, D]; k_cache/v_cache uint8 [num_blocks, bs, Hkv, row_bytes];
+    block_table int32 [B, max_blocks]; context_lens int32 [B]; scales fp32 [1] or [Hkv, D].
+    The workspace (uint8 tensor) is allocated here when not given.
+    """
+    import torch
+    a = _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                   kv_kind, k_scale, v_scale, k_scale_mode, v_scale_mode, softmax_scale, causal)
+    lib = load()
+    need = lib.paged_attn_workspace_size(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.paged_attn_fwd(ctypes.byref(a), _ptr(workspace), workspace.numel(),
+                              _stream(stream)))
+    return out
+
+
+def pa_plan(block_table, context_lens, max_context_len, *, q_shape, k_cache_shape, kv_kind,
+            k_scale_mode=SCALE_NONE, v_scale_mode=SCALE_NONE, stream=None):
+    """Planner probe: returns (entries int32 [B, nsplit, entries_per_unit, 3], info)."""
+    import torch
+    B, next_n, Hq, D = q_shape
+    nb, bs, Hkv, _ = k_cache_shape
+    a = AttnArgs(q_dtype=DT_F16, kv_kind=kv_kind, k_scale_mode=k_scale_mode,
+                 v_scale_mode=v_scale_mode, block_table=_ptr(block_table),
+                 context_lens=_ptr(context_lens), max_context_len=int(max_context_len), batch=B,
+                 next_n=next_n, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                 max_blocks_per_seq=block_table.shape[1], num_blocks=nb, softmax_scale=0.0,
+                 causal=1)
+    lib = load()
+    info = (ctypes.c_int32 * 4)()
+    _check(lib.pa_plan(ctypes.byref(a), None, 0, ctypes.cast(info, _vp), None))
+    split, nsplit, epu = info[0], info[1], info[2]
+    entries = torch.empty((B, nsplit, epu, 3), dtype=torch.int32, device=block_table.device)
+    _check(lib.pa_plan(ctypes.byref(a), _ptr(entries), entries.numel() // 3,
+                       ctypes.cast(info, _vp), _stream(stream)))
+    return entries, {"split_tokens": split, "nsplit": nsplit, "entries_per_unit": epu}
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 paged MQA logits
+# ---------------------------------------------------------------------------
+
+def _logits_args(out, q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len,
+                 sf_vec_size):
+    B, next_n, H, Dh = q.shape
+    return LogitsArgs(out=_ptr(out), out_row_stride=out.stride(0) if out is not None else 0,
+                      q=_ptr(q), sf_q=_ptr(sf_q), kv_fused=_ptr(kv_fused), weights=_ptr(weights),
+                      context_lens=_ptr(context_lens), block_table=_ptr(block_table), batch=B,
+                      next_n=next_n, num_heads=H, head_dim=2 * Dh, block_size=kv_fused.shape[1],
+                      max_blocks_per_seq=block_table.shape[1], num_blocks=kv_fused.shape[0],
+                      max_context_len=int(max_context_len), sf_vec_size=int(sf_vec_size))
+
+
+def paged_mqa_logits_workspace_size(q, sf_q, kv_fused, weights, context_lens, block_table,
+                                    max_context_len, sf_vec_size=32):
+    a = _logits_args(None, q, sf_q, kv_fused, weights, context_lens, block_table,
+                     max_context_len, sf_vec_size)
+    return load().paged_mqa_logits_workspace_size(ctypes.byref(a))
+
+
+def paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len, *,
+                     sf_vec_size=32, out=None, workspace=None, stream=None):
+    """Weighted per-head MXFP4 logits [B*next_n, max_context_len] fp32 (include/pa.h)."""
+    import torch
+    B, next_n = q.shape[:2]
+    if out is None:
+        out = torch.empty((B * next_n, max_context_len), dtype=torch.float32, device=q.device)
+    a = _logits_args(out, q, sf_q, kv_fused, weights, context_lens, block_table,
+                     max_context_len, sf_vec_size)
+    lib = load()
+    need = lib.paged_mqa_logits_workspace_size(ctypes.byref(a))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.paged_mqa_logits(ctypes.byref(a), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0,
+                                _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# KV insert and the codec probe
+# ---------------------------------------------------------------------------
+
+def kv_insert(k_cache, v_cache, k, v, slot_mapping, *, kv_kind, k_scale=None, v_scale=None,
+              k_scale_mode=None, v_scale_mode=None, stream=None):
+    """Quantize rows k, v [T, Hkv, D] fp16 into the paged caches at slot_mapping (int64)."""
+    T, Hkv, D = k.shape
+    a = InsertArgs(k_cache=_ptr(k_cache), v_cache=_ptr(v_cache), kv_kind=kv_kind, k=_ptr(k),
+                   v=_ptr(v), in_dtype=DT_F16, slot_mapping=_ptr(slot_mapping), num_tokens=T,
+                   num_slots=slot_mapping.shape[0], num_kv_heads=Hkv, head_dim=D,
+                   block_size=k_cache.shape[1], num_blocks=k_cache.shape[0],
+                   k_scale=_ptr(k_scale), k_scale_mode=_mode(k_scale, k_scale_mode),
+                   v_scale=_ptr(v_scale), v_scale_mode=_mode(v_scale, v_scale_mode))
+    _check(load().kv_insert(ctypes.byref(a), _stream(stream)))
+
+
+def pa_dequantize(kind, codes, n, scale=None, mode=None, channels=1, out=None, stream=None):
+    """Codec probe: out[i] = fp32(code_i) * scale (include/pa.h)."""
+    import torch
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=codes.device)
+    _check(load().pa_dequantize(kind, _ptr(codes), n, _ptr(scale), _mode(scale, mode), channels,
+                                _ptr(out), _stream(stream)))
+    return out

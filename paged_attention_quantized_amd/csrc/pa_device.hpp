@@ -1,0 +1,159 @@
+// pa_device.hpp -- device helpers shared by the gfx950 kernels of libpa:
+// vector types, KV-cache codecs (code -> fp16, exact for every kind), the
+// planner's page-entry function and small wavefront utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+__device__ __forceinline__ uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
+
+// ---------------------------------------------------------------------------
+// Cache element kinds. Every decode is exact: E4M3, INT8 and INT4 codes are all
+// representable in fp16 ([NULLPAD] E4M3 NaN bytes 0x7F/0xFF decode to fp16 NaN).
+// ---------------------------------------------------------------------------
+
+template <int KIND>
+struct Kv;
+
+// fp16 cache: 2 bytes per element, no decode.
+template <>
+struct Kv<PA_KV_F16> {
+  static constexpr int kBits = 16;
+  // one dword -> one pair, natural order
+  static constexpr int kPairsPerDword = 1;
+  __device__ static void decode(uint32_t w, h2* out) { out[0] = as_h2(w); }
+  // element order of the pairs produced from one dword (see decode)
+  __device__ static constexpr int order(int e) { return e; }
+};
+
+// OCP FP8 E4M3FN via the gfx950 scaled fp8 -> fp16 conversion (scale 1.0):
+// bytes (0,1) and (2,3) of a dword become two fp16 pairs.
+template <>
+struct Kv<PA_KV_E4M3> {
+  static constexpr int kBits = 8;
+  static constexpr int kPairsPerDword = 2;
+  __device__ static void decode(uint32_t w, h2* out) {
+    out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  }
+  __device__ static constexpr int order(int e) { return e; }
+};
+
+// INT8: bias each byte to unsigned (x ^ 0x80), place it under the fp16
+// exponent of 1024 (0x64xx = 1024 + byte) and subtract 1024 + 128.
+template <>
+struct Kv<PA_KV_INT8> {
+  static constexpr int kBits = 8;
+  static constexpr int kPairsPerDword = 2;
+  __device__ static void decode(uint32_t w, h2* out) {
+    uint32_t x = w ^ 0x80808080u;
+    uint32_t lo = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+    uint32_t hi = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    out[0] = as_h2(lo) - bias;
+    out[1] = as_h2(hi) - bias;
+  }
+  __device__ static constexpr int order(int e) { return e; }
+};
+
+// INT4: eight signed nibbles per dword (element k at bits 4k..4k+3). Flipping
+// bit 3 of every nibble maps value v to v + 8 in [0, 15]; nibbles k and k+4 are
+// masked under the fp16 exponent of 1024 and 1032 is subtracted. The pairs come
+// out as (e0,e4), (e1,e5), (e2,e6), (e3,e7).
+template <>
+struct Kv<PA_KV_INT4> {
+  static constexpr int kBits = 4;
+  static constexpr int kPairsPerDword = 4;
+  __device__ static void decode(uint32_t w, h2* out) {
+    uint32_t x = w ^ 0x88888888u;
+    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      out[k] = as_h2(((x >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - bias;
+  }
+  // slot e of the 8 fp16 values produced from one dword holds element order(e)
+  __device__ static constexpr int order(int e) { return (e >> 1) + 4 * (e & 1); }
+};
+
+// Decode a run of dwords into fp16 values. Slot s of the output holds element
+// (s / (2 * kPairsPerDword)) * (2 * kPairsPerDword) + Kv::order(s % (2*kPairsPerDword))
+// of the run.
+template <int KIND, int NDW>
+__device__ __forceinline__ void decode_run(const uint32_t* w, _Float16* out) {
+  constexpr int P = Kv<KIND>::kPairsPerDword;
+#pragma unroll
+  for (int i = 0; i < NDW; ++i) {
+    h2 pr[P];
+    Kv<KIND>::decode(w[i], pr);
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      out[(i * P + k) * 2 + 0] = pr[k][0];
+      out[(i * P + k) * 2 + 1] = pr[k][1];
+    }
+  }
+}
+
+// element index (within the run) of output slot s of decode_run
+template <int KIND>
+__device__ __forceinline__ constexpr int run_elem(int s) {
+  constexpr int E = 2 * Kv<KIND>::kPairsPerDword;
+  return (s / E) * E + Kv<KIND>::order(s % E);
+}
+
+// ---------------------------------------------------------------------------
+// Planner ([RELOC] logical order; [NULLPAD] padding entries are null block 0
+// with mask 0 and are never dereferenced). The unit (b, split) walks logical
+// blocks split * pages_per_split + e in ascending e. Entries past the sequence
+// or past the split are padding.
+// ---------------------------------------------------------------------------
+
+struct PlanEntry {
+  int32_t phys;
+  int32_t lblk;
+  uint32_t mask;  // bit j: token slot j is a real, in-range token
+};
+
+__device__ __forceinline__ PlanEntry plan_entry(const int32_t* __restrict__ table_row, int L,
+                                                int bs, int first_lblk, int pages_per_split,
+                                                int e) {
+  PlanEntry x;
+  x.lblk = first_lblk + e;
+  int start = x.lblk * bs;
+  if (e < pages_per_split && start < L) {
+    x.phys = table_row[x.lblk];
+    int valid = L - start < bs ? L - start : bs;
+    x.mask = valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u);
+  } else {
+    x.phys = 0;
+    x.mask = 0u;
+  }
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// wavefront helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+
+}  // namespace pa

@@ -1,0 +1,201 @@
+"""GPU parity of paged_attn_fwd against the oracle, through the C ABI.
+
+Tolerance: |gpu - oracle| <= max(2e-3, 1 fp16 ulp of the oracle value) per
+element (the 2e-3 bound on fp16 outputs, widened only where a fp16 ulp is
+larger). Bitwise: identical output under physical relocation of pages and an
+unpaged layout, and across repeated runs. Zero NaN with NaN-poisoned null
+block and tail slots.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.gpu_util import DevAttn, compare_attn, oracle_attn, run_attn, say
+
+pytestmark = pytest.mark.gpu
+
+
+def small_cases():
+    """Sizes the oracle finishes in seconds; several 32-token chunks, several
+    splits, ragged tails, and the shapes of every workload."""
+    rng = np.random.default_rng(77)
+    return [
+        W.tiny_f16(),
+        W.attn_case("fp8_decode_small", 1101, B=6, next_n=1, Hq=32, Hkv=8, D=128, bs=16,
+                    lens=list(rng.integers(1, 700, 6)), kv_kind=W.KV_E4M3,
+                    scale_mode=W.SCALE_PER_TENSOR),
+        W.attn_case("int8_perchan_small", 1102, B=3, next_n=1, Hq=16, Hkv=2, D=256, bs=32,
+                    lens=[1000, 333, 64], kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_CHANNEL,
+                    q_dist=(-100.0, 100.0), zero_k_channel_frac=0.1,
+                    v_scale_range=(1e-2, 65504.0 / 127)),
+        W.attn_case("int4_perchan_small", 1103, B=3, next_n=1, Hq=16, Hkv=2, D=256, bs=32,
+                    lens=[777, 32, 1], kv_kind=W.KV_INT4, scale_mode=W.SCALE_PER_CHANNEL,
+                    q_dist=(-100.0, 100.0), zero_k_channel_frac=0.1),
+        W.attn_case("fp8_verify_small", 1104, B=3, next_n=4, Hq=64, Hkv=8, D=128, bs=32,
+                    lens=[900, 37, 5], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR),
+        W.attn_case("f16_d128_gqa8", 1105, B=2, next_n=2, Hq=16, Hkv=2, D=128, bs=16,
+                    lens=[300, 95], kv_kind=W.KV_F16, scale_mode=W.SCALE_NONE),
+        W.attn_case("int8_pt_d64", 1106, B=2, next_n=1, Hq=8, Hkv=8, D=64, bs=16,
+                    lens=[129, 500], kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_TENSOR),
+        W.attn_case("int4_pt_d128", 1107, B=2, next_n=3, Hq=12, Hkv=4, D=128, bs=32,
+                    lens=[257, 3], kv_kind=W.KV_INT4, scale_mode=W.SCALE_PER_TENSOR,
+                    causal=True),
+        W.attn_case("e4m3_noncausal_rows", 1108, B=2, next_n=2, Hq=8, Hkv=1, D=128, bs=16,
+                    lens=[70, 16], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR,
+                    causal=False),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(9))
+def test_small_parity(pa, idx):
+    case = small_cases()[idx]
+    say(f"parity {case.name} B={case.batch} next_n={case.next_n} lens={list(case.context_lens)}")
+    got = run_attn(pa, case)
+    ref = oracle_attn(case)
+    r = compare_attn(got, ref, case.name)
+    say(f"{case.name}: max err/tol = {r:.3f}")
+
+
+@pytest.mark.parametrize("idx", [0, 1, 3, 4])
+def test_relocation_and_unpaged_bit_identical(pa, idx):
+    case = small_cases()[idx]
+    say(f"relocation {case.name}")
+    base = run_attn(pa, case)
+    for other in (W.relocate(case, 5), W.relocate(case, 6), W.unpaged(case)):
+        got = run_attn(pa, other)
+        assert np.array_equal(got.view(np.uint16), base.view(np.uint16))
+
+
+def test_repeat_runs_bitwise_equal(pa):
+    case = small_cases()[4]
+    say("repeat fp8_verify_small")
+    d = DevAttn(case)
+    a = d.run(pa).cpu().numpy()
+    for _ in range(3):
+        assert np.array_equal(d.run(pa).cpu().numpy().view(np.uint16), a.view(np.uint16))
+
+
+def test_poisoned_null_block_and_tails_no_nan(pa):
+    """Null block 0 and tail slots hold E4M3 NaN bytes (0x7F/0xFF), the padded
+    block table points at block 0: no NaN may reach the output."""
+    case = W.attn_case("poison", 1201, B=8, next_n=1, Hq=32, Hkv=8, D=128, bs=16,
+                       lens=[1, 15, 16, 17, 31, 33, 100, 250], kv_kind=W.KV_E4M3,
+                       scale_mode=W.SCALE_PER_TENSOR, max_context_len=512)
+    assert (case.block_table == 0).any()
+    say("poisoned null block")
+    got = run_attn(pa, case)
+    assert not np.isnan(got.astype(np.float32)).any()
+    compare_attn(got, oracle_attn(case), case.name)
+
+
+def test_edge_lengths(pa):
+    """Empty sequences, one token, exact page and chunk multiples, and causal
+    rows that see no token (L < next_n)."""
+    case = W.attn_case("edges", 1301, B=7, next_n=3, Hq=8, Hkv=2, D=128, bs=16,
+                       lens=[0, 1, 2, 16, 32, 64, 3], kv_kind=W.KV_E4M3,
+                       scale_mode=W.SCALE_PER_TENSOR, max_context_len=80)
+    say("edge lengths")
+    got = run_attn(pa, case)
+    ref = oracle_attn(case)
+    compare_attn(got, ref, case.name)
+    assert np.all(got[0] == 0)  # L = 0: +0 everywhere
+    assert np.all(got[1, :2] == 0)  # L = 1, rows 0 and 1 see no token
+
+
+def test_worked_case_inf_times_zero(pa):
+    """q = 100, per-channel k_scale = 1000 (and 1e4), every K code zero: finite
+    and equal to the mean of V ("Normalize the PER_CHANNEL K scale folded into
+    Q for paged XQA", Description)."""
+    for kind in (W.KV_INT4, W.KV_INT8, W.KV_E4M3):
+        for ks in (1000.0, 1e4):
+            case = W.attn_case("worked", 1401, B=2, next_n=1, Hq=8, Hkv=2, D=128, bs=16,
+                               lens=[19, 300], kv_kind=kind,
+                               scale_mode=W.SCALE_PER_TENSOR if kind == W.KV_E4M3
+                               else W.SCALE_PER_CHANNEL, v_scale_range=(0.5, 2.0))
+            case.q[:] = np.float16(100.0)
+            case.k_scale = np.full((2, 128), ks, np.float32)
+            case.k_scale_mode = W.SCALE_PER_CHANNEL
+            case.k_cache[:] = 0
+            say(f"worked case kind={kind} k_scale={ks}")
+            got = run_attn(pa, case)
+            assert np.isfinite(got.astype(np.float32)).all()
+            compare_attn(got, oracle_attn(case), f"worked kind={kind} ks={ks}")
+
+
+def test_plan_probe(pa):
+    """The planner walks logical blocks in ascending order, covers [0, L)
+    exactly once per sequence, pads every unit to a multiple of 8 entries with
+    null (block 0, mask 0) entries, and never points a live entry at block 0."""
+    case = small_cases()[1]
+    d = DevAttn(case)
+    say("plan probe")
+    entries, info = pa.pa_plan(d.bt, d.cl, case.max_context_len, q_shape=case.q.shape,
+                               k_cache_shape=case.k_cache.shape, kv_kind=case.kv_kind,
+                               k_scale_mode=case.k_scale_mode)
+    e = entries.cpu().numpy()
+    bs = case.block_size
+    assert info["entries_per_unit"] % 8 == 0
+    assert info["split_tokens"] % bs == 0
+    for b in range(case.batch):
+        L = int(case.context_lens[b])
+        seen = []
+        for s in range(info["nsplit"]):
+            for phys, lblk, mask in e[b, s]:
+                mask = int(np.uint32(mask))
+                if mask == 0:
+                    assert phys == 0
+                    continue
+                assert phys == case.block_table[b, lblk] and phys != 0
+                for j in range(bs):
+                    if mask >> j & 1:
+                        seen.append(lblk * bs + j)
+        assert seen == list(range(L))
+
+
+def test_workspace_and_args_errors(pa):
+    case = small_cases()[0]
+    d = DevAttn(case)
+    out = torch.empty(case.q.shape, dtype=torch.float16, device="cuda")
+    with pytest.raises(pa.PaError, match="WORKSPACE"):
+        pa.paged_attn_fwd(out, d.q, d.k, d.v, d.bt, d.cl, case.max_context_len,
+                          kv_kind=case.kv_kind, workspace=torch.empty(1, dtype=torch.uint8,
+                                                                      device="cuda"))
+    with pytest.raises(pa.PaError, match="PRECONDITION"):
+        pa.paged_attn_fwd(out, d.q, d.k, d.v, d.bt, d.cl, 10_000, kv_kind=case.kv_kind)
+
+
+# ---------------------------------------------------------------------------
+# full workload sizes, in the launch configuration the benchmark times;
+# sampled sequences are checked against the oracle
+# ---------------------------------------------------------------------------
+
+def _full_sampled(pa, case, sample):
+    say(f"full {case.name}: B={case.batch} tokens={int(case.context_lens.sum())}")
+    got = run_attn(pa, case)
+    assert not np.isnan(got.astype(np.float32)).any()
+    sub = case.sub_batch(sample)
+    ref = oracle_attn(sub)
+    r = compare_attn(got[sample], ref, case.name)
+    say(f"{case.name}: sampled max err/tol = {r:.3f}")
+    return got
+
+
+def test_full_fp8_decode(pa):
+    case = W.fp8_decode()
+    _full_sampled(pa, case, [0, 17, 40, 63])
+
+
+@pytest.mark.parametrize("kind", [W.KV_INT8, W.KV_INT4])
+def test_full_int_perchan(pa, kind):
+    case = W.int_perchan(kind)
+    _full_sampled(pa, case, [0, 31])
+
+
+def test_full_fp8_verify_double_shuffle(pa):
+    case = W.fp8_verify()
+    got = _full_sampled(pa, case, [5])
+    for seed in (11, 12):
+        say(f"fp8_verify relocation {seed}")
+        other = run_attn(pa, W.relocate(case, seed))
+        assert np.array_equal(other.view(np.uint16), got.view(np.uint16))
