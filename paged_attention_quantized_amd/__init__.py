@@ -12,7 +12,8 @@ import os
 
 __all__ = [
     "load", "paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
-    "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "PaError",
+    "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "pa_set_profile_events",
+    "PaError",
     "KV_F16", "KV_BF16", "KV_E4M3", "KV_INT8", "KV_INT4",
     "SCALE_NONE", "SCALE_PER_TENSOR", "SCALE_PER_CHANNEL",
 ]
@@ -65,7 +66,8 @@ class PaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
-           "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "pa_last_error"]
+           "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "pa_last_error",
+           "pa_set_profile_events"]
 
 
 def load(path: str | None = None):
@@ -93,6 +95,8 @@ def load(path: str | None = None):
     lib.pa_dequantize.restype = _i32
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_set_profile_events.argtypes = [_vp, _vp]
+    lib.pa_set_profile_events.restype = _i32
     if path is None:
         _lib = lib
     return lib
@@ -246,6 +250,11 @@ def kv_insert(k_cache, v_cache, k, v, slot_mapping, *, kv_kind, k_scale=None, v_
                    k_scale=_ptr(k_scale), k_scale_mode=_mode(k_scale, k_scale_mode),
                    v_scale=_ptr(v_scale), v_scale_mode=_mode(v_scale, v_scale_mode))
     _check(load().kv_insert(ctypes.byref(a), _stream(stream)))
+
+
+def pa_set_profile_events(start_event, stop_event):
+    """Bracket the dominant kernel of later calls with two hipEvent_t handles (or clear)."""
+    _check(load().pa_set_profile_events(start_event, stop_event))
 
 
 def pa_dequantize(kind, codes, n, scale=None, mode=None, channels=1, out=None, stream=None):

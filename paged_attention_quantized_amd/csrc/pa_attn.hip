@@ -502,7 +502,9 @@ extern "C" pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace,
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
   AttnParams p = make_params(a, sh, workspace);
   hipStream_t s = (hipStream_t)stream;
+  prof_begin(s);
   hipLaunchKernelGGL(fn, dim3((unsigned)sh.units), dim3(64), 0, s, p);
+  prof_end(s);
   if ((st = launch_status("paged_attn split kernel")) != PA_OK) return st;
   hipLaunchKernelGGL(pick_merge(a->head_dim), dim3((unsigned)(a->batch * a->num_kv_heads),
                      (unsigned)ceil_div((int64_t)sh.R * a->head_dim, 256)), dim3(256), 0, s, p);

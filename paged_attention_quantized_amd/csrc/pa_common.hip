@@ -17,6 +17,24 @@ pa_status fail(pa_status st, const char* fmt, ...) {
 
 void clear_error() { g_err[0] = '\0'; }
 
+// Profiling hook: events recorded right before and right after the dominant
+// kernel of the next calls on this thread.
+static thread_local hipEvent_t g_prof_start = nullptr;
+static thread_local hipEvent_t g_prof_stop = nullptr;
+
+void prof_begin(hipStream_t s) {
+  if (g_prof_start) hipEventRecord(g_prof_start, s);
+}
+
+void prof_end(hipStream_t s) {
+  if (g_prof_stop) hipEventRecord(g_prof_stop, s);
+}
+
+void set_prof_events(void* start, void* stop) {
+  g_prof_start = (hipEvent_t)start;
+  g_prof_stop = (hipEvent_t)stop;
+}
+
 pa_status launch_status(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -26,3 +44,10 @@ pa_status launch_status(const char* what) {
 }  // namespace pa
 
 extern "C" const char* pa_last_error(void) { return pa::g_err; }
+
+extern "C" pa_status pa_set_profile_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_set_profile_events: give both events or neither");
+  pa::set_prof_events(start_event, stop_event);
+  return PA_OK;
+}

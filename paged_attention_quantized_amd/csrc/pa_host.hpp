@@ -14,6 +14,8 @@ namespace pa {
 pa_status fail(pa_status st, const char* fmt, ...);
 void clear_error();
 pa_status launch_status(const char* what);
+void prof_begin(hipStream_t s);  // record the profiling start event, if set
+void prof_end(hipStream_t s);    // record the profiling stop event, if set
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
