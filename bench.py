@@ -277,7 +277,7 @@ def main():
         dtype = "fp4xfp4->f32"
     else:
         r = bench_attn(args, torch, pa, hip, case)
-        tag = "attn_split_" + args.workload
+        tag = "attn_ring_" + args.workload
         config = {"workload": args.workload, "batch": case.batch, "next_n": case.next_n,
                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
                   "head_dim": case.head_dim, "block_size": case.block_size,

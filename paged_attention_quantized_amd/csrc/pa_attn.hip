@@ -1,336 +1,143 @@
 // pa_attn.hip -- paged attention over a quantized KV cache on gfx950.
 //
-// Work unit = (sequence b, split s, KV head hk), one wavefront. A split covers
-// logical tokens [s*S, (s+1)*S) with S fixed from the shapes only, so the
-// reduction order never depends on physical block ids [RELOC, Summary].
-// Per 32-token chunk the wave
-//   1. reads the chunk's page entries (planner, logical order); entries with
-//      mask 0 are never read [NULLPAD, Root cause],
-//   2. loads K rows (16 B per lane, coalesced) and V rows (each lane owns
-//      head_dim/16 consecutive channels of 8 tokens),
-//   3. decodes codes to fp16 in registers (exact for E4M3/INT8/INT4) and zeroes
-//      V rows of tail tokens by select [NULLPAD, Fix],
-//   4. S^T = K Q'^T with v_mfma_f32_16x16x32_f16 (tokens x query rows); the
-//      per-channel K scale is folded into Q' = q * k_scale / max|k_scale|,
-//      carried as fp16 hi + lo parts [FOLD, Approach],
-//   5. online softmax in the exponent base 2 on raw scores (p = 2^((s - m) c)),
-//   6. O^T += V^T P^T with the same MFMA (channels x query rows).
-// The unit writes (m, l, c) and the unnormalized O; the merge kernel combines
-// splits in ascending logical order and applies v_scale / l.
+// Work decomposition. The KV reduction is cut into "items": TS consecutive
+// logical tokens of one sequence for one group of HPU KV heads. Items are
+// ordered by (sequence, head group, logical position) and the persistent grid
+// (one workgroup per compute unit) gives workgroup w the contiguous item range
+// [w*Q, (w+1)*Q), Q = ceil(items / workgroups). Every workgroup therefore gets
+// the same number of KV bytes whatever the mix of context lengths, and all
+// cut points depend on logical positions only, never on physical block ids
+// [RELOC, Summary].
+//
+// Memory path. A workgroup streams its items through a ring of kStages stages
+// in LDS. A stage holds the K rows, then the V rows, of the item's TS tokens x
+// HPU heads, fetched with global_load_lds_dwordx4 (HBM -> LDS, no registers):
+// the 16-byte loads of a wave cover whole rows, so a page is read as a few long
+// contiguous runs. kStages - 1 stages are in flight while one is computed; each
+// step waits with an explicit vmcnt and a bare s_barrier, and every step issues
+// the same number of loads (past the end: dummy in-bounds loads into the free
+// slot) so the count stays exact. Blocks are looked up with scalar loads only,
+// so no vector load waits behind the ring. Within a row, 16-byte pieces are
+// stored XOR-swizzled by the token index to spread LDS banks. Tokens past the
+// sequence end are read only inside real pages; pages past the end are never
+// read (their lanes re-read the stage's first page), which keeps the null
+// block 0 unread [NULLPAD, Root cause].
+//
+// Compute. Wave w of the workgroup serves head hl = w % HPU of the group and
+// the 16-token sub-tile st = w / HPU of every stage:
+//   1. K codes from LDS -> fp16 (exact for E4M3/INT8/INT4), S^T = K Q'^T with
+//      v_mfma_f32_16x16x32_f16 (tokens x query rows); a PER_CHANNEL K scale is
+//      folded into Q' = q * k_scale / max|k_scale| as fp16 hi + lo parts and
+//      max|k_scale| goes into the score scale [FOLD, Approach],
+//   2. online softmax in base 2 on raw scores; tokens past the end or past a
+//      row's causal limit are selected to p = 0 (never multiplied),
+//   3. V codes from LDS -> fp16, rows of invalid tokens zeroed by select
+//      [NULLPAD, Fix], O^T += V^T P^T with v_mfma_f32_16x16x16_f16.
+// At the end of each (sequence, head group) run inside its range a wave writes
+// its (m, l, c) and unnormalized O as a partial; the merge kernel combines the
+// partials of a (sequence, KV head) in workgroup order, then sub-tile order,
+// and applies v_scale / l.
 #include <math.h>
 
-#include "pa_device.hpp"
+#include "pa_attn.hpp"
 #include "pa_host.hpp"
 
 namespace pa {
 
-struct AttnParams {
-  _Float16* out;
-  const _Float16* q;
-  const uint8_t* k_cache;
-  const uint8_t* v_cache;
-  const float* k_scale;
-  const float* v_scale;
-  const int32_t* block_table;
-  const int32_t* context_lens;
-  f4* ws_ml;     // [units, R] (m_raw, l, c, 0)
-  float* ws_o;   // [units, R, D]
-  int B, next_n, Hq, Hkv, G, R, bs, max_blocks;
-  int split_tokens, nsplit, pages_per_split;
-  int k_scale_mode, v_scale_mode, causal;
-  float softmax_scale;
-};
-
-template <int KIND, int D, int RT, bool HILO>
-__global__ __launch_bounds__(64) void attn_split_kernel(AttnParams p) {
-  constexpr int BITS = Kv<KIND>::kBits;
-  constexpr int RB = D * BITS / 8;   // bytes per (token, head) row
-  constexpr int NJ = RB / 64;        // 16-byte K chunks per lane per token
-  constexpr int EPC = 128 / BITS;    // elements per 16-byte chunk
-  constexpr int KPC = EPC / 8;       // MFMA k-steps (32 channels) per chunk per lane group
-  constexpr int KS = D / 32;         // k-steps of QK
-  constexpr int DV = D / 16;         // channels each lane owns for V
-  constexpr int VB = RB / 16;        // V bytes per lane per token
-  constexpr int VDW = VB / 4;
-  static_assert(RB % 64 == 0, "row bytes must be a multiple of 64");
-  static_assert(NJ * KPC == KS, "k-step bookkeeping");
-
-  const int lane = threadIdx.x;
-  const int n = lane & 15, g = lane >> 4;
-  int unit = blockIdx.x;
-  const int hk = unit % p.Hkv;
-  unit /= p.Hkv;
-  const int s = unit % p.nsplit;
-  const int b = unit / p.nsplit;
-  const int L = p.context_lens[b];
-  const int t_begin = s * p.split_tokens;
-  if (t_begin >= L) return;
-  const int t_end = min(t_begin + p.split_tokens, L);
-  const int32_t* table_row = p.block_table + (size_t)b * p.max_blocks;
-  const int first_lblk = t_begin / p.bs;
-
-  // ---- scale constants: fold normalizer for PER_CHANNEL K [FOLD, Approach] ----
-  float qk, inv_m = 0.f;
-  if constexpr (HILO) {
-    float mx = 0.f;
-    for (int i = lane; i < p.Hkv * D; i += 64) mx = fmaxf(mx, fabsf(p.k_scale[i]));
-    mx = wave_max(mx);
-    inv_m = mx > 0.f ? 1.0f / mx : 0.f;
-    qk = p.softmax_scale * mx;
-  } else {
-    qk = p.softmax_scale * (p.k_scale_mode == PA_SCALE_PER_TENSOR ? p.k_scale[0] : 1.0f);
-  }
-  const float sgn = qk < 0.f ? -1.f : 1.f;
-  const float c2 = fabsf(qk) * kLog2e;
-
-  // ---- Q' operands (B of the QK MFMA): lane (n, g) holds row 16*rt+n, the 8
-  // channels of k-step ks that lane group g's K chunk provides ----
-  h8 qa[RT][KS];
-  h8 qb[RT][HILO ? KS : 1];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = 16 * rt + n;
-    const bool rv = r < p.R;
-    const int i = r / p.G, hg = r % p.G;
-    const _Float16* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int j = ks / KPC, w = ks % KPC;
-      const int d0 = (g + 4 * j) * EPC + 8 * w;
-      h8 v = {};
-      if (rv) v = *reinterpret_cast<const h8*>(qrow + d0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = d0 + run_elem<KIND>(e);
-        const float x = (float)v[run_elem<KIND>(e)];
-        if constexpr (HILO) {
-          const float xf = x * (p.k_scale[hk * D + d] * inv_m) * sgn;
-          const _Float16 hi = (_Float16)xf;
-          qa[rt][ks][e] = hi;
-          qb[rt][ks][e] = (_Float16)(xf - (float)hi);
-        } else {
-          qa[rt][ks][e] = (_Float16)(x * sgn);
-        }
-      }
-    }
-  }
-
-  f4 o[RT][DV];
-  float m_run[RT], l_run[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
-#pragma unroll
-    for (int q = 0; q < DV; ++q) o[rt][q] = f4{0.f, 0.f, 0.f, 0.f};
-  }
-  int lim[RT];  // query row 16*rt+n sees tokens t <= lim
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int i = (16 * rt + n) / p.G;
-    lim[rt] = p.causal ? (L - p.next_n + i) : 0x7fffffff;
-  }
-
-  for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-    u4 kraw[2][NJ];
-    uint32_t vraw[8][VDW];
-    uint32_t tmask[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int tt = t0 + 16 * tau;
-      const int e_idx = tt / p.bs - first_lblk;
-      const PlanEntry en = plan_entry(table_row, L, p.bs, first_lblk, p.pages_per_split, e_idx);
-      const int slot0 = tt % p.bs;
-      tmask[tau] = (en.mask >> slot0) & 0xFFFFu;
-      if (tmask[tau] != 0u) {
-        const uint8_t* base = p.k_cache + (((size_t)en.phys * p.bs + slot0) * p.Hkv + hk) * RB;
-        const size_t tok_stride = (size_t)p.Hkv * RB;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          kraw[tau][j] = *reinterpret_cast<const u4*>(base + n * tok_stride + 16 * (g + 4 * j));
-        const uint8_t* vbase = p.v_cache + (((size_t)en.phys * p.bs + slot0) * p.Hkv + hk) * RB;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint8_t* src = vbase + (4 * g + e) * tok_stride + n * VB;
-          if constexpr (VDW == 4) {
-            u4 x = *reinterpret_cast<const u4*>(src);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) vraw[4 * tau + e][k] = x[k];
-          } else if constexpr (VDW == 2) {
-            u2 x = *reinterpret_cast<const u2*>(src);
-            vraw[4 * tau + e][0] = x[0];
-            vraw[4 * tau + e][1] = x[1];
-          } else {
-            vraw[4 * tau + e][0] = *reinterpret_cast<const uint32_t*>(src);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) kraw[tau][j] = u4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int k = 0; k < VDW; ++k) vraw[4 * tau + e][k] = 0u;
-      }
-      // tail tokens: zero their V codes by select so 0 * NaN never happens
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = (tmask[tau] >> (4 * g + e)) & 1u;
-#pragma unroll
-        for (int k = 0; k < VDW; ++k) vraw[4 * tau + e][k] = ok ? vraw[4 * tau + e][k] : 0u;
-      }
-    }
-
-    // ---- S^T = K Q'^T ----
-    f4 sacc[2][RT];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      h8 kop[KS];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        _Float16 hv[EPC];
-        uint32_t wd[4] = {kraw[tau][j][0], kraw[tau][j][1], kraw[tau][j][2], kraw[tau][j][3]};
-        decode_run<KIND, 4>(wd, hv);
-#pragma unroll
-        for (int w = 0; w < KPC; ++w)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kop[j * KPC + w][e] = hv[8 * w + e];
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], qa[rt][ks], acc, 0, 0, 0);
-          if constexpr (HILO)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], qb[rt][ks], acc, 0, 0, 0);
-        }
-        sacc[tau][rt] = acc;
-      }
-    }
-
-    // ---- online softmax (per query row = lane column n) ----
-    h8 pb[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float sv[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tk = 4 * g + e;
-          const int t = t0 + 16 * tau + tk;
-          const bool ok = ((tmask[tau] >> tk) & 1u) && t <= lim[rt];
-          const float x = ok ? sacc[tau][rt][e] : -INFINITY;
-          sv[4 * tau + e] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m_run[rt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f((m_run[rt] - m_use) * c2);
-      float psum = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const _Float16 ph = (_Float16)exp2f((sv[k] - m_use) * c2);
-        pb[rt][k] = ph;
-        psum += (float)ph;
-      }
-      l_run[rt] = alpha * l_run[rt] + psum;
-      m_run[rt] = m_new;
-#pragma unroll
-      for (int q = 0; q < DV; ++q) o[rt][q] *= alpha;
-    }
-
-    // ---- O^T += V^T P^T ----
-    _Float16 vh[8][DV];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) decode_run<KIND, VDW>(vraw[e], vh[e]);
-#pragma unroll
-    for (int q = 0; q < DV; ++q) {
-      h8 vop;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vop[e] = vh[e][q];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pb[rt], o[rt][q], 0, 0, 0);
-    }
-  }
-
-  // ---- write the split's partial state ----
-  const size_t u = blockIdx.x;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    float l = l_run[rt];
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
-    const int r = 16 * rt + n;
-    if (r < p.R) {
-      if (g == 0) p.ws_ml[u * p.R + r] = f4{m_run[rt], l, c2, 0.f};
-      float* orow = p.ws_o + (u * p.R + r) * D;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float tmp[DV];
-#pragma unroll
-        for (int q = 0; q < DV; ++q) tmp[run_elem<KIND>(q)] = o[rt][q][e];
-#pragma unroll
-        for (int k = 0; k < DV; k += 4)
-          *reinterpret_cast<f4*>(orow + DV * (4 * g + e) + k) =
-              f4{tmp[k], tmp[k + 1], tmp[k + 2], tmp[k + 3]};
-      }
-    }
-  }
-}
-
-// Combine the splits of each (b, hk) in ascending logical order [RELOC] and
-// apply the V scale and 1/l. A row with no visible token is +0.
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+// Combine the partials of each (sequence b, KV head hk) in a fixed order
+// (workgroup, then sub-tile), which depends on logical positions only [RELOC],
+// and apply the V scale and 1/l. A row with no visible token is +0. One thread
+// per 4 output channels; the item ranges of the ring kernel are recomputed
+// from context_lens.
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
+  __shared__ int tmp[8];
   const int bh = blockIdx.x;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
+  const int hg = hk / p.hpu, hl = hk % p.hpu;
+  int start_b = 0;
+  const int total = locate_items(p, 4, -1, tmp, &start_b, &start_b);
+  {
+    // first item of sequence b
+    int carry = 0;
+    if (threadIdx.x == 0) tmp[4] = 0;
+    for (int base = 0; base < p.B; base += 256) {
+      const int bb = base + (int)threadIdx.x;
+      const int items = bb < p.B ? p.hgroups * seq_stages(p, p.context_lens[bb]) : 0;
+      int chunk_total;
+      const int excl = carry + block_excl_scan(items, tmp, 4, &chunk_total);
+      if (bb == b) tmp[4] = excl;
+      carry += chunk_total;
+    }
+    __syncthreads();
+    start_b = tmp[4];
+  }
   const int idx = blockIdx.y * 256 + threadIdx.x;
-  if (idx >= p.R * D) return;
-  const int r = idx / D, d = idx % D;
+  if (4 * idx >= p.R * D) return;
+  const int per = (total + p.nwg - 1) / p.nwg;
   const int L = p.context_lens[b];
-  const int ns = (L + p.split_tokens - 1) / p.split_tokens;
+  const int nst = seq_stages(p, L);
+  const int run_start = start_b + hg * nst;
+  const int r = 4 * idx / D, d = 4 * idx % D;
   const int i = r / p.G, h = hk * p.G + r % p.G;
-  _Float16* dst = p.out + (((size_t)b * p.next_n + i) * p.Hq + h) * D + d;
-  float mstar = -INFINITY, c2 = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const f4 rec = p.ws_ml[((size_t)(b * p.nsplit + s) * p.Hkv + hk) * p.R + r];
-    mstar = fmaxf(mstar, rec[0]);
-    c2 = rec[2];
+  float m = -INFINITY, l = 0.f;
+  f4 o = {0.f, 0.f, 0.f, 0.f};
+  if (nst > 0) {
+    const int w_first = run_start / per, w_last = (run_start + nst - 1) / per;
+    const int run = b * p.hgroups + hg;
+    const int nparts = (w_last - w_first + 1) * p.nsub;
+    constexpr int U = 4;
+    for (int k0 = 0; k0 < nparts; k0 += U) {
+      f4 rec[U], x[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        if (k0 + k < nparts) {
+          const int part = k0 + k;
+          const size_t u = part_index(p, run, w_first + part / p.nsub, hl, part % p.nsub);
+          rec[k] = p.ws_ml[u * p.R + r];
+          x[k] = *reinterpret_cast<const f4*>(p.ws_o + (u * p.R + r) * D + d);
+        } else {
+          rec[k] = f4{-INFINITY, 0.f, 0.f, 0.f};
+          x[k] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        if (rec[k][0] == -INFINITY) continue;  // a partial that saw no token
+        const float cc = rec[k][2];
+        const float mn = fmaxf(m, rec[k][0]);
+        const float a = m == -INFINITY ? 0.f : exp2f((m - mn) * cc);
+        const float bw = exp2f((rec[k][0] - mn) * cc);
+        l = l * a + rec[k][1] * bw;
+        o = o * a + x[k] * bw;
+        m = mn;
+      }
+    }
   }
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t u = (size_t)(b * p.nsplit + s) * p.Hkv + hk;
-    const f4 rec = p.ws_ml[u * p.R + r];
-    const float w = rec[0] == -INFINITY ? 0.f : exp2f((rec[0] - mstar) * c2);
-    l += w * rec[1];
-    o += w * p.ws_o[(u * p.R + r) * D + d];
-  }
-  float val = l > 0.f ? o / l : 0.f;
-  if (p.v_scale_mode == PA_SCALE_PER_TENSOR)
+  f4 val = l > 0.f ? o / l : f4{0.f, 0.f, 0.f, 0.f};
+  if (p.v_scale_mode == PA_SCALE_PER_TENSOR) {
     val *= p.v_scale[0];
-  else if (p.v_scale_mode == PA_SCALE_PER_CHANNEL)
-    val *= p.v_scale[hk * D + d];
-  *dst = (_Float16)val;
+  } else if (p.v_scale_mode == PA_SCALE_PER_CHANNEL) {
+    const float* vs = p.v_scale + hk * D + d;
+    val *= f4{vs[0], vs[1], vs[2], vs[3]};
+  }
+  _Float16* dst = p.out + (((size_t)b * p.next_n + i) * p.Hq + h) * D + d;
+  *reinterpret_cast<h4*>(dst) =
+      h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
 }
 
-// Planner probe: the entries the attention kernel walks, one thread per entry.
-__global__ void plan_dump_kernel(AttnParams p, int entries_per_unit, int32_t* entries) {
+// Planner probe: the page entries each sequence's tokens are read through, in
+// the logical order the kernel consumes them, padded to a multiple of 8 with
+// null entries {0, logical block, 0} that are never read [NULLPAD].
+__global__ void plan_dump_kernel(AttnParams p, int entries_per_seq, int pages_max,
+                                 int32_t* entries) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.B * p.nsplit * entries_per_unit;
+  const int64_t total = (int64_t)p.B * entries_per_seq;
   if (idx >= total) return;
-  const int e = idx % entries_per_unit;
-  const int unit = idx / entries_per_unit;
-  const int s = unit % p.nsplit, b = unit / p.nsplit;
+  const int e = idx % entries_per_seq;
+  const int b = idx / entries_per_seq;
   const int L = p.context_lens[b];
-  const int first_lblk = s * p.split_tokens / p.bs;
-  const PlanEntry x = plan_entry(p.block_table + (size_t)b * p.max_blocks, L, p.bs, first_lblk,
-                                 p.pages_per_split, e);
+  const PlanEntry x =
+      plan_entry(p.block_table + (size_t)b * p.max_blocks, L, p.bs, 0, pages_max, e);
   entries[idx * 3 + 0] = x.phys;
   entries[idx * 3 + 1] = x.lblk;
   entries[idx * 3 + 2] = (int32_t)x.mask;
@@ -343,10 +150,34 @@ __global__ void plan_dump_kernel(AttnParams p, int entries_per_unit, int32_t* en
 namespace {
 
 struct Shape {
-  int R, RT, RB, split, nsplit, pages_per_split, entries_per_unit;
-  int64_t units;
+  int R, RT, RB, hpu, hgroups, ts, nw, nsub, nwg;
+  int pages_max, entries_per_seq;
+  int64_t parts;
   size_t ml_bytes, o_bytes;
 };
+
+int gcd_int(int x, int y) { return y == 0 ? x : gcd_int(y, x % y); }
+
+int ilog2(int x) {  // x is a power of two
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+// Compute units of the current device (the persistent grid size), cached.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs) {
   if (!a) return fail(PA_ERR_INVALID_ARG, "paged_attn: args is NULL");
@@ -385,23 +216,29 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs) {
   sh->R = R;
   sh->RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   sh->RB = rb;
-  // Split size: from shapes only. Enough units to fill the chip several times,
-  // but a split long enough that its partial (R x D fp32) stays small against the
-  // KV bytes it reads.
-  const int64_t work = (int64_t)a->batch * a->num_kv_heads * (int64_t)a->max_context_len;
-  int64_t split = round_up(ceil_div(work > 0 ? work : 1, 4096), 32);
-  const int64_t min_split = ceil_div((int64_t)R * a->head_dim * 4 * 16, 2 * (int64_t)rb);
-  if (split < min_split) split = min_split;
-  if (split < 64) split = 64;
-  split = round_up(split, 32);
-  if (split > 1 << 20) split = 1 << 20;
-  sh->split = (int)split;
-  sh->nsplit = (int)(a->max_context_len > 0 ? ceil_div(a->max_context_len, split) : 1);
-  sh->pages_per_split = sh->split / a->block_size;
-  sh->entries_per_unit = (int)round_up(sh->pages_per_split, 8);
-  sh->units = (int64_t)a->batch * sh->nsplit * a->num_kv_heads;
-  sh->ml_bytes = (size_t)round_up(sh->units * R * 16, 256);
-  sh->o_bytes = (size_t)round_up(sh->units * R * a->head_dim * 4, 256);
+  // An item spans hpu KV heads (a divisor of the KV head count, at most 1 KiB
+  // of row bytes per token) and ts tokens, so that one stage (K and V) is at
+  // most 32 KiB and a workgroup has at most 8 waves of 16-token sub-tiles.
+  int hpu = gcd_int(a->num_kv_heads, kMaxWaves);
+  while (hpu > 1 && hpu * rb > 1024) hpu /= 2;
+  int ts = kStageMax / 2 / (hpu * rb);
+  if (ts > 64) ts = 64;
+  if (ts > 16 * kMaxWaves / hpu) ts = 16 * kMaxWaves / hpu;
+  if (ts < 16) ts = 16;
+  sh->hpu = hpu;
+  sh->hgroups = a->num_kv_heads / hpu;
+  sh->ts = ts;
+  sh->nsub = ts / 16;
+  sh->nw = hpu * sh->nsub;
+  sh->nwg = device_cus();
+  sh->pages_max = (int)ceil_div(a->max_context_len > 0 ? a->max_context_len : 1, a->block_size);
+  sh->entries_per_seq = (int)round_up(sh->pages_max, 8);
+  // partial slots: one per (run, workgroup) pair a run can span, at most
+  // runs + workgroups of them, each with one partial per wave
+  const int64_t slots = (int64_t)a->batch * sh->hgroups + sh->nwg;
+  sh->parts = slots * sh->nw;
+  sh->ml_bytes = (size_t)round_up(sh->parts * R * 16, 256);
+  sh->o_bytes = (size_t)round_up(sh->parts * R * a->head_dim * 4, 256);
   return PA_OK;
 }
 
@@ -425,9 +262,15 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   p.R = sh.R;
   p.bs = a->block_size;
   p.max_blocks = a->max_blocks_per_seq;
-  p.split_tokens = sh.split;
-  p.nsplit = sh.nsplit;
-  p.pages_per_split = sh.pages_per_split;
+  p.hpu = sh.hpu;
+  p.hgroups = sh.hgroups;
+  p.ts = sh.ts;
+  p.nw = sh.nw;
+  p.nsub = sh.nsub;
+  p.nwg = sh.nwg;
+  p.lbs = ilog2(a->block_size);
+  p.lts = ilog2(sh.ts);
+  p.lhpu = ilog2(sh.hpu);
   p.k_scale_mode = a->k_scale_mode;
   p.v_scale_mode = a->v_scale_mode;
   p.causal = a->causal ? 1 : 0;
@@ -435,45 +278,32 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   return p;
 }
 
-typedef void (*SplitFn)(AttnParams);
-
-template <int KIND, int D>
-SplitFn pick_rt(int RT, bool hilo) {
-  if (hilo) {
-    if constexpr (KIND == PA_KV_F16) return nullptr;
-    else {
-      if (RT == 1) return attn_split_kernel<KIND, D, 1, true>;
-      if (RT == 2) return attn_split_kernel<KIND, D, 2, true>;
-      return attn_split_kernel<KIND, D, 4, true>;
-    }
-  }
-  if (RT == 1) return attn_split_kernel<KIND, D, 1, false>;
-  if (RT == 2) return attn_split_kernel<KIND, D, 2, false>;
-  return attn_split_kernel<KIND, D, 4, false>;
-}
-
-template <int KIND>
-SplitFn pick_d(int D, int RT, bool hilo) {
-  if constexpr (KIND != PA_KV_INT4)
-    if (D == 64) return pick_rt<KIND, 64>(RT, hilo);
-  if (D == 128) return pick_rt<KIND, 128>(RT, hilo);
-  return pick_rt<KIND, 256>(RT, hilo);
-}
-
-SplitFn pick_split(int kind, int D, int RT, bool hilo) {
+RingFn pick_ring(int kind, int D, int nw, int RT, bool hilo) {
   switch (kind) {
-    case PA_KV_F16: return pick_d<PA_KV_F16>(D, RT, hilo);
-    case PA_KV_E4M3: return pick_d<PA_KV_E4M3>(D, RT, hilo);
-    case PA_KV_INT8: return pick_d<PA_KV_INT8>(D, RT, hilo);
-    case PA_KV_INT4: return pick_d<PA_KV_INT4>(D, RT, hilo);
+    case PA_KV_F16: return pick_ring_f16(D, nw, RT, hilo);
+    case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, hilo);
+    case PA_KV_INT8: return pick_ring_int8(D, nw, RT, hilo);
+    case PA_KV_INT4: return pick_ring_int4(D, nw, RT, hilo);
   }
   return nullptr;
 }
 
-SplitFn pick_merge(int D) {
-  if (D == 64) return attn_merge_kernel<64>;
-  if (D == 128) return attn_merge_kernel<128>;
-  return attn_merge_kernel<256>;
+// Enqueue the ring kernel and the merge for checked arguments.
+pa_status launch_attn(const pa_attn_args* a, const Shape& sh, void* workspace, hipStream_t s) {
+  const bool hilo = a->k_scale_mode == PA_SCALE_PER_CHANNEL;
+  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, hilo);
+  if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
+  AttnParams p = make_params(a, sh, workspace);
+  prof_begin(s);
+  hipLaunchKernelGGL(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), 0, s, p, a->block_table,
+                     a->context_lens);
+  prof_end(s);
+  pa_status st = launch_status("paged_attn ring kernel");
+  if (st != PA_OK) return st;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(a->batch * a->num_kv_heads),
+                     (unsigned)ceil_div((int64_t)sh.R * a->head_dim / 4, 256)), dim3(256), 0, s,
+                     p, a->head_dim);
+  return launch_status("paged_attn merge kernel");
 }
 
 }  // namespace
@@ -497,18 +327,7 @@ extern "C" pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace,
     return fail(PA_ERR_WORKSPACE, "paged_attn: workspace needs %zu bytes, got %zu",
                 sh.ml_bytes + sh.o_bytes, workspace_bytes);
   if (a->batch == 0) return PA_OK;
-  const bool hilo = a->k_scale_mode == PA_SCALE_PER_CHANNEL;
-  SplitFn fn = pick_split(a->kv_kind, a->head_dim, sh.RT, hilo);
-  if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
-  AttnParams p = make_params(a, sh, workspace);
-  hipStream_t s = (hipStream_t)stream;
-  prof_begin(s);
-  hipLaunchKernelGGL(fn, dim3((unsigned)sh.units), dim3(64), 0, s, p);
-  prof_end(s);
-  if ((st = launch_status("paged_attn split kernel")) != PA_OK) return st;
-  hipLaunchKernelGGL(pick_merge(a->head_dim), dim3((unsigned)(a->batch * a->num_kv_heads),
-                     (unsigned)ceil_div((int64_t)sh.R * a->head_dim, 256)), dim3(256), 0, s, p);
-  return launch_status("paged_attn merge kernel");
+  return launch_attn(a, sh, workspace, (hipStream_t)stream);
 }
 
 extern "C" pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t max_entries,
@@ -516,12 +335,12 @@ extern "C" pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t ma
   Shape sh;
   pa_status st = check_args(a, &sh, false);
   if (st != PA_OK) return st;
-  const int64_t total = (int64_t)a->batch * sh.nsplit * sh.entries_per_unit;
+  const int64_t total = (int64_t)a->batch * sh.entries_per_seq;
   if (info) {
-    info[0] = sh.split;
-    info[1] = sh.nsplit;
-    info[2] = sh.entries_per_unit;
-    info[3] = 0;
+    info[0] = sh.pages_max * a->block_size;
+    info[1] = 1;
+    info[2] = sh.entries_per_seq;
+    info[3] = sh.ts;
   }
   if (!entries) {
     if (!info) return fail(PA_ERR_INVALID_ARG, "pa_plan: entries and info both NULL");
@@ -533,6 +352,6 @@ extern "C" pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t ma
   AttnParams p = make_params(a, sh, nullptr);
   if (total > 0)
     hipLaunchKernelGGL(plan_dump_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
-                       (hipStream_t)stream, p, sh.entries_per_unit, entries);
+                       (hipStream_t)stream, p, sh.entries_per_seq, sh.pages_max, entries);
   return launch_status("pa_plan kernel");
 }

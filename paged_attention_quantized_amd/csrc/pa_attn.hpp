@@ -1,0 +1,582 @@
+// pa_attn.hpp -- device side of the paged attention kernels (shared by the
+// per-KV-kind translation units and the host part in pa_attn.hip). The design
+// is described at the top of pa_attn.hip.
+#pragma once
+
+#include <math.h>
+
+#include "pa_device.hpp"
+
+namespace pa {
+
+constexpr int kStages = 4;             // LDS ring depth
+constexpr int kStageMax = 32 * 1024;   // bytes per stage (K and V planes)
+constexpr int kMaxWaves = 8;           // wavefronts per workgroup
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+struct AttnParams {
+  _Float16* out;
+  const _Float16* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  f4* ws_ml;     // [partials, R] (m_raw, l, c, 0)
+  float* ws_o;   // [partials, R, D]
+  int B, next_n, Hq, Hkv, G, R, bs, max_blocks;
+  int hpu, hgroups, ts, nw, nsub;  // heads per item, head groups, tokens per item, waves, sub-tiles
+  int nwg;                         // workgroups of the persistent grid
+  int lbs, lts, lhpu;              // log2 of bs, ts, hpu (all powers of two)
+  int k_scale_mode, v_scale_mode, causal;
+  float softmax_scale;
+};
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// items of one sequence for one head group
+__device__ __forceinline__ int seq_stages(const AttnParams& p, int L) {
+  return (L + p.ts - 1) >> p.lts;
+}
+
+// Exclusive prefix sum over the nw waves of the workgroup; *total gets the
+// sum. Uses lds_tmp[0 .. nw) and leaves it free (ends with a barrier).
+__device__ int block_excl_scan(int x, int* lds_tmp, int nw, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int y = __shfl_up(incl, m, 64);
+    if (lane >= m) incl += y;
+  }
+  if (lane == 63) lds_tmp[wv] = incl;
+  __syncthreads();
+  int before = 0, t = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int v = lds_tmp[i];
+    before += i < wv ? v : 0;
+    t += v;
+  }
+  __syncthreads();
+  *total = t;
+  return before + incl - x;
+}
+
+// Item count of the whole batch; with target >= 0 also the sequence holding
+// item `target` (*b_out) and that sequence's first item index (*start_out).
+// All threads of the workgroup call it; uses lds_tmp[0 .. nw + 2).
+__device__ int locate_items(const AttnParams& p, int nw, int target, int* lds_tmp, int* b_out,
+                            int* start_out) {
+  const int nt = 64 * nw;
+  int carry = 0;
+  if (threadIdx.x == 0) lds_tmp[nw] = 0;
+  for (int base = 0; base < p.B; base += nt) {
+    const int b = base + (int)threadIdx.x;
+    const int items = b < p.B ? p.hgroups * seq_stages(p, p.context_lens[b]) : 0;
+    int chunk_total;
+    const int excl = carry + block_excl_scan(items, lds_tmp, nw, &chunk_total);
+    if (target >= 0 && items > 0 && excl <= target && target < excl + items) {
+      lds_tmp[nw] = b;
+      lds_tmp[nw + 1] = excl;
+    }
+    carry += chunk_total;
+  }
+  __syncthreads();
+  if (target >= 0) {
+    *b_out = lds_tmp[nw];
+    *start_out = lds_tmp[nw + 1];
+  }
+  __syncthreads();
+  return carry;
+}
+
+// Position of one item in the (sequence, head group, stage) order; all fields
+// are workgroup-uniform.
+struct ItemPos {
+  int b, L, nst, hg, k;
+};
+
+__device__ __forceinline__ void item_next(const AttnParams& p, const int32_t* __restrict__ lens,
+                                          ItemPos& it) {
+  if (++it.k < it.nst) return;
+  it.k = 0;
+  if (++it.hg < p.hgroups) return;
+  it.hg = 0;
+  do {
+    ++it.b;
+    it.L = it.b < p.B ? lens[uni(it.b)] : 0;
+    it.nst = seq_stages(p, it.L);
+  } while (it.nst == 0 && it.b < p.B);
+}
+
+template <int KIND, int D>
+struct Geo {
+  static constexpr int BITS = Kv<KIND>::kBits;
+  static constexpr int RB = D * BITS / 8;   // bytes per (token, head) row
+  static constexpr int CPR = RB / 16;       // 16-byte pieces per row
+  static constexpr int NJ = RB / 64;        // K pieces per lane per token
+  static constexpr int EPC = 128 / BITS;    // elements per 16-byte piece
+  static constexpr int KPC = EPC / 8;       // MFMA k-steps (8 channels per lane) per piece
+  static constexpr int KS = D / 32;         // k-steps of QK
+  static constexpr int DV = D / 16;         // channels each lane owns for V
+  static constexpr int VB = RB / 16;        // V bytes per lane per token
+  static constexpr int VDW = VB / 4;
+  static constexpr int NL = RB / 32;        // ring loads per thread per stage
+  static_assert(RB % 64 == 0, "row bytes must be a multiple of 64");
+  static_assert(NJ * KPC == KS, "k-step bookkeeping");
+  static_assert(VB <= 16 || VB % 16 == 0, "V bytes per lane");
+};
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes lds_base + 16 * i (lds_base is wave-uniform). Kept out of templates:
+// the LDS address-space cast is device-only.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   0);
+}
+
+// Per-thread constants of the ring loads. Load l of wave wv covers stage pieces
+// [(l*nw + wv)*64, +64): one plane, and whole rows of tpi = 1024 / (hpu*RB)
+// consecutive tokens starting at tau0 (tpi divides ts and bs, so the 1 KiB a
+// load covers never crosses a page). voff is the lane's byte offset from the
+// row block of token tau0, head 0 of the group; tau0 and plane are uniform.
+template <int KIND, int D>
+struct LoadPlan {
+  uint32_t voff[Geo<KIND, D>::NL];
+  int tau0[Geo<KIND, D>::NL];
+  int plane[Geo<KIND, D>::NL];
+};
+
+template <int KIND, int D>
+__device__ __forceinline__ void make_load_plan(const AttnParams& p, LoadPlan<KIND, D>& lp) {
+  using G_ = Geo<KIND, D>;
+  const int lane = threadIdx.x & 63, wv = uni(threadIdx.x >> 6);
+  const int plane_pieces = (p.ts * G_::CPR) << p.lhpu;
+  const uint32_t tok_stride = (uint32_t)p.Hkv * G_::RB;
+#pragma unroll
+  for (int l = 0; l < G_::NL; ++l) {
+    const int cb = (l * p.nw + wv) * 64;                 // first piece of the load (uniform)
+    const int plane = cb >= plane_pieces ? 1 : 0;
+    const int ccb = cb - plane * plane_pieces;
+    const int tau0 = (ccb / G_::CPR) >> p.lhpu;
+    const int cc = ccb + lane;
+    const int row = cc / G_::CPR, pos = cc % G_::CPR;
+    const int tau = row >> p.lhpu, hl = row & ((1 << p.lhpu) - 1);
+    const int j = pos ^ (tau & (G_::CPR - 1));
+    lp.voff[l] = (uint32_t)(tau - tau0) * tok_stride + (uint32_t)hl * G_::RB + 16u * j;
+    lp.tau0[l] = tau0;
+    lp.plane[l] = plane;
+  }
+}
+
+// Issue the ring loads of one item into `slot`. Every thread issues exactly NL
+// loads whether the item is live or not. Stage layout: K plane then V plane,
+// each [TS tokens][HPU heads][CPR pieces]; piece j of row (tau, hl) is stored
+// at position j ^ (tau & (CPR - 1)). Each load's address is a scalar page base
+// (one scalar block-table load per load) plus the lane's constant offset. A
+// page past the sequence end is replaced by the last real page, whose bytes
+// only feed masked tokens.
+template <int KIND, int D>
+__device__ __forceinline__ void issue_stage(const AttnParams& p,
+                                            const int32_t* __restrict__ table, const ItemPos& it,
+                                            bool live, const LoadPlan<KIND, D>& lp,
+                                            uint8_t* slot) {
+  using G_ = Geo<KIND, D>;
+  const int wv = uni(threadIdx.x >> 6);
+  if (live) {
+    const int t0 = it.k << p.lts;
+    const int toff = t0 & ((1 << p.lbs) - 1);  // 0 unless a page holds several items
+    const int blk0 = t0 >> p.lbs;
+    const int last_blk = (it.L - 1) >> p.lbs;
+    const int32_t* table_row = table + (size_t)it.b * p.max_blocks;
+    const size_t tok_stride = (size_t)p.Hkv * G_::RB;
+    const size_t page_stride = tok_stride << p.lbs;
+    const size_t head_off = ((size_t)it.hg * G_::RB) << p.lhpu;
+    int phys[G_::NL];
+#pragma unroll
+    for (int l = 0; l < G_::NL; ++l)
+      phys[l] = table_row[min(blk0 + ((toff + lp.tau0[l]) >> p.lbs), last_blk)];
+#pragma unroll
+    for (int l = 0; l < G_::NL; ++l) {
+      const int sl = (toff + lp.tau0[l]) & ((1 << p.lbs) - 1);
+      const uint8_t* sbase = (lp.plane[l] ? p.v_cache : p.k_cache) +
+                             (size_t)phys[l] * page_stride + (size_t)sl * tok_stride + head_off;
+      dma16(sbase + lp.voff[l], slot + (l * p.nw + wv) * 1024);
+    }
+  } else {
+    // past the end of the range: the same number of loads, of 16 readable
+    // bytes, into a slot nobody reads
+    const uint8_t* sbase = reinterpret_cast<const uint8_t*>(p.q);
+#pragma unroll
+    for (int l = 0; l < G_::NL; ++l)
+      dma16(sbase, slot + (l * p.nw + wv) * 1024);
+  }
+}
+
+// Softmax state and Q' operands of one wave.
+template <int KIND, int D, int RT, bool HILO>
+struct WaveState {
+  h8 qa[RT][Geo<KIND, D>::KS];
+  h8 qb[RT][HILO ? Geo<KIND, D>::KS : 1];
+  f4 o[RT][Geo<KIND, D>::DV];
+  float m_run[RT], l_run[RT];
+  int lim[RT];  // query row 16*rt+n sees tokens t <= lim
+};
+
+// Load Q' of (sequence b, KV head hk) and reset the softmax state.
+template <int KIND, int D, int RT, bool HILO>
+__device__ __forceinline__ void start_run(const AttnParams& p, int b, int hk, int L, float inv_m,
+                                          float sgn, WaveState<KIND, D, RT, HILO>& w) {
+  using G_ = Geo<KIND, D>;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = 16 * rt + n;
+    const bool rv = r < p.R;
+    const int i = r / p.G, hg = r % p.G;
+    const _Float16* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
+#pragma unroll
+    for (int ks = 0; ks < G_::KS; ++ks) {
+      const int j = ks / G_::KPC, u = ks % G_::KPC;
+      const int d0 = (g + 4 * j) * G_::EPC + 8 * u;
+      h8 v = {};
+      if (rv) v = *reinterpret_cast<const h8*>(qrow + d0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = d0 + run_elem<KIND>(e);
+        const float x = (float)v[run_elem<KIND>(e)];
+        if constexpr (HILO) {
+          const float xf = x * (p.k_scale[hk * D + d] * inv_m) * sgn;
+          const _Float16 hi = (_Float16)xf;
+          w.qa[rt][ks][e] = hi;
+          w.qb[rt][ks][e] = (_Float16)(xf - (float)hi);
+        } else {
+          w.qa[rt][ks][e] = (_Float16)(x * sgn);
+        }
+      }
+    }
+    w.m_run[rt] = -INFINITY;
+    w.l_run[rt] = 0.f;
+#pragma unroll
+    for (int q = 0; q < G_::DV; ++q) w.o[rt][q] = f4{0.f, 0.f, 0.f, 0.f};
+    w.lim[rt] = p.causal ? (L - p.next_n + i) : 0x7fffffff;
+  }
+}
+
+// LDS byte offsets (within a stage) of the pieces a lane reads in
+// compute_tile: K pieces g + 4j of token 16*st + n, and V bytes
+// [n*VB, n*VB + VB) of tokens 16*st + 4g + e, both for head hl.
+template <int KIND, int D>
+struct TileOffs {
+  static constexpr int VP = Geo<KIND, D>::VB >= 16 ? Geo<KIND, D>::VB / 16 : 1;
+  int k[Geo<KIND, D>::NJ];
+  int v[4][VP];
+};
+
+template <int KIND, int D>
+__device__ __forceinline__ void make_tile_offs(const AttnParams& p, int st, int hl,
+                                               TileOffs<KIND, D>& to) {
+  using G_ = Geo<KIND, D>;
+  constexpr int CPR = G_::CPR, RB = G_::RB, VB = G_::VB;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int plane_bytes = (p.ts * RB) << p.lhpu;
+  {
+    const int tau = 16 * st + n;
+    const int row = ((tau << p.lhpu) + hl) * RB;
+#pragma unroll
+    for (int j = 0; j < G_::NJ; ++j) to.k[j] = row + 16 * ((g + 4 * j) ^ (tau & (CPR - 1)));
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int tau = 16 * st + 4 * g + e;
+    const int row = plane_bytes + ((tau << p.lhpu) + hl) * RB;
+    const int byte = n * VB;
+#pragma unroll
+    for (int pp = 0; pp < TileOffs<KIND, D>::VP; ++pp)
+      to.v[e][pp] = row + 16 * ((byte / 16 + pp) ^ (tau & (CPR - 1))) + (VB < 16 ? byte % 16 : 0);
+  }
+}
+
+// max over the four 16-lane rows of the wave (lanes n, n+16, n+32, n+48)
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// One 16-token sub-tile (tokens t0 .. t0 + 15) of the wave's head from a ring slot.
+template <int KIND, int D, int RT, bool HILO>
+__device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs<KIND, D>& to,
+                                             int t0, int L, float c2,
+                                             WaveState<KIND, D, RT, HILO>& w) {
+  using G_ = Geo<KIND, D>;
+  constexpr int KS = G_::KS, NJ = G_::NJ, KPC = G_::KPC, EPC = G_::EPC, DV = G_::DV;
+  constexpr int VDW = G_::VDW, VB = G_::VB;
+  const int lane = threadIdx.x & 63, g = lane >> 4;
+
+  // ---- K operand: lane (n, g) holds token n, pieces g + 4j ----
+  h8 kop[KS];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const u4 raw = *reinterpret_cast<const u4*>(slot + to.k[j]);
+    _Float16 hv[EPC];
+    uint32_t wd[4] = {raw[0], raw[1], raw[2], raw[3]};
+    decode_run<KIND, 4>(wd, hv);
+#pragma unroll
+    for (int u = 0; u < KPC; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kop[j * KPC + u][e] = hv[8 * u + e];
+  }
+  // ---- V codes: lane (n, g) holds tokens 4g + e, row bytes [n*VB, n*VB + VB) ----
+  uint32_t vraw[4][VDW];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (VB >= 16) {
+#pragma unroll
+      for (int pp = 0; pp < VB / 16; ++pp) {
+        const u4 x = *reinterpret_cast<const u4*>(slot + to.v[e][pp]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vraw[e][4 * pp + k] = x[k];
+      }
+    } else if constexpr (VDW == 2) {
+      const u2 x = *reinterpret_cast<const u2*>(slot + to.v[e][0]);
+      vraw[e][0] = x[0];
+      vraw[e][1] = x[1];
+    } else {
+      vraw[e][0] = *reinterpret_cast<const uint32_t*>(slot + to.v[e][0]);
+    }
+    // tokens past the end: zero their V codes by select, so no 0 * NaN can
+    // reach O [NULLPAD, Fix]
+    const bool ok = t0 + 4 * g + e < L;
+#pragma unroll
+    for (int k = 0; k < VDW; ++k) vraw[e][k] = ok ? vraw[e][k] : 0u;
+  }
+
+  f4 sacc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qa[rt][ks], acc, 0, 0, 0);
+      if constexpr (HILO)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qb[rt][ks], acc, 0, 0, 0);
+    }
+    sacc[rt] = acc;
+  }
+
+  // ---- online softmax (query row = lane column n) ----
+  h4 pb[RT];
+  bool rescale = false;
+  float alpha[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    bool okv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = t0 + 4 * g + e;
+      okv[e] = t < L && t <= w.lim[rt];
+      mx = okv[e] ? fmaxf(mx, sacc[rt][e]) : mx;
+    }
+    mx = rows_max(mx);
+    const float m_old = w.m_run[rt];
+    const float m_new = fmaxf(m_old, mx);
+    // the state needs rescaling only when a row that has seen tokens gets a
+    // larger max; a row that has seen nothing holds zeros
+    alpha[rt] = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - m_new) * c2);
+    rescale |= m_old != m_new && m_old != -INFINITY;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 ph =
+          okv[e] ? (_Float16)__builtin_amdgcn_exp2f((sacc[rt][e] - m_new) * c2) : (_Float16)0.f;
+      pb[rt][e] = ph;
+      psum += (float)ph;
+    }
+    w.l_run[rt] = alpha[rt] * w.l_run[rt] + psum;
+    w.m_run[rt] = m_new;
+  }
+  if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int q = 0; q < DV; ++q) w.o[rt][q] *= alpha[rt];
+  }
+
+  // ---- O^T += V^T P^T ----
+  _Float16 vh[4][DV];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) decode_run<KIND, VDW>(vraw[e], vh[e]);
+#pragma unroll
+  for (int q = 0; q < DV; ++q) {
+    const h4 vop = {vh[0][q], vh[1][q], vh[2][q], vh[3][q]};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pb[rt], w.o[rt][q], 0, 0, 0);
+  }
+}
+
+// Partial index of (run r, workgroup w, head-in-group hl, sub-tile st); run
+// r = b * hgroups + hg. Slot r + w is unique: a later workgroup only reaches
+// later runs, so (r, w) != (r', w') with r + w == r' + w' cannot both occur.
+__device__ __forceinline__ size_t part_index(const AttnParams& p, int r, int w, int hl, int st) {
+  return ((size_t)(r + w) * p.hpu + hl) * p.nsub + st;
+}
+
+template <int KIND, int D, int RT, bool HILO>
+__device__ __forceinline__ void write_partial(const AttnParams& p, size_t u, float c2,
+                                              const WaveState<KIND, D, RT, HILO>& w) {
+  constexpr int DV = Geo<KIND, D>::DV;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float l = w.l_run[rt];
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    const int r = 16 * rt + n;
+    if (r < p.R) {
+      if (g == 0) p.ws_ml[u * p.R + r] = f4{w.m_run[rt], l, c2, 0.f};
+      float* orow = p.ws_o + (u * p.R + r) * D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float tmp[DV];
+#pragma unroll
+        for (int q = 0; q < DV; ++q) tmp[run_elem<KIND>(q)] = w.o[rt][q][e];
+#pragma unroll
+        for (int k = 0; k < DV; k += 4)
+          *reinterpret_cast<f4*>(orow + DV * (4 * g + e) + k) =
+              f4{tmp[k], tmp[k + 1], tmp[k + 2], tmp[k + 3]};
+      }
+    }
+  }
+}
+
+template <int KIND, int D, int RT, bool HILO, int NWB>
+__global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
+    AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens) {
+  using G_ = Geo<KIND, D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageMax];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int hl = wv & (p.hpu - 1), st = wv >> p.lhpu;
+  const int stage_bytes = (2 * p.ts * G_::RB) << p.lhpu;
+  int* scratch = reinterpret_cast<int*>(ring);
+
+  // ---- this workgroup's item range ----
+  int b0 = 0, start0 = 0;
+  const int total = locate_items(p, p.nw, -1, scratch, &b0, &start0);
+  const int per = (total + p.nwg - 1) / p.nwg;
+  const int i0 = (int)blockIdx.x * per;
+  const int i1 = min(i0 + per, total);
+  if (i0 >= i1) return;
+  locate_items(p, p.nw, i0, scratch, &b0, &start0);
+  ItemPos cp;
+  cp.b = uni(b0);
+  cp.L = lens[cp.b];
+  cp.nst = seq_stages(p, cp.L);
+  cp.hg = (i0 - uni(start0)) / cp.nst;
+  cp.k = (i0 - uni(start0)) % cp.nst;
+  const int nitems = i1 - i0;
+
+  // ---- scale constants: fold normalizer for PER_CHANNEL K [FOLD, Approach] ----
+  float qk, inv_m = 0.f;
+  if constexpr (HILO) {
+    float mx = 0.f;
+    for (int i = lane; i < p.Hkv * D; i += 64) mx = fmaxf(mx, fabsf(p.k_scale[i]));
+    mx = wave_max(mx);
+    inv_m = mx > 0.f ? 1.0f / mx : 0.f;
+    qk = p.softmax_scale * mx;
+  } else {
+    qk = p.softmax_scale * (p.k_scale_mode == PA_SCALE_PER_TENSOR ? p.k_scale[0] : 1.0f);
+  }
+  const float sgn = qk < 0.f ? -1.f : 1.f;
+  const float c2 = fabsf(qk) * kLog2e;
+
+  LoadPlan<KIND, D> lp;
+  make_load_plan<KIND, D>(p, lp);
+  TileOffs<KIND, D> to;
+  make_tile_offs<KIND, D>(p, st, hl, to);
+
+  // Q' of the first run is loaded before the ring starts, so waiting for it
+  // never waits for ring loads.
+  WaveState<KIND, D, RT, HILO> w;
+  start_run<KIND, D, RT, HILO>(p, cp.b, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
+
+  // ---- ring prologue: kStages - 1 items in flight ----
+  ItemPos ld = cp;
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j) {
+    const bool live = j < nitems;
+    issue_stage<KIND, D>(p, table, ld, live, lp, ring + j * stage_bytes);
+    if (live) item_next(p, lens, ld);
+  }
+
+  for (int j = 0; j < nitems; ++j) {
+    // item j has landed for every wave, and every wave is done with item j - 1
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * G_::NL) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    {
+      const int jn = j + kStages - 1;
+      const bool live = jn < nitems;
+      issue_stage<KIND, D>(p, table, ld, live, lp, ring + (jn % kStages) * stage_bytes);
+      if (live) item_next(p, lens, ld);
+    }
+    const int t0 = (cp.k << p.lts) + 16 * st;
+    if (t0 < cp.L)
+      compute_tile<KIND, D, RT, HILO>(ring + (j % kStages) * stage_bytes, to, t0, cp.L, c2, w);
+    // end of a (sequence, head group) run inside this range: write the partial
+    const int b = cp.b, hg = cp.hg;
+    item_next(p, lens, cp);
+    if (j + 1 == nitems || cp.b != b || cp.hg != hg) {
+      write_partial<KIND, D, RT, HILO>(p, part_index(p, b * p.hgroups + hg, blockIdx.x, hl, st),
+                                       c2, w);
+      if (j + 1 < nitems)
+        start_run<KIND, D, RT, HILO>(p, cp.b, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+typedef void (*RingFn)(AttnParams, const int32_t*, const int32_t*);
+
+// NWB: the launch bound in waves (4 or 8); a 4-wave workgroup gets twice the
+// registers per wave.
+template <int KIND, int D, int NWB>
+RingFn pick_rt(int RT, bool hilo) {
+  if (hilo) {
+    if constexpr (KIND == PA_KV_F16) return nullptr;
+    else {
+      if (RT == 1) return attn_ring_kernel<KIND, D, 1, true, NWB>;
+      if (RT == 2) return attn_ring_kernel<KIND, D, 2, true, NWB>;
+      return attn_ring_kernel<KIND, D, 4, true, NWB>;
+    }
+  }
+  if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB>;
+  if (RT == 2) return attn_ring_kernel<KIND, D, 2, false, NWB>;
+  return attn_ring_kernel<KIND, D, 4, false, NWB>;
+}
+
+template <int KIND, int D>
+RingFn pick_nw(int nw, int RT, bool hilo) {
+  return nw <= 4 ? pick_rt<KIND, D, 4>(RT, hilo) : pick_rt<KIND, D, 8>(RT, hilo);
+}
+
+template <int KIND>
+RingFn pick_d(int D, int nw, int RT, bool hilo) {
+  if constexpr (KIND != PA_KV_INT4)
+    if (D == 64) return pick_nw<KIND, 64>(nw, RT, hilo);
+  if (D == 128) return pick_nw<KIND, 128>(nw, RT, hilo);
+  return pick_nw<KIND, 256>(nw, RT, hilo);
+}
+
+// Ring kernel of one KV kind (each defined in its own translation unit).
+RingFn pick_ring_f16(int D, int nw, int RT, bool hilo);
+RingFn pick_ring_e4m3(int D, int nw, int RT, bool hilo);
+RingFn pick_ring_int8(int D, int nw, int RT, bool hilo);
+RingFn pick_ring_int4(int D, int nw, int RT, bool hilo);
+
+}  // namespace pa

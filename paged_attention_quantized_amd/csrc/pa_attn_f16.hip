@@ -1,0 +1,8 @@
+// pa_attn_f16.hip -- paged attention ring kernels for fp16 KV caches.
+#include "pa_attn.hpp"
+
+namespace pa {
+
+RingFn pick_ring_f16(int D, int nw, int RT, bool hilo) { return pick_d<PA_KV_F16>(D, nw, RT, hilo); }
+
+}  // namespace pa

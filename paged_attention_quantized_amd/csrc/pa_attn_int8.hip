@@ -1,0 +1,8 @@
+// pa_attn_int8.hip -- paged attention ring kernels for INT8 KV caches.
+#include "pa_attn.hpp"
+
+namespace pa {
+
+RingFn pick_ring_int8(int D, int nw, int RT, bool hilo) { return pick_d<PA_KV_INT8>(D, nw, RT, hilo); }
+
+}  // namespace pa
