@@ -261,11 +261,12 @@ const char* pa_last_error(void);
 
 /*
  * Profiling hook for benchmarks: while set, every later paged_attn_fwd /
- * paged_mqa_logits call on the calling thread records start_event on its
- * stream right before its dominant kernel (the split-KV attention kernel,
- * the logits kernel) and stop_event right after it. Both are hipEvent_t
- * handles owned by the caller; pass NULL, NULL to clear. Returns
- * PA_ERR_INVALID_ARG if exactly one is NULL.
+ * paged_mqa_logits call on the calling thread launches its dominant kernel
+ * (the attention ring kernel, the logits kernel) with start_event and
+ * stop_event attached to that kernel's dispatch (hipExtLaunchKernelGGL), so
+ * the pair measures the kernel alone. Both are hipEvent_t handles owned by the
+ * caller; pass NULL, NULL to clear. Returns PA_ERR_INVALID_ARG if exactly one
+ * is NULL.
  */
 pa_status pa_set_profile_events(void* start_event, void* stop_event);
 

@@ -47,52 +47,37 @@ namespace pa {
 // Combine the partials of each (sequence b, KV head hk) in a fixed order
 // (workgroup, then sub-tile), which depends on logical positions only [RELOC],
 // and apply the V scale and 1/l. A row with no visible token is +0. One thread
-// per 4 output channels; the item ranges of the ring kernel are recomputed
-// from context_lens.
+// per 4 output channels; the item ranges of the ring kernel follow from the
+// sequence starts it published.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
-  __shared__ int tmp[8];
   const int bh = blockIdx.x;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
-  const int hg = hk / p.hpu, hl = hk % p.hpu;
-  int start_b = 0;
-  const int total = locate_items(p, 4, -1, tmp, &start_b, &start_b);
-  {
-    // first item of sequence b
-    int carry = 0;
-    if (threadIdx.x == 0) tmp[4] = 0;
-    for (int base = 0; base < p.B; base += 256) {
-      const int bb = base + (int)threadIdx.x;
-      const int items = bb < p.B ? p.hgroups * seq_stages(p, p.context_lens[bb]) : 0;
-      int chunk_total;
-      const int excl = carry + block_excl_scan(items, tmp, 4, &chunk_total);
-      if (bb == b) tmp[4] = excl;
-      carry += chunk_total;
-    }
-    __syncthreads();
-    start_b = tmp[4];
-  }
+  const int hg = hk >> p.lhpu, hl = hk & (p.hpu - 1);
   const int idx = blockIdx.y * 256 + threadIdx.x;
   if (4 * idx >= p.R * D) return;
+  const int total = p.ws_seq[p.B];
+  const int start_b = p.ws_seq[b];
   const int per = (total + p.nwg - 1) / p.nwg;
   const int L = p.context_lens[b];
   const int nst = seq_stages(p, L);
   const int run_start = start_b + hg * nst;
   const int r = 4 * idx / D, d = 4 * idx % D;
   const int i = r / p.G, h = hk * p.G + r % p.G;
+  const int nsub = p.wgmerge ? 1 : p.nsub;
   float m = -INFINITY, l = 0.f;
   f4 o = {0.f, 0.f, 0.f, 0.f};
   if (nst > 0) {
     const int w_first = run_start / per, w_last = (run_start + nst - 1) / per;
     const int run = b * p.hgroups + hg;
-    const int nparts = (w_last - w_first + 1) * p.nsub;
-    constexpr int U = 4;
+    const int nparts = (w_last - w_first + 1) * nsub;
+    constexpr int U = 8;
     for (int k0 = 0; k0 < nparts; k0 += U) {
       f4 rec[U], x[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         if (k0 + k < nparts) {
           const int part = k0 + k;
-          const size_t u = part_index(p, run, w_first + part / p.nsub, hl, part % p.nsub);
+          const size_t u = part_index(p, run, w_first + part / nsub, hl, part % nsub);
           rec[k] = p.ws_ml[u * p.R + r];
           x[k] = *reinterpret_cast<const f4*>(p.ws_o + (u * p.R + r) * D + d);
         } else {
@@ -152,8 +137,9 @@ namespace {
 struct Shape {
   int R, RT, RB, hpu, hgroups, ts, nw, nsub, nwg;
   int pages_max, entries_per_seq;
+  int wgmerge;
   int64_t parts;
-  size_t ml_bytes, o_bytes;
+  size_t ml_bytes, o_bytes, seq_bytes;
 };
 
 int gcd_int(int x, int y) { return y == 0 ? x : gcd_int(y, x % y); }
@@ -233,12 +219,18 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs) {
   sh->nwg = device_cus();
   sh->pages_max = (int)ceil_div(a->max_context_len > 0 ? a->max_context_len : 1, a->block_size);
   sh->entries_per_seq = (int)round_up(sh->pages_max, 8);
+  // Sub-tile states are merged inside the workgroup when one head's state (in
+  // the MFMA layout: 16*RT rows x D fp32, plus m and l) fits the LDS exchange
+  // buffer.
+  const int xch_per_head = sh->RT * (a->head_dim / 16) * 1024 + sh->RT * 512;
+  sh->wgmerge = (sh->nsub > 1 && xch_per_head <= kXchBytes) ? 1 : 0;
   // partial slots: one per (run, workgroup) pair a run can span, at most
-  // runs + workgroups of them, each with one partial per wave
+  // runs + workgroups of them, each with one partial per head and sub-tile
   const int64_t slots = (int64_t)a->batch * sh->hgroups + sh->nwg;
   sh->parts = slots * sh->nw;
   sh->ml_bytes = (size_t)round_up(sh->parts * R * 16, 256);
   sh->o_bytes = (size_t)round_up(sh->parts * R * a->head_dim * 4, 256);
+  sh->seq_bytes = (size_t)round_up(((int64_t)a->batch + 1) * 4, 256);
   return PA_OK;
 }
 
@@ -254,6 +246,7 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   p.context_lens = a->context_lens;
   p.ws_ml = (f4*)ws;
   p.ws_o = (float*)((char*)ws + sh.ml_bytes);
+  p.ws_seq = (int*)((char*)ws + sh.ml_bytes + sh.o_bytes);
   p.B = a->batch;
   p.next_n = a->next_n;
   p.Hq = a->num_q_heads;
@@ -271,6 +264,7 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   p.lbs = ilog2(a->block_size);
   p.lts = ilog2(sh.ts);
   p.lhpu = ilog2(sh.hpu);
+  p.wgmerge = sh.wgmerge;
   p.k_scale_mode = a->k_scale_mode;
   p.v_scale_mode = a->v_scale_mode;
   p.causal = a->causal ? 1 : 0;
@@ -294,10 +288,8 @@ pa_status launch_attn(const pa_attn_args* a, const Shape& sh, void* workspace, h
   RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, hilo);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
   AttnParams p = make_params(a, sh, workspace);
-  prof_begin(s);
-  hipLaunchKernelGGL(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), 0, s, p, a->block_table,
-                     a->context_lens);
-  prof_end(s);
+  launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), s, p, a->block_table,
+               a->context_lens);
   pa_status st = launch_status("paged_attn ring kernel");
   if (st != PA_OK) return st;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(a->batch * a->num_kv_heads),
@@ -315,7 +307,7 @@ using namespace pa;
 extern "C" size_t paged_attn_workspace_size(const pa_attn_args* a) {
   Shape sh;
   if (check_args(a, &sh, false) != PA_OK) return 0;
-  return sh.ml_bytes + sh.o_bytes;
+  return sh.ml_bytes + sh.o_bytes + sh.seq_bytes;
 }
 
 extern "C" pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace,
@@ -323,9 +315,10 @@ extern "C" pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace,
   Shape sh;
   pa_status st = check_args(a, &sh, true);
   if (st != PA_OK) return st;
-  if (workspace_bytes < sh.ml_bytes + sh.o_bytes || !workspace)
-    return fail(PA_ERR_WORKSPACE, "paged_attn: workspace needs %zu bytes, got %zu",
-                sh.ml_bytes + sh.o_bytes, workspace_bytes);
+  const size_t ws_need = sh.ml_bytes + sh.o_bytes + sh.seq_bytes;
+  if (workspace_bytes < ws_need || !workspace)
+    return fail(PA_ERR_WORKSPACE, "paged_attn: workspace needs %zu bytes, got %zu", ws_need,
+                workspace_bytes);
   if (a->batch == 0) return PA_OK;
   return launch_attn(a, sh, workspace, (hipStream_t)stream);
 }

@@ -12,6 +12,7 @@ namespace pa {
 constexpr int kStages = 4;             // LDS ring depth
 constexpr int kStageMax = 32 * 1024;   // bytes per stage (K and V planes)
 constexpr int kMaxWaves = 8;           // wavefronts per workgroup
+constexpr int kXchBytes = 32 * 1024;   // LDS exchange buffer (ring + exchange = 160 KiB)
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
@@ -26,10 +27,12 @@ struct AttnParams {
   const int32_t* context_lens;
   f4* ws_ml;     // [partials, R] (m_raw, l, c, 0)
   float* ws_o;   // [partials, R, D]
+  int* ws_seq;   // [B + 1]: first item of each sequence, then the item total
   int B, next_n, Hq, Hkv, G, R, bs, max_blocks;
   int hpu, hgroups, ts, nw, nsub;  // heads per item, head groups, tokens per item, waves, sub-tiles
   int nwg;                         // workgroups of the persistent grid
   int lbs, lts, lhpu;              // log2 of bs, ts, hpu (all powers of two)
+  int wgmerge;                     // sub-tile states merged in the workgroup: one partial per head
   int k_scale_mode, v_scale_mode, causal;
   float softmax_scale;
 };
@@ -41,55 +44,15 @@ __device__ __forceinline__ int seq_stages(const AttnParams& p, int L) {
   return (L + p.ts - 1) >> p.lts;
 }
 
-// Exclusive prefix sum over the nw waves of the workgroup; *total gets the
-// sum. Uses lds_tmp[0 .. nw) and leaves it free (ends with a barrier).
-__device__ int block_excl_scan(int x, int* lds_tmp, int nw, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int incl = x;
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
-    const int y = __shfl_up(incl, m, 64);
-    if (lane >= m) incl += y;
+    const int y = __shfl_up(x, m, 64);
+    if (lane >= m) x += y;
   }
-  if (lane == 63) lds_tmp[wv] = incl;
-  __syncthreads();
-  int before = 0, t = 0;
-  for (int i = 0; i < nw; ++i) {
-    const int v = lds_tmp[i];
-    before += i < wv ? v : 0;
-    t += v;
-  }
-  __syncthreads();
-  *total = t;
-  return before + incl - x;
-}
-
-// Item count of the whole batch; with target >= 0 also the sequence holding
-// item `target` (*b_out) and that sequence's first item index (*start_out).
-// All threads of the workgroup call it; uses lds_tmp[0 .. nw + 2).
-__device__ int locate_items(const AttnParams& p, int nw, int target, int* lds_tmp, int* b_out,
-                            int* start_out) {
-  const int nt = 64 * nw;
-  int carry = 0;
-  if (threadIdx.x == 0) lds_tmp[nw] = 0;
-  for (int base = 0; base < p.B; base += nt) {
-    const int b = base + (int)threadIdx.x;
-    const int items = b < p.B ? p.hgroups * seq_stages(p, p.context_lens[b]) : 0;
-    int chunk_total;
-    const int excl = carry + block_excl_scan(items, lds_tmp, nw, &chunk_total);
-    if (target >= 0 && items > 0 && excl <= target && target < excl + items) {
-      lds_tmp[nw] = b;
-      lds_tmp[nw + 1] = excl;
-    }
-    carry += chunk_total;
-  }
-  __syncthreads();
-  if (target >= 0) {
-    *b_out = lds_tmp[nw];
-    *start_out = lds_tmp[nw + 1];
-  }
-  __syncthreads();
-  return carry;
+  return x;
 }
 
 // Position of one item in the (sequence, head group, stage) order; all fields
@@ -129,12 +92,18 @@ struct Geo {
   static_assert(VB <= 16 || VB % 16 == 0, "V bytes per lane");
 };
 
-// 16 bytes per lane from global memory straight into LDS: lane i of the wave
-// writes lds_base + 16 * i (lds_base is wave-uniform). Kept out of templates:
-// the LDS address-space cast is device-only.
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
-                                   0);
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4,
+// scalar-base form): lane i of the wave writes lds + 16 * i, reading
+// sbase + voff; lds and sbase are wave-uniform. The load is issued through
+// inline asm so that the compiler does not treat the asynchronous LDS write as
+// something every later LDS read has to wait for (it would wait for the whole
+// ring); the ring's own vmcnt + barrier protocol orders writes and reads. The
+// asm sets M0 itself; nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, const uint8_t* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff),
+               "s"(sbase)
+               : "memory");
 }
 
 // Per-thread constants of the ring loads. Load l of wave wv covers stage pieces
@@ -145,8 +114,12 @@ __device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
 template <int KIND, int D>
 struct LoadPlan {
   uint32_t voff[Geo<KIND, D>::NL];
-  int tau0[Geo<KIND, D>::NL];
-  int plane[Geo<KIND, D>::NL];
+  // uniform per wave: tau0 | plane << 8 | pi << 9, pi = page of the item the
+  // load reads (0 when a page holds the whole item)
+  int meta[Geo<KIND, D>::NL];
+  __device__ int tau0(int l) const { return meta[l] & 255; }
+  __device__ int plane(int l) const { return (meta[l] >> 8) & 1; }
+  __device__ int pi(int l) const { return meta[l] >> 9; }
 };
 
 template <int KIND, int D>
@@ -166,52 +139,62 @@ __device__ __forceinline__ void make_load_plan(const AttnParams& p, LoadPlan<KIN
     const int tau = row >> p.lhpu, hl = row & ((1 << p.lhpu) - 1);
     const int j = pos ^ (tau & (G_::CPR - 1));
     lp.voff[l] = (uint32_t)(tau - tau0) * tok_stride + (uint32_t)hl * G_::RB + 16u * j;
-    lp.tau0[l] = tau0;
-    lp.plane[l] = plane;
+    // items start on a page boundary when ts >= bs and inside one page otherwise
+    const int pi = p.ts >= (1 << p.lbs) ? tau0 >> p.lbs : 0;
+    lp.meta[l] = tau0 | (plane << 8) | (pi << 9);
   }
+}
+
+// The page each ring load of an item reads, looked up one loop iteration
+// before the loads are issued (scalar loads; the wait for them falls on the
+// next iteration's issue, not on the compute in between). A page index past
+// the sequence's last page is clamped to it: such a page only feeds masked
+// tokens.
+template <int KIND, int D>
+struct PageSet {
+  int phys[Geo<KIND, D>::NL];
+};
+
+template <int KIND, int D>
+__device__ __forceinline__ void load_pages(const AttnParams& p, const int32_t* __restrict__ table,
+                                           const ItemPos& it, const LoadPlan<KIND, D>& lp,
+                                           PageSet<KIND, D>& pg) {
+  const int blk0 = (it.k << p.lts) >> p.lbs;
+  const int last_blk = (it.L - 1) >> p.lbs;
+  const int32_t* table_row = table + (size_t)it.b * p.max_blocks;
+#pragma unroll
+  for (int l = 0; l < Geo<KIND, D>::NL; ++l) pg.phys[l] = table_row[min(blk0 + lp.pi(l), last_blk)];
 }
 
 // Issue the ring loads of one item into `slot`. Every thread issues exactly NL
 // loads whether the item is live or not. Stage layout: K plane then V plane,
 // each [TS tokens][HPU heads][CPR pieces]; piece j of row (tau, hl) is stored
 // at position j ^ (tau & (CPR - 1)). Each load's address is a scalar page base
-// (one scalar block-table load per load) plus the lane's constant offset. A
-// page past the sequence end is replaced by the last real page, whose bytes
-// only feed masked tokens.
+// plus the lane's constant offset.
 template <int KIND, int D>
-__device__ __forceinline__ void issue_stage(const AttnParams& p,
-                                            const int32_t* __restrict__ table, const ItemPos& it,
-                                            bool live, const LoadPlan<KIND, D>& lp,
-                                            uint8_t* slot) {
+__device__ __forceinline__ void issue_stage(const AttnParams& p, const ItemPos& it,
+                                            const PageSet<KIND, D>& pg, bool live,
+                                            const LoadPlan<KIND, D>& lp, uint8_t* slot) {
   using G_ = Geo<KIND, D>;
   const int wv = uni(threadIdx.x >> 6);
   if (live) {
-    const int t0 = it.k << p.lts;
-    const int toff = t0 & ((1 << p.lbs) - 1);  // 0 unless a page holds several items
-    const int blk0 = t0 >> p.lbs;
-    const int last_blk = (it.L - 1) >> p.lbs;
-    const int32_t* table_row = table + (size_t)it.b * p.max_blocks;
+    const int toff = (it.k << p.lts) & ((1 << p.lbs) - 1);  // 0 unless a page holds several items
     const size_t tok_stride = (size_t)p.Hkv * G_::RB;
     const size_t page_stride = tok_stride << p.lbs;
     const size_t head_off = ((size_t)it.hg * G_::RB) << p.lhpu;
-    int phys[G_::NL];
-#pragma unroll
-    for (int l = 0; l < G_::NL; ++l)
-      phys[l] = table_row[min(blk0 + ((toff + lp.tau0[l]) >> p.lbs), last_blk)];
 #pragma unroll
     for (int l = 0; l < G_::NL; ++l) {
-      const int sl = (toff + lp.tau0[l]) & ((1 << p.lbs) - 1);
-      const uint8_t* sbase = (lp.plane[l] ? p.v_cache : p.k_cache) +
-                             (size_t)phys[l] * page_stride + (size_t)sl * tok_stride + head_off;
-      dma16(sbase + lp.voff[l], slot + (l * p.nw + wv) * 1024);
+      const int sl = (toff + lp.tau0(l)) & ((1 << p.lbs) - 1);
+      const uint8_t* sbase = (lp.plane(l) ? p.v_cache : p.k_cache) + (size_t)pg.phys[l] * page_stride +
+                             (size_t)sl * tok_stride + head_off;
+      dma16(sbase, lp.voff[l], slot + (l * p.nw + wv) * 1024);
     }
   } else {
     // past the end of the range: the same number of loads, of 16 readable
     // bytes, into a slot nobody reads
     const uint8_t* sbase = reinterpret_cast<const uint8_t*>(p.q);
 #pragma unroll
-    for (int l = 0; l < G_::NL; ++l)
-      dma16(sbase, slot + (l * p.nw + wv) * 1024);
+    for (int l = 0; l < G_::NL; ++l) dma16(sbase, 0u, slot + (l * p.nw + wv) * 1024);
   }
 }
 
@@ -420,6 +403,56 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
   }
 }
 
+// Exchange of a wave's softmax state through LDS, in the MFMA register layout
+// (lane-major), so the receiving wave of the same head combines element-wise:
+// o as [rt][q][lane] f4, then m and l as [rt][lane] floats.
+template <int KIND, int D, int RT, bool HILO>
+__device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, HILO>& w, float* xbuf) {
+  constexpr int DV = Geo<KIND, D>::DV;
+  const int lane = threadIdx.x & 63;
+  f4* xo = reinterpret_cast<f4*>(xbuf);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int q = 0; q < DV; ++q) xo[(rt * DV + q) * 64 + lane] = w.o[rt][q];
+    xbuf[RT * DV * 256 + rt * 64 + lane] = w.m_run[rt];
+    xbuf[RT * DV * 256 + (RT + rt) * 64 + lane] = w.l_run[rt];
+  }
+}
+
+// Combine the state in xbuf into w (w first, then xbuf: a fixed order).
+template <int KIND, int D, int RT, bool HILO>
+__device__ __forceinline__ void xch_merge(WaveState<KIND, D, RT, HILO>& w, const float* xbuf,
+                                          float c2) {
+  constexpr int DV = Geo<KIND, D>::DV;
+  const int lane = threadIdx.x & 63;
+  const f4* xo = reinterpret_cast<const f4*>(xbuf);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float mb = xbuf[RT * DV * 256 + rt * 64 + lane];
+    const float lb = xbuf[RT * DV * 256 + (RT + rt) * 64 + lane];
+    const float ma = w.m_run[rt];
+    const float mn = fmaxf(ma, mb);
+    const float a = ma == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ma - mn) * c2);
+    const float bw = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - mn) * c2);
+    w.l_run[rt] = w.l_run[rt] * a + lb * bw;
+    w.m_run[rt] = mn;
+#pragma unroll
+    for (int q = 0; q < DV; ++q) {
+      w.o[rt][q] = w.o[rt][q] * a + xo[(rt * DV + q) * 64 + lane] * bw;
+      __builtin_amdgcn_sched_barrier(0);  // keep one f4 in flight: register pressure
+    }
+  }
+}
+
+// Barrier over the workgroup that leaves the ring loads in flight: LDS writes
+// are waited for, vector memory is not.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Partial index of (run r, workgroup w, head-in-group hl, sub-tile st); run
 // r = b * hgroups + hg. Slot r + w is unique: a later workgroup only reaches
 // later runs, so (r, w) != (r', w') with r + w == r' + w' cannot both occur.
@@ -460,25 +493,65 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens) {
   using G_ = Geo<KIND, D>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageMax];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = uni(threadIdx.x >> 6);  // wave-uniform
   const int hl = wv & (p.hpu - 1), st = wv >> p.lhpu;
   const int stage_bytes = (2 * p.ts * G_::RB) << p.lhpu;
-  int* scratch = reinterpret_cast<int*>(ring);
+  __shared__ __attribute__((aligned(16))) float xbuf[kXchBytes / 4];
+  int* xi = reinterpret_cast<int*>(xbuf);
 
-  // ---- this workgroup's item range ----
-  int b0 = 0, start0 = 0;
-  const int total = locate_items(p, p.nw, -1, scratch, &b0, &start0);
+  // ---- this workgroup's item range: one wave scans the sequence lengths;
+  // workgroup 0 also publishes every sequence's first item for the merge ----
+  if (wv == 0) {
+    int carry = 0;
+    for (int base = 0; base < p.B; base += 64) {
+      const int b = base + lane;
+      const int items = b < p.B ? p.hgroups * seq_stages(p, lens[b]) : 0;
+      const int incl = wave_incl_scan(items);
+      if (blockIdx.x == 0 && b < p.B) p.ws_seq[b] = carry + incl - items;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (blockIdx.x == 0 && lane == 0) p.ws_seq[p.B] = carry;
+    const int per_ = (carry + p.nwg - 1) / p.nwg;
+    const int target = (int)blockIdx.x * per_;
+    int fb = -1, fs = 0;
+    if (target < carry) {
+      int c0 = 0;
+      for (int base = 0; base < p.B; base += 64) {
+        const int b = base + lane;
+        const int items = b < p.B ? p.hgroups * seq_stages(p, lens[b]) : 0;
+        const int incl = wave_incl_scan(items);
+        const int excl = c0 + incl - items;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(items > 0 && excl <= target &&
+                                                          target < excl + items);
+        if (hit) {
+          const int first = __builtin_ctzll(hit);
+          fb = base + first;
+          fs = __shfl(excl, first, 64);
+          break;
+        }
+        c0 += __shfl(incl, 63, 64);
+      }
+    }
+    if (lane == 0) {
+      xi[0] = carry;
+      xi[1] = fb;
+      xi[2] = fs;
+    }
+  }
+  __syncthreads();
+  // workgroup-uniform (read back from LDS, so say so to the compiler)
+  const int total = uni(xi[0]);
+  const int b0 = uni(xi[1]), start0 = uni(xi[2]);
   const int per = (total + p.nwg - 1) / p.nwg;
   const int i0 = (int)blockIdx.x * per;
   const int i1 = min(i0 + per, total);
   if (i0 >= i1) return;
-  locate_items(p, p.nw, i0, scratch, &b0, &start0);
   ItemPos cp;
-  cp.b = uni(b0);
+  cp.b = b0;
   cp.L = lens[cp.b];
   cp.nst = seq_stages(p, cp.L);
-  cp.hg = (i0 - uni(start0)) / cp.nst;
-  cp.k = (i0 - uni(start0)) % cp.nst;
+  cp.hg = (i0 - start0) / cp.nst;
+  cp.k = (i0 - start0) % cp.nst;
   const int nitems = i1 - i0;
 
   // ---- scale constants: fold normalizer for PER_CHANNEL K [FOLD, Approach] ----
@@ -505,26 +578,35 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   WaveState<KIND, D, RT, HILO> w;
   start_run<KIND, D, RT, HILO>(p, cp.b, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
 
-  // ---- ring prologue: kStages - 1 items in flight ----
-  ItemPos ld = cp;
+  // ---- ring prologue: kStages - 1 items in flight; the block-table loads of
+  // all of them (and of the next one) are issued before any is waited for ----
+  ItemPos pos[kStages];
+  pos[0] = cp;
 #pragma unroll
-  for (int j = 0; j < kStages - 1; ++j) {
-    const bool live = j < nitems;
-    issue_stage<KIND, D>(p, table, ld, live, lp, ring + j * stage_bytes);
-    if (live) item_next(p, lens, ld);
+  for (int j = 1; j < kStages; ++j) {
+    pos[j] = pos[j - 1];
+    if (j - 1 < nitems) item_next(p, lens, pos[j]);
   }
+  PageSet<KIND, D> pgs[kStages - 1];
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < nitems) load_pages<KIND, D>(p, table, pos[j], lp, pgs[j]);
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j)
+    issue_stage<KIND, D>(p, pos[j], pgs[j], j < nitems, lp, ring + j * stage_bytes);
+  ItemPos ld = pos[kStages - 1];
+  PageSet<KIND, D> pg;
+  if (kStages - 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
 
   for (int j = 0; j < nitems; ++j) {
     // item j has landed for every wave, and every wave is done with item j - 1
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * G_::NL) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    {
-      const int jn = j + kStages - 1;
-      const bool live = jn < nitems;
-      issue_stage<KIND, D>(p, table, ld, live, lp, ring + (jn % kStages) * stage_bytes);
-      if (live) item_next(p, lens, ld);
-    }
+    const int jn = j + kStages - 1;
+    const bool live_n = jn < nitems;
+    issue_stage<KIND, D>(p, ld, pg, live_n, lp, ring + (jn % kStages) * stage_bytes);
+    if (live_n) item_next(p, lens, ld);
     const int t0 = (cp.k << p.lts) + 16 * st;
     if (t0 < cp.L)
       compute_tile<KIND, D, RT, HILO>(ring + (j % kStages) * stage_bytes, to, t0, cp.L, c2, w);
@@ -532,11 +614,27 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     const int b = cp.b, hg = cp.hg;
     item_next(p, lens, cp);
     if (j + 1 == nitems || cp.b != b || cp.hg != hg) {
-      write_partial<KIND, D, RT, HILO>(p, part_index(p, b * p.hgroups + hg, blockIdx.x, hl, st),
-                                       c2, w);
+      if (p.wgmerge) {
+        // fold sub-tiles 1 .. nsub-1 of each head into sub-tile 0, in order
+        for (int h = 0; h < p.hpu; ++h)
+          for (int s2 = 1; s2 < p.nsub; ++s2) {
+            if (hl == h && st == s2) xch_put<KIND, D, RT, HILO>(w, xbuf);
+            lds_barrier();
+            if (hl == h && st == 0) xch_merge<KIND, D, RT, HILO>(w, xbuf, c2);
+            lds_barrier();
+          }
+        if (st == 0)
+          write_partial<KIND, D, RT, HILO>(p, part_index(p, b * p.hgroups + hg, blockIdx.x, hl, 0),
+                                           c2, w);
+      } else {
+        write_partial<KIND, D, RT, HILO>(p, part_index(p, b * p.hgroups + hg, blockIdx.x, hl, st),
+                                         c2, w);
+      }
       if (j + 1 < nitems)
         start_run<KIND, D, RT, HILO>(p, cp.b, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
     }
+    // pages of the item the next iteration issues
+    if (jn + 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }

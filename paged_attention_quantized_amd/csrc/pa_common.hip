@@ -17,17 +17,15 @@ pa_status fail(pa_status st, const char* fmt, ...) {
 
 void clear_error() { g_err[0] = '\0'; }
 
-// Profiling hook: events recorded right before and right after the dominant
-// kernel of the next calls on this thread.
+// Profiling hook: events the dominant kernel of the next calls on this thread
+// is launched with (stamped by the kernel's own dispatch).
 static thread_local hipEvent_t g_prof_start = nullptr;
 static thread_local hipEvent_t g_prof_stop = nullptr;
 
-void prof_begin(hipStream_t s) {
-  if (g_prof_start) hipEventRecord(g_prof_start, s);
-}
-
-void prof_end(hipStream_t s) {
-  if (g_prof_stop) hipEventRecord(g_prof_stop, s);
+bool prof_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = g_prof_start;
+  *stop = g_prof_stop;
+  return g_prof_start != nullptr;
 }
 
 void set_prof_events(void* start, void* stop) {

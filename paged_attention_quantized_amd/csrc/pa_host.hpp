@@ -2,6 +2,7 @@
 // argument checks shared by the entry points.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -14,8 +15,19 @@ namespace pa {
 pa_status fail(pa_status st, const char* fmt, ...);
 void clear_error();
 pa_status launch_status(const char* what);
-void prof_begin(hipStream_t s);  // record the profiling start event, if set
-void prof_end(hipStream_t s);    // record the profiling stop event, if set
+// Profiling events set by pa_set_profile_events (false if none).
+bool prof_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Launch a kernel; with profiling events set, through hipExtLaunchKernelGGL so
+// that the events carry the kernel's own start and end times.
+template <typename F, typename... Args>
+void launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t e0, e1;
+  if (prof_events(&e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

@@ -206,8 +206,6 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
   p.max_ctx = a->max_context_len;
   p.nchunks = (int)ceil_div(a->max_context_len, kLogitsChunk);
   hipStream_t s = (hipStream_t)stream;
-  prof_begin(s);
-  hipLaunchKernelGGL(fn, dim3((unsigned)((int64_t)a->batch * p.nchunks)), dim3(64), 0, s, p);
-  prof_end(s);
+  launch_timed(fn, dim3((unsigned)((int64_t)a->batch * p.nchunks)), dim3(64), s, p);
   return launch_status("paged_mqa_logits kernel");
 }
