@@ -199,3 +199,65 @@ def test_full_fp8_verify_double_shuffle(pa):
         say(f"fp8_verify relocation {seed}")
         other = run_attn(pa, W.relocate(case, seed))
         assert np.array_equal(other.view(np.uint16), got.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# shapes that exercise the work split: many sequences (the range scan loops
+# over chunks of 64), several KV head groups, a non-power-of-two KV head
+# count, two-wave workgroups, 64 query rows per KV head, one long sequence
+# spread over every workgroup
+# ---------------------------------------------------------------------------
+
+def split_cases():
+    rng = np.random.default_rng(88)
+    return [
+        W.attn_case("many_seqs", 1501, B=150, next_n=1, Hq=8, Hkv=2, D=128, bs=16,
+                    lens=list(rng.integers(0, 300, 150)), kv_kind=W.KV_E4M3,
+                    scale_mode=W.SCALE_PER_TENSOR, max_context_len=320),
+        W.attn_case("kv16_groups", 1502, B=3, next_n=1, Hq=32, Hkv=16, D=128, bs=16,
+                    lens=[100, 517, 33], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR),
+        W.attn_case("kv6", 1503, B=2, next_n=2, Hq=12, Hkv=6, D=128, bs=32,
+                    lens=[200, 65], kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_TENSOR),
+        W.attn_case("f16_d256", 1504, B=2, next_n=1, Hq=4, Hkv=2, D=256, bs=16,
+                    lens=[130, 47], kv_kind=W.KV_F16, scale_mode=W.SCALE_NONE),
+        W.attn_case("rows64", 1505, B=2, next_n=4, Hq=32, Hkv=2, D=128, bs=32,
+                    lens=[300, 90], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR),
+        W.attn_case("one_long", 1506, B=1, next_n=1, Hq=8, Hkv=8, D=128, bs=16,
+                    lens=[60000], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR),
+        W.attn_case("int4_d128_kv1", 1507, B=3, next_n=1, Hq=8, Hkv=1, D=128, bs=16,
+                    lens=[1, 64, 257], kv_kind=W.KV_INT4, scale_mode=W.SCALE_PER_CHANNEL,
+                    q_dist=(-100.0, 100.0), zero_k_channel_frac=0.1),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_split_shapes_parity(pa, idx):
+    case = split_cases()[idx]
+    say(f"split shape {case.name} B={case.batch} Hkv={case.num_kv_heads} lens<= "
+        f"{int(case.context_lens.max())}")
+    got = run_attn(pa, case)
+    ref = oracle_attn(case)
+    r = compare_attn(got, ref, case.name)
+    say(f"{case.name}: max err/tol = {r:.3f}")
+
+
+@pytest.mark.parametrize("idx", [0, 1, 5])
+def test_split_shapes_relocation(pa, idx):
+    case = split_cases()[idx]
+    say(f"split shape relocation {case.name}")
+    base = run_attn(pa, case)
+    got = run_attn(pa, W.relocate(case, 9))
+    assert np.array_equal(got.view(np.uint16), base.view(np.uint16))
+
+
+def test_zero_per_channel_k_scale_is_uniform(pa):
+    """max|k_scale| = 0: the folded q and the score scale are 0, every visible
+    token gets the same weight (the mean of V), and no NaN appears."""
+    case = W.attn_case("kzero", 1601, B=2, next_n=1, Hq=8, Hkv=2, D=128, bs=16, lens=[40, 7],
+                       kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_CHANNEL,
+                       v_scale_range=(0.5, 2.0))
+    case.k_scale = np.zeros_like(case.k_scale)
+    say("zero per-channel k_scale")
+    got = run_attn(pa, case)
+    assert np.isfinite(got.astype(np.float32)).all()
+    compare_attn(got, oracle_attn(case), "kzero")
