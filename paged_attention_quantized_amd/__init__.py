@@ -13,7 +13,7 @@ import os
 __all__ = [
     "load", "paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
     "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "pa_set_profile_events",
-    "PaError",
+    "prepare_paged_attn_fwd", "prepare_paged_mqa_logits", "Prepared", "PaError",
     "KV_F16", "KV_BF16", "KV_E4M3", "KV_INT8", "KV_INT4",
     "SCALE_NONE", "SCALE_PER_TENSOR", "SCALE_PER_CHANNEL",
 ]
@@ -111,6 +111,21 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+class Prepared:
+    """One library call with its argument struct already marshalled: calling it
+    passes the same struct, workspace and stream through the C ABI again. It
+    keeps references to the tensors whose pointers the struct holds."""
+
+    def __init__(self, fn, args, keep, *rest):
+        self._fn, self._args, self._ref, self._keep, self._rest = fn, args, ctypes.byref(args), \
+            keep, rest
+
+    def __call__(self):
+        status = self._fn(self._ref, *self._rest)
+        if status != 0:
+            _check(status)
+
+
 def _stream(stream):
     if stream is not None:
         return stream
@@ -151,6 +166,24 @@ def paged_attn_workspace_size(q, k_cache, block_table, max_context_len, kv_kind,
     return load().paged_attn_workspace_size(ctypes.byref(a))
 
 
+def prepare_paged_attn_fwd(out, q, k_cache, v_cache, block_table, context_lens,
+                           max_context_len, *, kv_kind, k_scale=None, v_scale=None,
+                           k_scale_mode=None, v_scale_mode=None, softmax_scale=0.0, causal=True,
+                           workspace=None, stream=None):
+    """paged_attn_fwd with its argument struct built once: calling the result
+    enqueues the same work again on the same tensors (their storage must stay
+    alive). Arguments as for paged_attn_fwd."""
+    import torch
+    a = _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                   kv_kind, k_scale, v_scale, k_scale_mode, v_scale_mode, softmax_scale, causal)
+    lib = load()
+    need = lib.paged_attn_workspace_size(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    return Prepared(lib.paged_attn_fwd, a, (out, q, k_cache, v_cache, workspace), _ptr(workspace),
+                    workspace.numel(), _stream(stream))
+
+
 def paged_attn_fwd(out, q, k_cache, v_cache, block_table, context_lens, max_context_len, *,
                    kv_kind, k_scale=None, v_scale=None, k_scale_mode=None, v_scale_mode=None,
                    softmax_scale=0.0, causal=True, workspace=None, stream=None):
@@ -160,15 +193,11 @@ def paged_attn_fwd(out, q, k_cache, v_cache, block_table, context_lens, max_cont
     block_table int32 [B, max_blocks]; context_lens int32 [B]; scales fp32 [1] or [Hkv, D].
     The workspace (uint8 tensor) is allocated here when not given.
     """
-    import torch
-    a = _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
-                   kv_kind, k_scale, v_scale, k_scale_mode, v_scale_mode, softmax_scale, causal)
-    lib = load()
-    need = lib.paged_attn_workspace_size(ctypes.byref(a))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check(lib.paged_attn_fwd(ctypes.byref(a), _ptr(workspace), workspace.numel(),
-                              _stream(stream)))
+    prepare_paged_attn_fwd(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                           kv_kind=kv_kind, k_scale=k_scale, v_scale=v_scale,
+                           k_scale_mode=k_scale_mode, v_scale_mode=v_scale_mode,
+                           softmax_scale=softmax_scale, causal=causal, workspace=workspace,
+                           stream=stream)()
     return out
 
 
@@ -216,9 +245,11 @@ def paged_mqa_logits_workspace_size(q, sf_q, kv_fused, weights, context_lens, bl
     return load().paged_mqa_logits_workspace_size(ctypes.byref(a))
 
 
-def paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len, *,
-                     sf_vec_size=32, out=None, workspace=None, stream=None):
-    """Weighted per-head MXFP4 logits [B*next_n, max_context_len] fp32 (include/pa.h)."""
+def prepare_paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table,
+                             max_context_len, *, sf_vec_size=32, out=None, workspace=None,
+                             stream=None):
+    """paged_mqa_logits with its argument struct built once (see
+    prepare_paged_attn_fwd); the result's .out is the output tensor."""
     import torch
     B, next_n = q.shape[:2]
     if out is None:
@@ -229,10 +260,20 @@ def paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_
     need = lib.paged_mqa_logits_workspace_size(ctypes.byref(a))
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(lib.paged_mqa_logits(ctypes.byref(a), _ptr(workspace),
-                                workspace.numel() if workspace is not None else 0,
-                                _stream(stream)))
-    return out
+    call = Prepared(lib.paged_mqa_logits, a, (out, q, kv_fused, workspace), _ptr(workspace),
+                    workspace.numel() if workspace is not None else 0, _stream(stream))
+    call.out = out
+    return call
+
+
+def paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len, *,
+                     sf_vec_size=32, out=None, workspace=None, stream=None):
+    """Weighted per-head MXFP4 logits [B*next_n, max_context_len] fp32 (include/pa.h)."""
+    call = prepare_paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table,
+                                    max_context_len, sf_vec_size=sf_vec_size, out=out,
+                                    workspace=workspace, stream=stream)
+    call()
+    return call.out
 
 
 # ---------------------------------------------------------------------------

@@ -1,9 +1,11 @@
 // pa_logits.hip -- MXFP4 paged MQA logits on gfx950 [FP4API].
 //
-// Work unit = (sequence b, 256-token chunk), one wavefront. For each 64-token
-// KV block of the chunk that holds visible tokens:
-//   1. gather the block through block_table: each lane loads 16 FP4 bytes (32
-//      channels = one scale group) of one token and that group's UE8M0 byte;
+// Work unit = (sequence b, 256-token chunk), one wavefront. For the 64-token KV
+// blocks of the chunk that hold visible tokens:
+//   1. gather the blocks through block_table: each lane loads 16 FP4 bytes (32
+//      channels = one scale group) of one token and that group's UE8M0 byte.
+//      The loads of all blocks of the chunk are issued before the first MFMA,
+//      so a wave waits for one table lookup and one round of loads in all;
 //   2. S[h][t] = q_h . k_t with v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1,
 //      E8M0 scales per 32 channels, fp32 result; head_dim 128 is one MFMA);
 //      M rows are heads, N columns are tokens, and the heads of a row tile are
@@ -19,11 +21,18 @@
 #include "pa_device.hpp"
 #include "pa_host.hpp"
 
+#ifndef LOGITS_NB
+#define LOGITS_NB 1
+#endif
+#ifndef LOGITS_WPE
+#define LOGITS_WPE 3
+#endif
+
 namespace pa {
 
 typedef int i8v __attribute__((ext_vector_type(8)));
 
-constexpr int kLogitsChunk = 256;
+constexpr int kLogitsBlocks = LOGITS_NB;  // 64-token blocks per wave
 
 struct LogitsParams {
   float* out;
@@ -34,7 +43,7 @@ struct LogitsParams {
   const float* w;
   const int32_t* context_lens;
   const int32_t* block_table;
-  int B, max_blocks, max_ctx, nchunks;
+  int B, max_blocks, max_ctx, ngroups;
 };
 
 // 4x4 transpose of (lane group, register): after it, register t of lane group
@@ -52,78 +61,145 @@ __device__ __forceinline__ void transpose4(float& r0, float& r1, float& r2, floa
   r3 = __uint_as_float(d[1]);
 }
 
-template <int NN, int H>
-__global__ __launch_bounds__(64) void logits_kernel(LogitsParams p) {
+// Keeps a loaded value where it is: the empty asm needs the value in a register
+// here, so the compiler can neither sink the load into a later branch nor
+// split the loads of a chunk into several waits.
+template <typename T>
+__device__ __forceinline__ void pin(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
+// A workgroup is 4 waves over 4 consecutive chunks of one sequence; NB =
+// 64-token KV blocks per wave (chunk = 64*NB tokens). The q rows of the
+// sequence are staged once per workgroup in LDS.
+template <int NN, int H, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE))) void logits_kernel(
+    LogitsParams p) {
   constexpr int D = 128, BS = 64;
+  constexpr int CH = NB * BS;  // tokens per chunk
   constexpr int NTI = H / 16;  // row tiles per query row
   constexpr int HG = H / 4;    // heads per lane group after the MFMA
   constexpr int ROWB = D / 2;  // FP4 bytes per token
   constexpr int SFB = D / 32;  // scale bytes per token
   constexpr int BLK = BS * (ROWB + SFB);
-  const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
-  const int c = blockIdx.x % p.nchunks, b = blockIdx.x / p.nchunks;
+  constexpr int QN = NN * H * ROWB / 16;  // 16-byte q pieces of the sequence
+  constexpr int QP = (QN + 255) / 256;    // q pieces per thread
+  static_assert(NN * H <= 256, "one scale word per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[NN * H * ROWB];
+  __shared__ int32_t sflds[NN * H];
+  __shared__ float wlds[NN * H];
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = blockIdx.x % p.ngroups, b = blockIdx.x / p.ngroups;
   const int L = p.context_lens[b];
-  const int t_chunk = c * kLogitsChunk;
+  const int t_grp = grp * 4 * CH;
+  const int t_chunk = t_grp + wave * CH;
+  const bool grp_live = t_grp < L;  // some wave of the workgroup reads KV
+  // blocks of this chunk inside max_context_len, and those holding visible tokens
+  const int nblk = max(0, min(NB, (p.max_ctx - t_chunk + BS - 1) / BS));
+  const int nvis = t_chunk < L ? min(nblk, (L - t_chunk + BS - 1) / BS) : 0;
+  float* orow = p.out + (size_t)b * NN * p.out_stride;
 
-  // ---- q operands: A rows are heads; row j of row tile rt holds head
-  // HG*(j/4) + 4*rt + j%4, lane group g its channels [32g, 32g+32) ----
-  i8v qa[NN][NTI];
-  int qs[NN][NTI];
-  if (t_chunk < L) {
+  // ---- loads that need only b: this chunk's block-table columns (lane k reads
+  // column k, clamped to the last column inside max_context_len), the q rows of
+  // the sequence (each thread QP 16-byte pieces), their scales and weights ----
+  const int32_t* trow = p.block_table + (size_t)b * p.max_blocks + t_chunk / BS;
+  const int pg_lane = nblk > 0 ? trow[min(lane, nblk - 1)] : 0;
+  u4 qv[QP];
+  int sfv = 0;
+  float wv = 0.f;
+  if (grp_live) {
 #pragma unroll
-    for (int i = 0; i < NN; ++i)
-#pragma unroll
-      for (int rt = 0; rt < NTI; ++rt) {
-        const int h = HG * (j >> 2) + 4 * rt + (j & 3);
-        const size_t row = ((size_t)b * NN + i) * H + h;
-        const u4 v = *reinterpret_cast<const u4*>(p.q + row * ROWB + 16 * g);
-        qa[i][rt] = i8v{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-        qs[i][rt] = (p.sf_q[row] >> (8 * g)) & 0xFF;
-      }
+    for (int k = 0; k < QP; ++k)
+      if (tid + 256 * k < QN)
+        qv[k] = reinterpret_cast<const u4*>(p.q + (size_t)b * NN * H * ROWB)[tid + 256 * k];
+    if (tid < NN * H) {
+      sfv = p.sf_q[(size_t)b * NN * H + tid];
+      wv = p.w[(size_t)b * NN * H + tid];
+    }
   }
 
-#pragma unroll 1
-  for (int k = 0; k < kLogitsChunk / BS; ++k) {
-    const int t_blk = t_chunk + k * BS;
-    if (t_blk >= p.max_ctx) break;
-    const int t = t_blk + lane;  // the token this lane stores
-    if (t_blk >= L) {
-      // no visible token in this block: -inf, nothing is read
+  // ---- the FP4 rows and scale bytes of all blocks of the chunk. A block with
+  // no visible token takes the chunk's first block: its loads hit lines already
+  // in flight and are never used; a chunk with none reads nothing ----
+  u4 kraw[NB][4];
+  int ks[NB][4];
+  if (nvis > 0) {
 #pragma unroll
-      for (int i = 0; i < NN; ++i)
-        if (t < p.max_ctx) p.out[((size_t)b * NN + i) * p.out_stride + t] = -INFINITY;
-      continue;
+    for (int k = 0; k < NB; ++k) {
+      const int pg = __builtin_amdgcn_readlane(pg_lane, k < nvis ? k : 0);
+      const uint8_t* blk = p.kv + (size_t)pg * BLK;
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const int tok = 16 * tau + j;
+        kraw[k][tau] = *reinterpret_cast<const u4*>(blk + tok * ROWB + 16 * g);
+        ks[k][tau] = blk[BS * ROWB + tok * SFB + g];
+      }
     }
-    const uint8_t* blk = p.kv + (size_t)p.block_table[(size_t)b * p.max_blocks + t_blk / BS] * BLK;
-    // ---- k operands for the 4 token tiles: column j is token 16*tau + j ----
-    i8v kb[4];
-    int ks[4];
+  }
+
+  // columns of blocks with no visible token: -inf
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int t = t_chunk + k * BS + lane;
+    if (k >= nvis && k < nblk && t < p.max_ctx)
+#pragma unroll
+      for (int i = 0; i < NN; ++i) orow[(size_t)i * p.out_stride + t] = -INFINITY;
+  }
+  if (!grp_live) return;  // uniform over the workgroup
+
+  if (grp_live) {
+#pragma unroll
+    for (int k = 0; k < QP; ++k)
+      if (tid + 256 * k < QN) reinterpret_cast<u4*>(qlds)[tid + 256 * k] = qv[k];
+    if (tid < NN * H) {
+      sflds[tid] = sfv;
+      wlds[tid] = wv;
+    }
+  }
+  __syncthreads();
+  if (nvis == 0) return;
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-      const int tok = 16 * tau + j;
-      const u4 v = *reinterpret_cast<const u4*>(blk + tok * ROWB + 16 * g);
-      kb[tau] = i8v{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-      ks[tau] = blk[BS * ROWB + tok * SFB + g];
+      pin(kraw[k][tau]);
+      pin(ks[k][tau]);
     }
+
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    if (k >= nvis) continue;
+    const int t = t_chunk + k * BS + lane;  // the token this lane stores
 #pragma unroll
     for (int i = 0; i < NN; ++i) {
       float s[NTI][4][4];  // [rt][tau][e]
 #pragma unroll
-      for (int rt = 0; rt < NTI; ++rt)
+      for (int rt = 0; rt < NTI; ++rt) {
+        // A rows are heads: row j of row tile rt holds head HG*(j/4) + 4*rt + j%4,
+        // lane group g its channels [32g, 32g+32)
+        const int h = HG * (j >> 2) + 4 * rt + (j & 3);
+        const u4 v = *reinterpret_cast<const u4*>(qlds + (i * H + h) * ROWB + 16 * g);
+        const i8v qa = i8v{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        const int qs = (sflds[i * H + h] >> (8 * g)) & 0xFF;
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
+          // B columns are tokens: column j of token tile tau is token 16*tau + j
+          const u4 kv4 = kraw[k][tau];
+          const i8v kb = i8v{(int)kv4[0], (int)kv4[1], (int)kv4[2], (int)kv4[3], 0, 0, 0, 0};
           const f4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              qa[i][rt], kb[tau], f4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, qs[i][rt], 0, ks[tau]);
+              qa, kb, f4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, qs, 0, ks[k][tau]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[rt][tau][e] = acc[e];
         }
+      }
       // lane (j, g) holds heads HG*g + 4*rt + e of tokens 16*tau + j; transpose so
       // that lane (j, g) holds heads HG*tau + 4*rt + e of token 16*g + j
 #pragma unroll
       for (int rt = 0; rt < NTI; ++rt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) transpose4(s[rt][0][e], s[rt][1][e], s[rt][2][e], s[rt][3][e]);
-      const float* wrow = p.w + ((size_t)b * NN + i) * H;
+      const float* wrow = wlds + i * H;
       float acc = 0.f;
 #pragma unroll
       for (int tau = 0; tau < 4; ++tau)
@@ -131,28 +207,28 @@ __global__ __launch_bounds__(64) void logits_kernel(LogitsParams p) {
         for (int rt = 0; rt < NTI; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc = fmaf(wrow[HG * tau + 4 * rt + e], s[rt][tau][e], acc);
-      if (t < p.max_ctx)
-        p.out[((size_t)b * NN + i) * p.out_stride + t] = t < L ? acc : -INFINITY;
+      if (t < p.max_ctx) orow[(size_t)i * p.out_stride + t] = t < L ? acc : -INFINITY;
     }
   }
 }
 
 typedef void (*LogitsFn)(LogitsParams);
 
-template <int NN>
+template <int NN, int NB>
 LogitsFn pick_h(int H) {
-  if (H == 16) return logits_kernel<NN, 16>;
-  if (H == 32) return logits_kernel<NN, 32>;
-  if (H == 64) return logits_kernel<NN, 64>;
+  if (H == 16) return logits_kernel<NN, 16, NB>;
+  if (H == 32) return logits_kernel<NN, 32, NB>;
+  if (H == 64) return logits_kernel<NN, 64, NB>;
   return nullptr;
 }
 
-LogitsFn pick_logits(int NN, int H) {
+template <int NB>
+LogitsFn pick_nn(int NN, int H) {
   switch (NN) {
-    case 1: return pick_h<1>(H);
-    case 2: return pick_h<2>(H);
-    case 3: return pick_h<3>(H);
-    case 4: return pick_h<4>(H);
+    case 1: return pick_h<1, NB>(H);
+    case 2: return pick_h<2, NB>(H);
+    case 3: return pick_h<3, NB>(H);
+    case 4: return pick_h<4, NB>(H);
   }
   return nullptr;
 }
@@ -179,7 +255,7 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
     return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: head_dim must be 128, sf_vec_size 32");
   if (a->block_size != 64) return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: block_size must be 64");
   if (a->next_n > 4) return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: next_n must be 1..4");
-  LogitsFn fn = pick_logits(a->next_n, a->num_heads);
+  LogitsFn fn = pick_nn<kLogitsBlocks>(a->next_n, a->num_heads);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: num_heads must be 16, 32 or 64");
   if (a->out_row_stride < a->max_context_len)
     return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: out_row_stride < max_context_len");
@@ -204,8 +280,8 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
   p.B = a->batch;
   p.max_blocks = a->max_blocks_per_seq;
   p.max_ctx = a->max_context_len;
-  p.nchunks = (int)ceil_div(a->max_context_len, kLogitsChunk);
+  p.ngroups = (int)ceil_div(a->max_context_len, 4 * 64 * kLogitsBlocks);
   hipStream_t s = (hipStream_t)stream;
-  launch_timed(fn, dim3((unsigned)((int64_t)a->batch * p.nchunks)), dim3(64), s, p);
+  launch_timed(fn, dim3((unsigned)((int64_t)a->batch * p.ngroups)), dim3(256), s, p);
   return launch_status("paged_mqa_logits kernel");
 }

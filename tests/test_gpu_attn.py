@@ -261,3 +261,81 @@ def test_zero_per_channel_k_scale_is_uniform(pa):
     got = run_attn(pa, case)
     assert np.isfinite(got.astype(np.float32)).all()
     compare_attn(got, oracle_attn(case), "kzero")
+
+
+# ---------------------------------------------------------------------------
+# workspace and launch contracts: the workspace needs no clearing (every
+# partial the merge reads is written earlier in the same call), repeated calls
+# and HIP graph replays on one workspace give bitwise the same output, and a
+# batch of many short sequences (runs inside one workgroup's range) is exact
+# ---------------------------------------------------------------------------
+
+def many_short():
+    rng = np.random.default_rng(1701)
+    return W.attn_case("many_short", 1701, B=600, next_n=1, Hq=32, Hkv=8, D=128, bs=16,
+                       lens=list(rng.integers(0, 300, 600)), kv_kind=W.KV_E4M3,
+                       scale_mode=W.SCALE_PER_TENSOR, max_context_len=304)
+
+
+def test_many_short_sequences_whole_runs(pa):
+    case = many_short()
+    say(f"many_short B={case.batch}")
+    got = run_attn(pa, case)
+    ref = oracle_attn(case)
+    r = compare_attn(got, ref, case.name)
+    say(f"many_short: max err/tol = {r:.3f}")
+
+
+@pytest.mark.parametrize("fill", ["random", "ones"])
+def test_dirty_workspace_and_reuse(pa, fill):
+    """A workspace holding arbitrary bytes gives the oracle's result, and
+    reusing it across calls gives bitwise the same output each time."""
+    for case in (small_cases()[1], split_cases()[5]):
+        d = DevAttn(case)
+        n = pa.paged_attn_workspace_size(d.q, d.k, d.bt, case.max_context_len, case.kv_kind,
+                                         case.k_scale_mode, case.v_scale_mode)
+        if fill == "random":
+            ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+        else:
+            ws = torch.full((n,), 255, dtype=torch.uint8, device="cuda")
+        say(f"dirty workspace ({fill}) {case.name}")
+        first = d.run(pa, workspace=ws).cpu().numpy()
+        compare_attn(first, oracle_attn(case), case.name)
+        for _ in range(3):
+            again = d.run(pa, workspace=ws).cpu().numpy()
+            assert np.array_equal(again.view(np.uint16), first.view(np.uint16))
+
+
+def test_graph_replay_matches_eager(pa):
+    """paged_attn_fwd captured once in a HIP graph and replayed several times,
+    with eager calls on the same workspace in between: every replay equals the
+    eager output bitwise."""
+    case = split_cases()[5]
+    d = DevAttn(case)
+    n = pa.paged_attn_workspace_size(d.q, d.k, d.bt, case.max_context_len, case.kv_kind,
+                                     case.k_scale_mode, case.v_scale_mode)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    say("graph replay: eager reference")
+    eager = d.run(pa, workspace=ws).cpu().numpy()
+    out = torch.full(case.q.shape, float("nan"), dtype=torch.float16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    say("graph replay: capture")
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pa.paged_attn_fwd(out, d.q, d.k, d.v, d.bt, d.cl, case.max_context_len,
+                              kv_kind=case.kv_kind, k_scale=d.ks, v_scale=d.vs,
+                              k_scale_mode=case.k_scale_mode, v_scale_mode=case.v_scale_mode,
+                              softmax_scale=case.softmax_scale, causal=case.causal,
+                              workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for k in range(4):
+        out.fill_(float("nan"))
+        say(f"graph replay {k}")
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint16), eager.view(np.uint16)), f"replay {k}"
+        mid = d.run(pa, workspace=ws).cpu().numpy()  # eager call between replays
+        assert np.array_equal(mid.view(np.uint16), eager.view(np.uint16))
