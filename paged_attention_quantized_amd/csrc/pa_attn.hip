@@ -3,9 +3,12 @@
 // Work decomposition. The KV reduction is cut into "items": TS consecutive
 // logical tokens of one sequence for one group of HPU KV heads. Items are
 // ordered by (sequence, head group, logical position) and the persistent grid
-// (one workgroup per compute unit) gives workgroup w the contiguous item range
-// [w*Q, (w+1)*Q), Q = ceil(items / workgroups). Every workgroup therefore gets
-// the same number of KV bytes whatever the mix of context lengths, and all
+// (one workgroup per compute unit) gives each workgroup a contiguous item
+// range of equal cost: every item costs one slot and every (sequence, head
+// group) run start kRunCost more (the q reload and partial store there drain
+// the load pipeline), and workgroup w takes the items in slots
+// [w*Q, (w+1)*Q), Q = ceil(slots / workgroups). Every workgroup therefore gets
+// about the same streaming time whatever the mix of context lengths, and all
 // cut points depend on logical positions only, never on physical block ids
 // [RELOC, Summary].
 //
@@ -55,19 +58,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
   const int hg = hk >> p.lhpu, hl = hk & (p.hpu - 1);
   const int idx = blockIdx.y * 256 + threadIdx.x;
   if (4 * idx >= p.R * D) return;
-  const int total = p.ws_seq[p.B];
-  const int start_b = p.ws_seq[b];
-  const int per = (total + p.nwg - 1) / p.nwg;
+  // the ring kernel's split: item k of run (b, hg) sits at cost slot
+  // first_slot(b) + hg * (nst + kRunCost) + kRunCost + k, and workgroup w owns
+  // slots [w * qc, (w + 1) * qc)
+  const int qc = max(1, (p.ws_seq[p.B] + p.nwg - 1) / p.nwg);
   const int L = p.context_lens[b];
   const int nst = seq_stages(p, L);
-  const int run_start = start_b + hg * nst;
+  const int slot0 = p.ws_seq[b] + hg * (nst + kRunCost) + kRunCost;
   const int r = 4 * idx / D, d = 4 * idx % D;
   const int i = r / p.G, h = hk * p.G + r % p.G;
   const int nsub = p.wgmerge ? 1 : p.nsub;
   float m = -INFINITY, l = 0.f;
   f4 o = {0.f, 0.f, 0.f, 0.f};
   if (nst > 0) {
-    const int w_first = run_start / per, w_last = (run_start + nst - 1) / per;
+    const int w_first = slot0 / qc, w_last = (slot0 + nst - 1) / qc;
     const int run = b * p.hgroups + hg;
     const int nparts = (w_last - w_first + 1) * nsub;
     constexpr int U = 8;

@@ -13,6 +13,7 @@ constexpr int kStages = 4;             // LDS ring depth
 constexpr int kStageMax = 32 * 1024;   // bytes per stage (K and V planes)
 constexpr int kMaxWaves = 8;           // wavefronts per workgroup
 constexpr int kXchBytes = 32 * 1024;   // LDS exchange buffer (ring + exchange = 160 KiB)
+constexpr int kRunCost = 2;            // work split: items a run start costs (q reload, partial)
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
@@ -27,7 +28,7 @@ struct AttnParams {
   const int32_t* context_lens;
   f4* ws_ml;     // [partials, R] (m_raw, l, c, 0)
   float* ws_o;   // [partials, R, D]
-  int* ws_seq;   // [B + 1]: first item of each sequence, then the item total
+  int* ws_seq;   // [B + 1]: first cost slot of each sequence, then the slot total
   int B, next_n, Hq, Hkv, G, R, bs, max_blocks;
   int hpu, hgroups, ts, nw, nsub;  // heads per item, head groups, tokens per item, waves, sub-tiles
   int nwg;                         // workgroups of the persistent grid
@@ -44,16 +45,22 @@ __device__ __forceinline__ int seq_stages(const AttnParams& p, int L) {
   return (L + p.ts - 1) >> p.lts;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
+// round trips): shifts by 1, 2, 4, 8 inside each row of 16 lanes (lanes whose
+// source falls outside the row read 0), then lane 15 of rows 0 and 2 is added
+// to rows 1 and 3, and lane 31 to rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const int y = __shfl_up(x, m, 64);
-    if (lane >= m) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
+
+// Value of lane `l` (wave-uniform) in every lane.
+__device__ __forceinline__ int lane_val(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 
 // Position of one item in the (sequence, head group, stage) order; all fields
 // are workgroup-uniform.
@@ -152,7 +159,7 @@ __device__ __forceinline__ void make_load_plan(const AttnParams& p, LoadPlan<KIN
 // tokens.
 template <int KIND, int D>
 struct PageSet {
-  int phys[Geo<KIND, D>::NL];
+  uint32_t phys[Geo<KIND, D>::NL];  // block ids are >= 0: zero-extended, no use right after the load
 };
 
 template <int KIND, int D>
@@ -163,7 +170,8 @@ __device__ __forceinline__ void load_pages(const AttnParams& p, const int32_t* _
   const int last_blk = (it.L - 1) >> p.lbs;
   const int32_t* table_row = table + (size_t)it.b * p.max_blocks;
 #pragma unroll
-  for (int l = 0; l < Geo<KIND, D>::NL; ++l) pg.phys[l] = table_row[min(blk0 + lp.pi(l), last_blk)];
+  for (int l = 0; l < Geo<KIND, D>::NL; ++l)
+    pg.phys[l] = (uint32_t)table_row[min(blk0 + lp.pi(l), last_blk)];
 }
 
 // Issue the ring loads of one item into `slot`. Every thread issues exactly NL
@@ -498,61 +506,85 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   const int stage_bytes = (2 * p.ts * G_::RB) << p.lhpu;
   __shared__ __attribute__((aligned(16))) float xbuf[kXchBytes / 4];
   int* xi = reinterpret_cast<int*>(xbuf);
+  // the per-tensor K scale is read first, so its latency overlaps the scan
+  const float ks_tensor =
+      (!HILO && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
 
-  // ---- this workgroup's item range: one wave scans the sequence lengths;
-  // workgroup 0 also publishes every sequence's first item for the merge ----
+  // ---- this workgroup's item range. Items are placed on a cost line where
+  // each (sequence, head group) run first takes kRunCost empty slots (the
+  // pipeline drain at a run start) and then one slot per item; workgroup w
+  // takes the items whose slots fall in [w*Qc, (w+1)*Qc). One wave scans the
+  // sequence lengths; workgroup 0 also publishes every sequence's first slot
+  // and the total for the merge kernel ----
   if (wv == 0) {
-    int carry = 0;
+    int ccarry = 0;
+    const int len_first = lane < p.B ? lens[lane] : 0;  // kept for the second pass
     for (int base = 0; base < p.B; base += 64) {
       const int b = base + lane;
-      const int items = b < p.B ? p.hgroups * seq_stages(p, lens[b]) : 0;
-      const int incl = wave_incl_scan(items);
-      if (blockIdx.x == 0 && b < p.B) p.ws_seq[b] = carry + incl - items;
-      carry += __shfl(incl, 63, 64);
+      const int nst = base == 0 ? seq_stages(p, len_first) : (b < p.B ? seq_stages(p, lens[b]) : 0);
+      const int cost = nst > 0 ? p.hgroups * (nst + kRunCost) : 0;
+      const int incl = wave_incl_scan(cost);
+      if (blockIdx.x == 0 && b < p.B) p.ws_seq[b] = ccarry + incl - cost;
+      ccarry += lane_val(incl, 63);
     }
-    if (blockIdx.x == 0 && lane == 0) p.ws_seq[p.B] = carry;
-    const int per_ = (carry + p.nwg - 1) / p.nwg;
-    const int target = (int)blockIdx.x * per_;
-    int fb = -1, fs = 0;
-    if (target < carry) {
-      int c0 = 0;
-      for (int base = 0; base < p.B; base += 64) {
-        const int b = base + lane;
-        const int items = b < p.B ? p.hgroups * seq_stages(p, lens[b]) : 0;
-        const int incl = wave_incl_scan(items);
-        const int excl = c0 + incl - items;
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(items > 0 && excl <= target &&
-                                                          target < excl + items);
-        if (hit) {
-          const int first = __builtin_ctzll(hit);
-          fb = base + first;
-          fs = __shfl(excl, first, 64);
-          break;
-        }
-        c0 += __shfl(incl, 63, 64);
+    if (blockIdx.x == 0 && lane == 0) p.ws_seq[p.B] = ccarry;
+    const int qc = max(1, (ccarry + p.nwg - 1) / p.nwg);
+    const int ta = (int)blockIdx.x * qc, tz = ta + qc;  // this workgroup's slots
+    // first item at or after slot ta (and tz): sequence, head group, stage, index
+    int fb = -1, fL = 0, fhg = 0, fk = 0, ia = -1, iz = -1;
+    int c0 = 0, n0 = 0;
+    for (int base = 0; base < p.B; base += 64) {
+      const int b = base + lane;
+      const int len = base == 0 ? len_first : (b < p.B ? lens[b] : 0);
+      const int nst = seq_stages(p, len);
+      const int items = p.hgroups * nst;
+      const int cost = nst > 0 ? p.hgroups * (nst + kRunCost) : 0;
+      const int ic = wave_incl_scan(cost), ii = wave_incl_scan(items);
+      const int ec = c0 + ic - cost, ei = n0 + ii - items;
+      // the first non-empty sequence whose slots end past t holds slot t
+      const uint64_t hit_a = ia >= 0 ? 0 : __builtin_amdgcn_ballot_w64(cost > 0 && ec + cost > ta);
+      const uint64_t hit_z = __builtin_amdgcn_ballot_w64(cost > 0 && ec + cost > tz);
+      if (hit_a) {
+        const int f = __builtin_ctzll(hit_a);
+        const int n = lane_val(nst, f), rel = ta - lane_val(ec, f);
+        const int hg = rel / (n + kRunCost), k = max(rel % (n + kRunCost) - kRunCost, 0);
+        fb = base + f;
+        fL = lane_val(len, f);
+        fhg = hg;
+        fk = k;
+        ia = lane_val(ei, f) + hg * n + k;
       }
+      if (hit_z) {
+        const int f = __builtin_ctzll(hit_z);
+        const int n = lane_val(nst, f), rel = tz - lane_val(ec, f);
+        const int hg = rel / (n + kRunCost), k = max(rel % (n + kRunCost) - kRunCost, 0);
+        iz = lane_val(ei, f) + hg * n + k;
+        break;
+      }
+      c0 += lane_val(ic, 63);
+      n0 += lane_val(ii, 63);
     }
+    // slots past the last sequence: the range ends at the item total
+    if (ia < 0) ia = n0;
+    if (iz < 0) iz = n0;
     if (lane == 0) {
-      xi[0] = carry;
+      xi[0] = iz - ia;
       xi[1] = fb;
-      xi[2] = fs;
+      xi[2] = fhg;
+      xi[3] = fk;
+      xi[4] = fL;
     }
   }
   __syncthreads();
   // workgroup-uniform (read back from LDS, so say so to the compiler)
-  const int total = uni(xi[0]);
-  const int b0 = uni(xi[1]), start0 = uni(xi[2]);
-  const int per = (total + p.nwg - 1) / p.nwg;
-  const int i0 = (int)blockIdx.x * per;
-  const int i1 = min(i0 + per, total);
-  if (i0 >= i1) return;
+  const int nitems = uni(xi[0]);
+  if (nitems <= 0) return;
   ItemPos cp;
-  cp.b = b0;
-  cp.L = lens[cp.b];
+  cp.b = uni(xi[1]);
+  cp.L = uni(xi[4]);
   cp.nst = seq_stages(p, cp.L);
-  cp.hg = (i0 - start0) / cp.nst;
-  cp.k = (i0 - start0) % cp.nst;
-  const int nitems = i1 - i0;
+  cp.hg = uni(xi[2]);
+  cp.k = uni(xi[3]);
 
   // ---- scale constants: fold normalizer for PER_CHANNEL K [FOLD, Approach] ----
   float qk, inv_m = 0.f;
@@ -563,7 +595,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     inv_m = mx > 0.f ? 1.0f / mx : 0.f;
     qk = p.softmax_scale * mx;
   } else {
-    qk = p.softmax_scale * (p.k_scale_mode == PA_SCALE_PER_TENSOR ? p.k_scale[0] : 1.0f);
+    qk = p.softmax_scale * ks_tensor;
   }
   const float sgn = qk < 0.f ? -1.f : 1.f;
   const float c2 = fabsf(qk) * kLog2e;
@@ -587,10 +619,21 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     pos[j] = pos[j - 1];
     if (j - 1 < nitems) item_next(p, lens, pos[j]);
   }
+  // Unconditional lookups (an item past the range looks up the range's first
+  // item instead, which is always valid) let every table load of the
+  // prologue be issued before the first wait.
   PageSet<KIND, D> pgs[kStages - 1];
 #pragma unroll
-  for (int j = 0; j < kStages - 1; ++j)
-    if (j < nitems) load_pages<KIND, D>(p, table, pos[j], lp, pgs[j]);
+  for (int j = 0; j < kStages - 1; ++j) {
+    const bool in = j < nitems;
+    ItemPos q;
+    q.b = in ? pos[j].b : pos[0].b;
+    q.L = in ? pos[j].L : pos[0].L;
+    q.nst = in ? pos[j].nst : pos[0].nst;
+    q.hg = in ? pos[j].hg : pos[0].hg;
+    q.k = in ? pos[j].k : pos[0].k;
+    load_pages<KIND, D>(p, table, q, lp, pgs[j]);
+  }
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j)
     issue_stage<KIND, D>(p, pos[j], pgs[j], j < nitems, lp, ring + j * stage_bytes);
