@@ -212,7 +212,8 @@ struct WaveState {
   h8 qa[RT][Geo<KIND, D>::KS];
   h8 qb[RT][HILO ? Geo<KIND, D>::KS : 1];
   f4 o[RT][Geo<KIND, D>::DV];
-  float m_run[RT], l_run[RT];
+  float m_run[RT];
+  f4 l_acc[RT];  // row sums of P, accumulated by the matrix cores (all 4 lanes of a row equal)
   int lim[RT];  // query row 16*rt+n sees tokens t <= lim
 };
 
@@ -249,7 +250,7 @@ __device__ __forceinline__ void start_run(const AttnParams& p, int b, int hk, in
       }
     }
     w.m_run[rt] = -INFINITY;
-    w.l_run[rt] = 0.f;
+    w.l_acc[rt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < G_::DV; ++q) w.o[rt][q] = f4{0.f, 0.f, 0.f, 0.f};
     w.lim[rt] = p.causal ? (L - p.next_n + i) : 0x7fffffff;
@@ -298,14 +299,74 @@ __device__ __forceinline__ float rows_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// One 16-token sub-tile (tokens t0 .. t0 + 15) of the wave's head from a ring slot.
+// Codes of the same dword of two tokens, regrouped so that each fp16 pair the
+// kind's decode produces is (token a, token b) of one channel, in natural
+// channel order: the first dword gives channels [0, P) of the dword's run, the
+// second [P, 2P) (P = pairs per dword). 8-bit codes interleave bytes; 4-bit and
+// 16-bit codes put the low halves, then the high halves, of the two tokens
+// side by side (an INT4 decode pairs nibbles k and k + 4).
+template <int KIND>
+__device__ __forceinline__ void pair_tokens(uint32_t xa, uint32_t xb, uint32_t& y0, uint32_t& y1) {
+  if constexpr (Kv<KIND>::kBits == 8) {
+    y0 = __builtin_amdgcn_perm(xb, xa, 0x05010400u);
+    y1 = __builtin_amdgcn_perm(xb, xa, 0x07030602u);
+  } else {
+    y0 = __builtin_amdgcn_perm(xb, xa, 0x05040100u);
+    y1 = __builtin_amdgcn_perm(xb, xa, 0x07060302u);
+  }
+}
+
+// Softmax step of one row tile: new running max, rescale factor, P as the B
+// operand of the PV product. MASK = false when every query row sees all 16
+// tokens (none past the end or past a row's causal limit): no selects then.
+template <bool MASK>
+__device__ __forceinline__ void tile_softmax(const f4 s, int t0, int L, int lim, float c2,
+                                             float& m_run, float& alpha, bool& rescale, h4& pb) {
+  const int g = (threadIdx.x & 63) >> 4;
+  bool okv[4];
+  float mx;
+  if constexpr (MASK) {
+    mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = t0 + 4 * g + e;
+      okv[e] = t < L && t <= lim;
+      mx = okv[e] ? fmaxf(mx, s[e]) : mx;
+    }
+  } else {
+    mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  }
+  mx = rows_max(mx);
+  const float m_old = m_run;
+  const float m_new = fmaxf(m_old, mx);
+  // the state needs rescaling only when a row that has seen tokens gets a
+  // larger max; a row that has seen nothing holds zeros
+  alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - m_new) * c2);
+  rescale |= m_old != m_new && m_old != -INFINITY;
+  float pf[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pf[e] = __builtin_amdgcn_exp2f((s[e] - m_new) * c2);
+    if constexpr (MASK) pf[e] = okv[e] ? pf[e] : 0.f;
+  }
+  const h2 p01 = {(_Float16)pf[0], (_Float16)pf[1]};
+  const h2 p23 = {(_Float16)pf[2], (_Float16)pf[3]};
+  pb = h4{p01[0], p01[1], p23[0], p23[1]};
+  m_run = m_new;
+}
+
+// One 16-token sub-tile (tokens t0 .. t0 + 15) of the wave's head from a ring
+// slot. full: every query row sees all 16 tokens (wave-uniform), so the
+// softmax and the V codes need no masking.
 template <int KIND, int D, int RT, bool HILO>
 __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs<KIND, D>& to,
-                                             int t0, int L, float c2,
+                                             int t0, int L, bool full, float c2,
                                              WaveState<KIND, D, RT, HILO>& w) {
   using G_ = Geo<KIND, D>;
   constexpr int KS = G_::KS, NJ = G_::NJ, KPC = G_::KPC, EPC = G_::EPC, DV = G_::DV;
   constexpr int VDW = G_::VDW, VB = G_::VB;
+  constexpr int P = Kv<KIND>::kPairsPerDword;
+  static_assert(VDW * 2 * P == DV, "V channels per lane");
   const int lane = threadIdx.x & 63, g = lane >> 4;
 
   // ---- K operand: lane (n, g) holds token n, pieces g + 4j ----
@@ -339,11 +400,16 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
     } else {
       vraw[e][0] = *reinterpret_cast<const uint32_t*>(slot + to.v[e][0]);
     }
+  }
+  if (!full) {
     // tokens past the end: zero their V codes by select, so no 0 * NaN can
     // reach O [NULLPAD, Fix]
-    const bool ok = t0 + 4 * g + e < L;
 #pragma unroll
-    for (int k = 0; k < VDW; ++k) vraw[e][k] = ok ? vraw[e][k] : 0u;
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = t0 + 4 * g + e < L;
+#pragma unroll
+      for (int k = 0; k < VDW; ++k) vraw[e][k] = ok ? vraw[e][k] : 0u;
+    }
   }
 
   f4 sacc[RT];
@@ -363,52 +429,50 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
   h4 pb[RT];
   bool rescale = false;
   float alpha[RT];
+  if (full) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    bool okv[4];
-    float mx = -INFINITY;
+    for (int rt = 0; rt < RT; ++rt)
+      tile_softmax<false>(sacc[rt], t0, L, w.lim[rt], c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = t0 + 4 * g + e;
-      okv[e] = t < L && t <= w.lim[rt];
-      mx = okv[e] ? fmaxf(mx, sacc[rt][e]) : mx;
-    }
-    mx = rows_max(mx);
-    const float m_old = w.m_run[rt];
-    const float m_new = fmaxf(m_old, mx);
-    // the state needs rescaling only when a row that has seen tokens gets a
-    // larger max; a row that has seen nothing holds zeros
-    alpha[rt] = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - m_new) * c2);
-    rescale |= m_old != m_new && m_old != -INFINITY;
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const _Float16 ph =
-          okv[e] ? (_Float16)__builtin_amdgcn_exp2f((sacc[rt][e] - m_new) * c2) : (_Float16)0.f;
-      pb[rt][e] = ph;
-      psum += (float)ph;
-    }
-    w.l_run[rt] = alpha[rt] * w.l_run[rt] + psum;
-    w.m_run[rt] = m_new;
+    for (int rt = 0; rt < RT; ++rt)
+      tile_softmax<true>(sacc[rt], t0, L, w.lim[rt], c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
   }
   if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
       for (int q = 0; q < DV; ++q) w.o[rt][q] *= alpha[rt];
+      w.l_acc[rt] *= alpha[rt];
+    }
   }
 
-  // ---- O^T += V^T P^T ----
-  _Float16 vh[4][DV];
+  // ---- O^T += V^T P^T: the A operand of channel q is (tokens 4g .. 4g+3) of
+  // that channel, built straight from decodes of token-paired codes ----
 #pragma unroll
-  for (int e = 0; e < 4; ++e) decode_run<KIND, VDW>(vraw[e], vh[e]);
+  for (int k = 0; k < VDW; ++k) {
+    // dword k of the lane's run: channels [2Pk, 2Pk + 2P), decoded and used at once
+    uint32_t y[4];
+    pair_tokens<KIND>(vraw[0][k], vraw[1][k], y[0], y[1]);
+    pair_tokens<KIND>(vraw[2][k], vraw[3][k], y[2], y[3]);
+    h2 pr[4][P];
 #pragma unroll
-  for (int q = 0; q < DV; ++q) {
-    const h4 vop = {vh[0][q], vh[1][q], vh[2][q], vh[3][q]};
+    for (int i = 0; i < 4; ++i) Kv<KIND>::decode(y[i], pr[i]);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pb[rt], w.o[rt][q], 0, 0, 0);
+    for (int i = 0; i < 2 * P; ++i) {
+      const h2 a = pr[i < P ? 0 : 1][i % P], b = pr[i < P ? 2 : 3][i % P];
+      const h4 vop = {a[0], a[1], b[0], b[1]};
+      const int q = 2 * P * k + i;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pb[rt], w.o[rt][q], 0, 0, 0);
+    }
   }
+  // row sums of P on the matrix cores: every lane gets its row's sum
+  const h4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+    w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb[rt], w.l_acc[rt], 0, 0, 0);
 }
 
 // Exchange of a wave's softmax state through LDS, in the MFMA register layout
@@ -424,7 +488,7 @@ __device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, HILO>& w, f
 #pragma unroll
     for (int q = 0; q < DV; ++q) xo[(rt * DV + q) * 64 + lane] = w.o[rt][q];
     xbuf[RT * DV * 256 + rt * 64 + lane] = w.m_run[rt];
-    xbuf[RT * DV * 256 + (RT + rt) * 64 + lane] = w.l_run[rt];
+    xbuf[RT * DV * 256 + (RT + rt) * 64 + lane] = w.l_acc[rt][0];
   }
 }
 
@@ -443,7 +507,8 @@ __device__ __forceinline__ void xch_merge(WaveState<KIND, D, RT, HILO>& w, const
     const float mn = fmaxf(ma, mb);
     const float a = ma == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ma - mn) * c2);
     const float bw = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - mn) * c2);
-    w.l_run[rt] = w.l_run[rt] * a + lb * bw;
+    const float l = w.l_acc[rt][0] * a + lb * bw;
+    w.l_acc[rt] = f4{l, l, l, l};
     w.m_run[rt] = mn;
 #pragma unroll
     for (int q = 0; q < DV; ++q) {
@@ -475,9 +540,7 @@ __device__ __forceinline__ void write_partial(const AttnParams& p, size_t u, flo
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    float l = w.l_run[rt];
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
+    const float l = w.l_acc[rt][0];
     const int r = 16 * rt + n;
     if (r < p.R) {
       if (g == 0) p.ws_ml[u * p.R + r] = f4{w.m_run[rt], l, c2, 0.f};
@@ -486,7 +549,7 @@ __device__ __forceinline__ void write_partial(const AttnParams& p, size_t u, flo
       for (int e = 0; e < 4; ++e) {
         float tmp[DV];
 #pragma unroll
-        for (int q = 0; q < DV; ++q) tmp[run_elem<KIND>(q)] = w.o[rt][q][e];
+        for (int q = 0; q < DV; ++q) tmp[q] = w.o[rt][q][e];
 #pragma unroll
         for (int k = 0; k < DV; k += 4)
           *reinterpret_cast<f4*>(orow + DV * (4 * g + e) + k) =
@@ -652,7 +715,8 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     if (live_n) item_next(p, lens, ld);
     const int t0 = (cp.k << p.lts) + 16 * st;
     if (t0 < cp.L)
-      compute_tile<KIND, D, RT, HILO>(ring + (j % kStages) * stage_bytes, to, t0, cp.L, c2, w);
+      compute_tile<KIND, D, RT, HILO>(ring + (j % kStages) * stage_bytes, to, t0, cp.L,
+                                      t0 + 16 <= cp.L - (p.causal ? p.next_n - 1 : 0), c2, w);
     // end of a (sequence, head group) run inside this range: write the partial
     const int b = cp.b, hg = cp.hg;
     item_next(p, lens, cp);
