@@ -81,7 +81,9 @@ def _bind(lib):
                                    i32, i32, i32, i32, i32, i32, i64, i32, f32, i32]
     lib.orc_paged_attn.restype = i32
     lib.orc_mqa_logits.argtypes = [P, i64, P, P, P, P, P, P,
-                                   i32, i32, i32, i32, i32, i32, i32, i32]
+                                   i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.orc_f32_to_bf16_array.argtypes = [P, P, i64]
+    lib.orc_f32_to_bf16_array.restype = None
     lib.orc_mqa_logits.restype = i32
     lib.orc_kv_insert.argtypes = [P, P, i32, P, P, i32, P, i64, i64,
                                   i32, i32, i32, i64, P, i32, P, i32]
@@ -169,12 +171,17 @@ def paged_attn(q, k_cache, v_cache, kv_kind, block_table, context_lens, *,
 
 
 def mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len, *,
-               sf_vec_size=32, out_rows=None, out_row_stride=None, lib=None):
+               sf_vec_size=32, out_rows=None, out_row_stride=None, sf_interleaved=False,
+               relu=False, out_format="f32", lib=None):
     """Reference MXFP4 paged MQA logits (see orc_mqa_logits in oracle.c).
 
     q: uint8 [B, next_n, H, D/2]; sf_q: int32 [B, next_n, H]; kv_fused: uint8
-    [num_blocks, bs, 1, D/2 + D/sf_vec]; weights: fp32 [B*next_n, H].
-    Returns fp32 [B*next_n, max_context_len] (or [out_rows, out_row_stride]).
+    [num_blocks, bs, 1, D/2 + D/sf_vec] with the scale tail in token order or,
+    with sf_interleaved, in the interleaved slot order; weights: fp32
+    [B*next_n, H]. relu puts max(., +0) between each head's dot product and its
+    weight. Returns [B*next_n, max_context_len] (or [out_rows, out_row_stride])
+    as fp32, or as fp16 / bf16 (uint16 bits) rounded to nearest even from the
+    fp32 values for out_format "f16" / "bf16".
     """
     lib = lib or load()
     q = np.ascontiguousarray(q, np.uint8)
@@ -191,10 +198,18 @@ def mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_contex
     out = np.full((rows, stride), np.nan, np.float32)
     rc = lib.orc_mqa_logits(_ptr(out), stride, _ptr(q), _ptr(sfq), _ptr(kv), _ptr(w), _ptr(cl),
                             _ptr(bt), B, next_n, H, D, bs, bt.shape[1], max_context_len,
-                            sf_vec_size)
+                            sf_vec_size, int(bool(sf_interleaved)), int(bool(relu)))
     if rc != 0:
         raise ValueError(f"orc_mqa_logits failed with code {rc}")
-    return out
+    if out_format == "f32":
+        return out
+    if out_format == "f16":
+        return out.astype(np.float16)  # IEEE round to nearest even
+    if out_format == "bf16":
+        bits = np.empty(out.shape, np.uint16)
+        lib.orc_f32_to_bf16_array(_ptr(out), _ptr(bits), out.size)
+        return bits
+    raise ValueError(f"unknown out_format {out_format!r}")
 
 
 def kv_insert(k_cache, v_cache, kv_kind, k, v, slot_mapping, *, k_scale=None,

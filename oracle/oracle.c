@@ -321,24 +321,46 @@ done:
 /* ------------------------------------------------------------------ */
 
 /*
+ * Scale-factor slot that holds token t's scale bytes within a kv_fused block
+ * [P5, is_kv_sf_interleaved]. In token order the slot is t. In the interleaved
+ * order the block's slots are split into spi equal runs dealt round-robin, and
+ * slot k holds token (k % spi) * (bs / spi) + k / spi (spi = scale bytes per
+ * token, one int32 per slot); the slot of t is found by walking k through
+ * that formula.
+ */
+static int sf_slot_of_token(int t, int bs, int spi, int interleaved) {
+  if (!interleaved) return t;
+  for (int k = 0; k < bs; ++k)
+    if ((k % spi) * (bs / spi) + k / spi == t) return k;
+  return -1;
+}
+
+/*
  * out[b*next_n + i, t] = sum over heads h (ascending, fp32 fmaf chain from +0)
- *   of weights[b*next_n + i, h] * S_h, with
+ *   of weights[b*next_n + i, h] * A(S_h), with
  *   S_h = sum over d (ascending, fp32) of deq(q[b,i,h,d]) * deq(k_t[d]),
  * for t < context_lens[b]; -inf for context_lens[b] <= t < max_context_len.
+ * A is the identity, or with relu != 0 the rectifier (S_h > 0 ? S_h : +0).
  *
  * Layouts from the API page: q [B, next_n, H, D/2] two E2M1 per byte; sf_q
  * [B, next_n, H] int32 holding D/sf_vec UE8M0 bytes; kv_fused
  * [num_blocks, bs, 1, D/2 + D/sf_vec] where each block stores all tokens' FP4
- * data first and then all tokens' scale bytes in token order; weights
- * [B*next_n, H] fp32. Readings: element 2j is the low nibble; byte g of the
- * int32 (bits 8g..8g+7) scales elements [g*sf_vec, (g+1)*sf_vec); there is no
- * activation between the dot product and the weight.
+ * data first and then all tokens' scale bytes, in token order, or with
+ * sf_interleaved != 0 in the interleaved slot order (sf_slot_of_token);
+ * weights [B*next_n, H] fp32. Readings: element 2j is the low nibble; byte g
+ * of the int32 (bits 8g..8g+7) scales elements [g*sf_vec, (g+1)*sf_vec); the
+ * pages name no activation, so A is the identity unless the caller asks for
+ * the rectifier. The output is fp32 here; fp16 / bf16 outputs are the
+ * round-to-nearest-even conversions of these values.
  */
 int orc_mqa_logits(float* out, int64_t out_row_stride, const uint8_t* q, const int32_t* sf_q,
                    const uint8_t* kv_fused, const float* weights, const int32_t* context_lens,
                    const int32_t* block_table, int B, int next_n, int H, int D, int bs,
-                   int max_blocks, int max_context_len, int sf_vec) {
+                   int max_blocks, int max_context_len, int sf_vec, int sf_interleaved,
+                   int relu) {
   int row_bytes = D / 2 + D / sf_vec;
+  int spi = D / sf_vec;
+  if (sf_interleaved && bs % spi != 0) return -3;
   for (int b = 0; b < B; ++b) {
     int L = context_lens[b];
     if (L > max_context_len || L > max_blocks * bs) return -2;
@@ -350,7 +372,8 @@ int orc_mqa_logits(float* out, int64_t out_row_stride, const uint8_t* q, const i
         int slot = t % bs;
         const uint8_t* base = kv_fused + blk * (int64_t)bs * row_bytes;
         const uint8_t* kdata = base + (int64_t)slot * (D / 2);
-        const uint8_t* ksf = base + (int64_t)bs * (D / 2) + (int64_t)slot * (D / sf_vec);
+        const uint8_t* ksf = base + (int64_t)bs * (D / 2) +
+                             (int64_t)sf_slot_of_token(slot, bs, spi, sf_interleaved) * (D / sf_vec);
         float acc = 0.0f;
         for (int h = 0; h < H; ++h) {
           const uint8_t* qd = q + (r * H + h) * (D / 2);
@@ -365,6 +388,7 @@ int orc_mqa_logits(float* out, int64_t out_row_stride, const uint8_t* q, const i
                        orc_ue8m0_to_f32(ksf[g]);
             sh += qv * kv;
           }
+          if (relu) sh = sh > 0.0f ? sh : 0.0f;
           acc = fmaf(weights[r * H + h], sh, acc);
         }
         orow[t] = acc;
@@ -373,6 +397,11 @@ int orc_mqa_logits(float* out, int64_t out_row_stride, const uint8_t* q, const i
     }
   }
   return 0;
+}
+
+/* fp32 -> bf16 bits of n values, round to nearest even (orc_f32_to_bf16). */
+void orc_f32_to_bf16_array(const float* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(x[i]);
 }
 
 /* ------------------------------------------------------------------ */

@@ -5,9 +5,13 @@ max_context_len, out).
 Independent references: per-head dot products by float64 table lookup and
 einsum (exact for the workload's exponent spread, tests/brute.py), one-hot
 weights (the chain then returns S_h itself, bit for bit), the fp32 recursive
-summation bound for general weights, relocation invariance, and the
--inf / untouched-row contract of the output.
+summation bound for general weights, relocation invariance, the
+-inf / untouched-row contract of the output, the interleaved scale-tail order
+(is_kv_sf_interleaved) against the token-order cache it was rewritten from,
+the rectifier variant, and the fp16 / bf16 outputs against torch's own
+round-to-nearest-even conversions.
 """
+import os
 import dataclasses
 
 import numpy as np
@@ -88,7 +92,74 @@ def pin_relocation(lib):
     assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
 
 
-ALL_PINS = [pin_one_hot_weights_exact, pin_weighted_sum_bound, pin_tail_and_rows, pin_relocation]
+def interleave_sf_tail(case, spi=4):
+    """The same cache with each block's scale tail rewritten in the interleaved
+    slot order of the API page: slot k holds token (k % spi) * (bs / spi) + k / spi."""
+    kv = case.kv_fused.copy()
+    nb, bs = kv.shape[0], kv.shape[1]
+    D = 2 * case.q.shape[-1]
+    flat = kv.reshape(nb, -1)
+    tail = flat[:, bs * D // 2:].reshape(nb, bs, spi).copy()
+    slot_token = [(k % spi) * (bs // spi) + k // spi for k in range(bs)]
+    flat[:, bs * D // 2:] = tail[:, slot_token, :].reshape(nb, -1)
+    return kv, slot_token
+
+
+def pin_interleaved_sf_tail(lib):
+    case = small_logits(seed=11, bs=64, lens=(200, 64, 1), max_len=256)
+    kv2, slot_token = interleave_sf_tail(case)
+    here = os.path.dirname(os.path.abspath(__file__))
+    printed = None
+    for line in open(os.path.join(here, "golden", "fp4_api.txt")):
+        if line.startswith("sf_interleave_slot_to_token"):
+            printed = [int(x) for x in line.split("#")[0].split("=")[1].split()]
+    assert slot_token[:len(printed)] == printed
+    base = run(case, lib)
+    got = run(dataclasses.replace(case, kv_fused=kv2), lib, sf_interleaved=True)
+    assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
+    # and reading the rewritten cache in token order is wrong (the pin has teeth)
+    wrong = run(dataclasses.replace(case, kv_fused=kv2), lib)
+    assert not np.array_equal(wrong.view(np.uint32), base.view(np.uint32))
+
+
+def pin_relu(lib):
+    case = small_logits(seed=12)
+    S = brute.logits_exact(case)
+    B, N, H = case.batch, case.next_n, case.num_heads
+    assert any((Sb < 0).any() for Sb in S) and any((Sb > 0).any() for Sb in S)
+    for h in (0, H - 1):
+        w = np.zeros((B * N, H), np.float32)
+        w[:, h] = 1.0
+        got = run(dataclasses.replace(case, weights=w), lib, relu=True)
+        for b in range(B):
+            L = int(case.context_lens[b])
+            for i in range(N):
+                ref = np.maximum(S[b][i, :, h], 0.0)
+                assert np.array_equal(got[b * N + i, :L].astype(np.float64), ref)
+    got = run(case, lib, relu=True)
+    w = case.weights.astype(np.float64)
+    for b in range(B):
+        L = int(case.context_lens[b])
+        for i in range(N):
+            terms = np.maximum(S[b][i], 0.0) * w[b * N + i][None, :]
+            bound = H * 2.0 ** -24 * np.abs(terms).sum(1) + 1e-30
+            assert np.all(np.abs(got[b * N + i, :L] - terms.sum(1)) <= bound)
+
+
+def pin_output_formats(lib):
+    import torch
+    case = small_logits(seed=13)
+    f32 = run(case, lib)
+    f16 = run(case, lib, out_format="f16")
+    bf16 = run(case, lib, out_format="bf16")
+    t = torch.from_numpy(f32)
+    assert np.array_equal(f16.view(np.uint16), t.to(torch.float16).numpy().view(np.uint16))
+    assert np.array_equal(bf16, t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    assert (bf16[0, int(case.context_lens[0]):case.max_context_len] == 0xFF80).all()  # -inf
+
+
+ALL_PINS = [pin_one_hot_weights_exact, pin_weighted_sum_bound, pin_tail_and_rows, pin_relocation,
+            pin_interleaved_sf_tail, pin_relu, pin_output_formats]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)

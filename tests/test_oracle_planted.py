@@ -63,9 +63,12 @@ MUTATIONS = {
     "int_round_away": ("float r = nearbyintf(y);", "float r = roundf(y);"),
     "logits_weight_row": ("acc = fmaf(weights[r * H + h], sh, acc);",
                           "acc = fmaf(weights[h], sh, acc);"),
-    "logits_sf_offset": ("const uint8_t* ksf = base + (int64_t)bs * (D / 2) + "
-                         "(int64_t)slot * (D / sf_vec);",
-                         "const uint8_t* ksf = base + (int64_t)slot * (D / sf_vec);"),
+    "logits_sf_offset": ("const uint8_t* ksf = base + (int64_t)bs * (D / 2) +\n",
+                         "const uint8_t* ksf = base +\n"),
+    "logits_sf_interleave_swapped": ("if ((k % spi) * (bs / spi) + k / spi == t) return k;",
+                                     "if ((k / spi) * (bs / spi) + k % spi == t) return k;"),
+    "logits_relu_inverted": ("if (relu) sh = sh > 0.0f ? sh : 0.0f;",
+                             "if (relu) sh = sh < 0.0f ? sh : 0.0f;"),
     "logits_tail_zero": ("orow[t] = -INFINITY;", "orow[t] = 0.0f;"),
     "logits_q_scale_byte": ("((qsf >> (8 * g)) & 0xFF)", "((qsf >> (8 * (3 - g))) & 0xFF)"),
     "insert_offset": ("int off = (int)(slot % bs);", "int off = (int)(slot % bs) ^ 1;"),
