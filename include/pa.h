@@ -160,28 +160,42 @@ pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t max_entries, 
 /* paged_mqa_logits [FP4API]                                                 */
 /* ------------------------------------------------------------------------ */
 
+/* Element type of the logits output [FP4API, output_dtype] and of its
+ * epilogue [FP4API, epi_dtype]. Zero is fp32, so a zero-initialised struct
+ * keeps the fp32 contract. */
+typedef enum { PA_LOGITS_F32 = 0, PA_LOGITS_F16 = 1, PA_LOGITS_BF16 = 2 } pa_logits_format;
+
 /*
  * out[b*next_n + i, t] = sum over heads h (ascending, fp32 fma chain) of
- *   weights[b*next_n + i, h] * (q[b,i,h,:] . k_t) with both operands MXFP4
+ *   weights[b*next_n + i, h] * A(q[b,i,h,:] . k_t) with both operands MXFP4
  *   (E2M1 values, one UE8M0 scale per sf_vec_size elements), for
  *   t < context_lens[b]; -inf for context_lens[b] <= t < max_context_len.
+ *   A is the identity, or with relu != 0 the rectifier max(., +0) (a variant
+ *   the API page does not name). The fp32 value is stored as out_format:
+ *   fp32, or fp16 / bf16 rounded to nearest even (-inf stays -inf).
  * Rows >= batch*next_n and columns >= max_context_len are not written.
  *
  * Layouts:
- *   out       [>= batch*next_n, out_row_stride] fp32, out_row_stride >= max_context_len
+ *   out       [>= batch*next_n, out_row_stride] of out_format, out_row_stride >=
+ *             max_context_len
  *   q         [batch, next_n, num_heads, head_dim/2] uint8, element 2j in the low nibble
  *   sf_q      [batch, next_n, num_heads] int32, byte g scales elements [32g, 32g+32)
  *   kv_fused  [num_blocks, block_size, 1, head_dim/2 + head_dim/sf_vec_size] uint8; each
  *             block holds [block_size * head_dim/2 FP4 bytes][block_size * head_dim/32 SF
- *             bytes], token order
+ *             bytes]. The SF tail is in token order, or with sf_interleaved != 0 in the
+ *             interleaved order [FP4API, is_kv_sf_interleaved]: 4-byte slot k holds the
+ *             scales of token (k % 4) * (block_size / 4) + k / 4.
  *   weights   [batch*next_n, num_heads] fp32
  *   block_table [batch, max_blocks_per_seq] int32 with max_blocks_per_seq >=
  *             round_up(max_context_len, 128) / block_size (checked on the host)
  * Supported: head_dim 128, sf_vec_size 32, block_size 64, num_heads a multiple of 16
- * up to 64, next_n 1..4. Workspace: none (pass NULL, 0).
+ * up to 64, next_n 1..4, epi_format PA_LOGITS_F32 (the page names fp16/bf16
+ * epilogues without defining their arithmetic; they return PA_ERR_UNSUPPORTED).
+ * There is no schedule argument: the grid follows max_context_len and each
+ * workgroup reads context_lens itself. Workspace: none (pass NULL, 0).
  */
 typedef struct pa_logits_args {
-  float* out;
+  void* out;
   int64_t out_row_stride;
   const uint8_t* q;
   const int32_t* sf_q;
@@ -198,6 +212,10 @@ typedef struct pa_logits_args {
   int64_t num_blocks;
   int32_t max_context_len;
   int32_t sf_vec_size;
+  pa_logits_format out_format;
+  pa_logits_format epi_format;
+  int32_t sf_interleaved;
+  int32_t relu;
 } pa_logits_args;
 
 size_t paged_mqa_logits_workspace_size(const pa_logits_args* a);

@@ -46,7 +46,8 @@ class LogitsArgs(ctypes.Structure):
                 ("kv_fused", _vp), ("weights", _vp), ("context_lens", _vp), ("block_table", _vp),
                 ("batch", _i32), ("next_n", _i32), ("num_heads", _i32), ("head_dim", _i32),
                 ("block_size", _i32), ("max_blocks_per_seq", _i32), ("num_blocks", _i64),
-                ("max_context_len", _i32), ("sf_vec_size", _i32)]
+                ("max_context_len", _i32), ("sf_vec_size", _i32), ("out_format", _i32),
+                ("epi_format", _i32), ("sf_interleaved", _i32), ("relu", _i32)]
 
 
 class InsertArgs(ctypes.Structure):
@@ -227,15 +228,29 @@ def pa_plan(block_table, context_lens, max_context_len, *, q_shape, k_cache_shap
 # MXFP4 paged MQA logits
 # ---------------------------------------------------------------------------
 
+LOGITS_F32, LOGITS_F16, LOGITS_BF16 = 0, 1, 2
+
+
+def _logits_format(dtype):
+    import torch
+    formats = {torch.float32: LOGITS_F32, torch.float16: LOGITS_F16, torch.bfloat16: LOGITS_BF16}
+    if dtype not in formats:
+        raise PaError(1, f"logits dtype must be float32, float16 or bfloat16, got {dtype}")
+    return formats[dtype]
+
+
 def _logits_args(out, q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len,
-                 sf_vec_size):
+                 sf_vec_size, out_format=LOGITS_F32, epi_format=LOGITS_F32, sf_interleaved=False,
+                 relu=False):
     B, next_n, H, Dh = q.shape
     return LogitsArgs(out=_ptr(out), out_row_stride=out.stride(0) if out is not None else 0,
                       q=_ptr(q), sf_q=_ptr(sf_q), kv_fused=_ptr(kv_fused), weights=_ptr(weights),
                       context_lens=_ptr(context_lens), block_table=_ptr(block_table), batch=B,
                       next_n=next_n, num_heads=H, head_dim=2 * Dh, block_size=kv_fused.shape[1],
                       max_blocks_per_seq=block_table.shape[1], num_blocks=kv_fused.shape[0],
-                      max_context_len=int(max_context_len), sf_vec_size=int(sf_vec_size))
+                      max_context_len=int(max_context_len), sf_vec_size=int(sf_vec_size),
+                      out_format=out_format, epi_format=epi_format,
+                      sf_interleaved=int(bool(sf_interleaved)), relu=int(bool(relu)))
 
 
 def paged_mqa_logits_workspace_size(q, sf_q, kv_fused, weights, context_lens, block_table,
@@ -246,16 +261,22 @@ def paged_mqa_logits_workspace_size(q, sf_q, kv_fused, weights, context_lens, bl
 
 
 def prepare_paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table,
-                             max_context_len, *, sf_vec_size=32, out=None, workspace=None,
-                             stream=None):
+                             max_context_len, *, sf_vec_size=32, output_dtype=None,
+                             epi_dtype=None, sf_interleaved=False, relu=False, out=None,
+                             workspace=None, stream=None):
     """paged_mqa_logits with its argument struct built once (see
     prepare_paged_attn_fwd); the result's .out is the output tensor."""
     import torch
     B, next_n = q.shape[:2]
+    if output_dtype is None:
+        output_dtype = out.dtype if out is not None else torch.float32
     if out is None:
-        out = torch.empty((B * next_n, max_context_len), dtype=torch.float32, device=q.device)
+        out = torch.empty((B * next_n, max_context_len), dtype=output_dtype, device=q.device)
+    elif out.dtype != output_dtype:
+        raise PaError(1, f"out is {out.dtype} but output_dtype is {output_dtype}")
     a = _logits_args(out, q, sf_q, kv_fused, weights, context_lens, block_table,
-                     max_context_len, sf_vec_size)
+                     max_context_len, sf_vec_size, _logits_format(output_dtype),
+                     _logits_format(epi_dtype or torch.float32), sf_interleaved, relu)
     lib = load()
     need = lib.paged_mqa_logits_workspace_size(ctypes.byref(a))
     if workspace is None and need:
@@ -267,10 +288,16 @@ def prepare_paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_tab
 
 
 def paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len, *,
-                     sf_vec_size=32, out=None, workspace=None, stream=None):
-    """Weighted per-head MXFP4 logits [B*next_n, max_context_len] fp32 (include/pa.h)."""
+                     sf_vec_size=32, output_dtype=None, epi_dtype=None, sf_interleaved=False,
+                     relu=False, out=None, workspace=None, stream=None):
+    """Weighted per-head MXFP4 logits [B*next_n, max_context_len] (include/pa.h):
+    float32 by default, or output_dtype float16 / bfloat16; sf_interleaved
+    reads kv_fused scale tails in the interleaved slot order; relu applies
+    max(., 0) between each head's dot product and its weight."""
     call = prepare_paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table,
-                                    max_context_len, sf_vec_size=sf_vec_size, out=out,
+                                    max_context_len, sf_vec_size=sf_vec_size,
+                                    output_dtype=output_dtype, epi_dtype=epi_dtype,
+                                    sf_interleaved=sf_interleaved, relu=relu, out=out,
                                     workspace=workspace, stream=stream)
     call()
     return call.out

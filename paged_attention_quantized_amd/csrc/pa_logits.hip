@@ -35,7 +35,7 @@ typedef int i8v __attribute__((ext_vector_type(8)));
 constexpr int kLogitsBlocks = LOGITS_NB;  // 64-token blocks per wave
 
 struct LogitsParams {
-  float* out;
+  void* out;
   int64_t out_stride;
   const uint8_t* q;
   const int32_t* sf_q;
@@ -44,6 +44,8 @@ struct LogitsParams {
   const int32_t* context_lens;
   const int32_t* block_table;
   int B, max_blocks, max_ctx, ngroups;
+  int sfi;   // scale tail in the interleaved slot order
+  int relu;  // rectifier between each head's dot and its weight
 };
 
 // 4x4 transpose of (lane group, register): after it, register t of lane group
@@ -72,7 +74,9 @@ __device__ __forceinline__ void pin(T& v) {
 // A workgroup is 4 waves over 4 consecutive chunks of one sequence; NB =
 // 64-token KV blocks per wave (chunk = 64*NB tokens). The q rows of the
 // sequence are staged once per workgroup in LDS.
-template <int NN, int H, int NB>
+// OT: output element type (float, _Float16 or __bf16; conversions round to
+// nearest even).
+template <int NN, int H, int NB, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE))) void logits_kernel(
     LogitsParams p) {
   constexpr int D = 128, BS = 64;
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   // blocks of this chunk inside max_context_len, and those holding visible tokens
   const int nblk = max(0, min(NB, (p.max_ctx - t_chunk + BS - 1) / BS));
   const int nvis = t_chunk < L ? min(nblk, (L - t_chunk + BS - 1) / BS) : 0;
-  float* orow = p.out + (size_t)b * NN * p.out_stride;
+  OT* orow = reinterpret_cast<OT*>(p.out) + (size_t)b * NN * p.out_stride;
 
   // ---- loads that need only b: this chunk's block-table columns (lane k reads
   // column k, clamped to the last column inside max_context_len), the q rows of
@@ -132,8 +136,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
 #pragma unroll
       for (int tau = 0; tau < 4; ++tau) {
         const int tok = 16 * tau + j;
+        // scale slot of the token: token order, or the interleaved order in
+        // which slot k holds token (k % SFB) * (BS / SFB) + k / SFB [FP4API,
+        // is_kv_sf_interleaved]; for tok = 16 tau + j that slot is 4 j + tau
+        static_assert(SFB == 4 && BS / SFB == 16, "interleaved slot arithmetic");
+        const int slot = p.sfi ? SFB * j + tau : tok;
         kraw[k][tau] = *reinterpret_cast<const u4*>(blk + tok * ROWB + 16 * g);
-        ks[k][tau] = blk[BS * ROWB + tok * SFB + g];
+        ks[k][tau] = blk[BS * ROWB + slot * SFB + g];
       }
     }
   }
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
     const int t = t_chunk + k * BS + lane;
     if (k >= nvis && k < nblk && t < p.max_ctx)
 #pragma unroll
-      for (int i = 0; i < NN; ++i) orow[(size_t)i * p.out_stride + t] = -INFINITY;
+      for (int i = 0; i < NN; ++i) orow[(size_t)i * p.out_stride + t] = (OT)(-INFINITY);
   }
   if (!grp_live) return;  // uniform over the workgroup
 
@@ -201,34 +210,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
         for (int e = 0; e < 4; ++e) transpose4(s[rt][0][e], s[rt][1][e], s[rt][2][e], s[rt][3][e]);
       const float* wrow = wlds + i * H;
       float acc = 0.f;
+      if (p.relu) {
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau)
+        for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
-        for (int rt = 0; rt < NTI; ++rt)
+          for (int rt = 0; rt < NTI; ++rt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = fmaf(wrow[HG * tau + 4 * rt + e], s[rt][tau][e], acc);
-      if (t < p.max_ctx) orow[(size_t)i * p.out_stride + t] = t < L ? acc : -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+              const float x = s[rt][tau][e];
+              acc = fmaf(wrow[HG * tau + 4 * rt + e], x > 0.f ? x : 0.f, acc);
+            }
+      } else {
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+          for (int rt = 0; rt < NTI; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc = fmaf(wrow[HG * tau + 4 * rt + e], s[rt][tau][e], acc);
+      }
+      if (t < p.max_ctx) orow[(size_t)i * p.out_stride + t] = (OT)(t < L ? acc : -INFINITY);
     }
   }
 }
 
 typedef void (*LogitsFn)(LogitsParams);
 
-template <int NN, int NB>
+template <int NN, int NB, typename OT>
 LogitsFn pick_h(int H) {
-  if (H == 16) return logits_kernel<NN, 16, NB>;
-  if (H == 32) return logits_kernel<NN, 32, NB>;
-  if (H == 64) return logits_kernel<NN, 64, NB>;
+  if (H == 16) return logits_kernel<NN, 16, NB, OT>;
+  if (H == 32) return logits_kernel<NN, 32, NB, OT>;
+  if (H == 64) return logits_kernel<NN, 64, NB, OT>;
+  return nullptr;
+}
+
+template <int NB, typename OT>
+LogitsFn pick_nn(int NN, int H) {
+  switch (NN) {
+    case 1: return pick_h<1, NB, OT>(H);
+    case 2: return pick_h<2, NB, OT>(H);
+    case 3: return pick_h<3, NB, OT>(H);
+    case 4: return pick_h<4, NB, OT>(H);
+  }
   return nullptr;
 }
 
 template <int NB>
-LogitsFn pick_nn(int NN, int H) {
-  switch (NN) {
-    case 1: return pick_h<1, NB>(H);
-    case 2: return pick_h<2, NB>(H);
-    case 3: return pick_h<3, NB>(H);
-    case 4: return pick_h<4, NB>(H);
+LogitsFn pick_out(int format, int NN, int H) {
+  switch (format) {
+    case PA_LOGITS_F32: return pick_nn<NB, float>(NN, H);
+    case PA_LOGITS_F16: return pick_nn<NB, _Float16>(NN, H);
+    case PA_LOGITS_BF16: return pick_nn<NB, __bf16>(NN, H);
   }
   return nullptr;
 }
@@ -255,7 +287,16 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
     return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: head_dim must be 128, sf_vec_size 32");
   if (a->block_size != 64) return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: block_size must be 64");
   if (a->next_n > 4) return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: next_n must be 1..4");
-  LogitsFn fn = pick_nn<kLogitsBlocks>(a->next_n, a->num_heads);
+  if (a->out_format != PA_LOGITS_F32 && a->out_format != PA_LOGITS_F16 &&
+      a->out_format != PA_LOGITS_BF16)
+    return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: unknown out_format");
+  if (a->epi_format != PA_LOGITS_F32)
+    return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: only an fp32 epilogue is supported");
+  if (a->sf_interleaved != 0 && a->sf_interleaved != 1)
+    return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: sf_interleaved must be 0 or 1");
+  if (a->relu != 0 && a->relu != 1)
+    return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: relu must be 0 or 1");
+  LogitsFn fn = pick_out<kLogitsBlocks>(a->out_format, a->next_n, a->num_heads);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: num_heads must be 16, 32 or 64");
   if (a->out_row_stride < a->max_context_len)
     return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: out_row_stride < max_context_len");
@@ -277,6 +318,8 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
   p.w = a->weights;
   p.context_lens = a->context_lens;
   p.block_table = a->block_table;
+  p.sfi = a->sf_interleaved;
+  p.relu = a->relu;
   p.B = a->batch;
   p.max_blocks = a->max_blocks_per_seq;
   p.max_ctx = a->max_context_len;

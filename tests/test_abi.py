@@ -4,6 +4,7 @@ codes without enqueuing any GPU work (no compute call is made here)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -114,3 +115,31 @@ def test_insert_validation():
     a.num_slots = 0
     a.k_scale = 0x1000
     assert lib.kv_insert(ctypes.byref(a), None) == 0  # nothing to insert: no launch
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The binding's ctypes structs have the sizes and field offsets the C
+    compiler gives the structs of include/pa.h."""
+    structs = {"pa_attn_args": pa.AttnArgs, "pa_logits_args": pa.LogitsArgs,
+               "pa_insert_args": pa.InsertArgs}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "pa.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                               text=True).stdout.split("\n"):
+        if line:
+            c, f, v = line.split()
+            got[(c, f)] = int(v)
+    for cname, py in structs.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)

@@ -21,21 +21,26 @@ from tests.gpu_util import dev, say
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(pa, case, out_rows=None, out_stride=None):
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def run_gpu(pa, case, out_rows=None, out_stride=None, out_format="f32", **kw):
     rows = out_rows or case.batch * case.next_n
     stride = out_stride or case.max_context_len
-    out = torch.full((rows, stride), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((rows, stride), float("nan"), dtype=TORCH_DT[out_format], device="cuda")
     pa.paged_mqa_logits(dev(case.q), dev(case.sf_q), dev(case.kv_fused), dev(case.weights),
                         dev(case.context_lens), dev(case.block_table), case.max_context_len,
-                        out=out)
+                        out=out, **kw)
     torch.cuda.synchronize()
+    if out_format == "bf16":
+        return out.view(torch.int16).cpu().numpy().view(np.uint16)
     return out.cpu().numpy()
 
 
-def run_oracle(case, out_rows=None, out_stride=None):
+def run_oracle(case, out_rows=None, out_stride=None, **kw):
     return oracle.mqa_logits(case.q, case.sf_q, case.kv_fused, case.weights, case.context_lens,
                              case.block_table, case.max_context_len, out_rows=out_rows,
-                             out_row_stride=out_stride)
+                             out_row_stride=out_stride, **kw)
 
 
 def assert_same(got, ref, name):
@@ -133,3 +138,51 @@ def test_full_mxfp4_logits_sampled(pa):
                                   context_lens=case.context_lens[b:b + 1],
                                   block_table=case.block_table[b:b + 1])
         assert_same(got[b * N:(b + 1) * N], run_oracle(sub), f"full b={b}")
+
+
+# ---------------------------------------------------------------------------
+# API breadth ("flashinfer.fp4_paged_mqa_logits" page: output_dtype,
+# is_kv_sf_interleaved; and the rectifier variant): bit-exact against the oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_logits_output_formats(pa, fmt):
+    case = small_cases()[0]
+    say(f"logits output format {fmt}")
+    got = run_gpu(pa, case, out_format=fmt)
+    ref = run_oracle(case, out_format=fmt)
+    assert got.dtype.itemsize == 2 and ref.dtype.itemsize == 2
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), fmt
+
+
+def test_logits_interleaved_scale_tail(pa):
+    from tests.test_oracle_logits import interleave_sf_tail
+    case = small_cases()[0]
+    kv2, _ = interleave_sf_tail(case)
+    inter = dataclasses.replace(case, kv_fused=kv2)
+    say("logits interleaved scale tail")
+    got = run_gpu(pa, inter, sf_interleaved=True)
+    assert_same(got, run_oracle(inter, sf_interleaved=True), "interleaved")
+    assert np.array_equal(got.view(np.uint32), run_gpu(pa, case).view(np.uint32))
+
+
+@pytest.mark.parametrize("idx", [0, 2])
+def test_logits_relu(pa, idx):
+    case = small_cases()[idx]
+    say(f"logits relu {case.name}")
+    got = run_gpu(pa, case, relu=True)
+    assert_same(got, run_oracle(case, relu=True), "relu " + case.name)
+    plain = run_gpu(pa, case)
+    assert not np.array_equal(np.nan_to_num(got), np.nan_to_num(plain))
+
+
+def test_logits_format_errors(pa):
+    case = small_cases()[0]
+    with pytest.raises(pa.PaError, match="UNSUPPORTED"):
+        run_gpu(pa, case, epi_dtype=torch.float16)
+    out = torch.empty((case.batch * case.next_n, case.max_context_len), dtype=torch.float16,
+                      device="cuda")
+    with pytest.raises(pa.PaError, match="INVALID_ARG"):
+        pa.paged_mqa_logits(dev(case.q), dev(case.sf_q), dev(case.kv_fused), dev(case.weights),
+                            dev(case.context_lens), dev(case.block_table), case.max_context_len,
+                            out=out, output_dtype=torch.float32)
