@@ -84,6 +84,12 @@ def _bind(lib):
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.orc_f32_to_bf16_array.argtypes = [P, P, i64]
     lib.orc_f32_to_bf16_array.restype = None
+    lib.orc_f32_to_e2m1.argtypes = [f32]
+    lib.orc_f32_to_e2m1.restype = ctypes.c_uint8
+    lib.orc_mx_scale_byte.argtypes = [f32]
+    lib.orc_mx_scale_byte.restype = ctypes.c_uint8
+    lib.orc_mxfp4_insert.argtypes = [P, P, i32, P, i64, i64, i32, i32, i64, i32, i32]
+    lib.orc_mxfp4_insert.restype = i32
     lib.orc_mqa_logits.restype = i32
     lib.orc_kv_insert.argtypes = [P, P, i32, P, P, i32, P, i64, i64,
                                   i32, i32, i32, i64, P, i32, P, i32]
@@ -229,3 +235,35 @@ def kv_insert(k_cache, v_cache, kv_kind, k, v, slot_mapping, *, k_scale=None,
                            v_scale_mode)
     if rc != 0:
         raise ValueError(f"orc_kv_insert failed with code {rc}")
+
+
+def f32_to_e2m1(x, lib=None):
+    """E2M1 codes (uint8, sign in bit 3) of fp32 values, nearest-even, saturating."""
+    lib = lib or load()
+    return np.array([lib.orc_f32_to_e2m1(float(v)) for v in np.asarray(x, np.float32).ravel()],
+                    np.uint8).reshape(np.shape(x))
+
+
+def mx_scale_byte(amax, lib=None):
+    """UE8M0 scale byte of a group with largest magnitude amax (see orc_mx_scale_byte)."""
+    lib = lib or load()
+    return np.array([lib.orc_mx_scale_byte(float(v)) for v in np.asarray(amax, np.float32).ravel()],
+                    np.uint8).reshape(np.shape(amax))
+
+
+def mxfp4_insert(kv_fused, k_bits, slot_mapping, *, in_dtype="f16", sf_vec_size=32,
+                 sf_interleaved=False, lib=None):
+    """Reference MXFP4 insert (see orc_mxfp4_insert in oracle.c): quantizes rows of
+    k_bits (uint16 fp16 / bf16 bits, [T, D]) into kv_fused ([num_blocks, bs, 1,
+    D/2 + D/sf_vec] uint8, modified in place) at slot_mapping (int64)."""
+    lib = lib or load()
+    assert kv_fused.flags.c_contiguous and kv_fused.dtype == np.uint8
+    k = np.ascontiguousarray(k_bits, np.uint16)
+    T, D = k.shape
+    sm = _c(slot_mapping, np.int64)
+    rc = lib.orc_mxfp4_insert(_ptr(kv_fused), _ptr(k), 1 if in_dtype == "bf16" else 0, _ptr(sm),
+                              T, sm.shape[0], D, kv_fused.shape[1], kv_fused.shape[0],
+                              sf_vec_size, int(bool(sf_interleaved)))
+    if rc != 0:
+        raise ValueError(f"orc_mxfp4_insert failed with code {rc}")
+    return kv_fused

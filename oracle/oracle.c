@@ -161,6 +161,43 @@ float orc_ue8m0_to_f32(uint8_t e) {
   return ldexpf(1.0f, (int)e - 127);
 }
 
+/*
+ * E2M1 code of y, round to nearest with ties to the even code, saturating to
+ * +-6 (the largest E2M1 magnitude). The magnitude code is the index of the
+ * nearest of the 8 representable magnitudes; the sign bit is y's sign bit.
+ * (Reading: the pages give no rounding rule for FP4 writes; nearest-even with
+ * saturation is the OCP Microscaling conversion.)
+ */
+uint8_t orc_f32_to_e2m1(float y) {
+  float a = fabsf(y);
+  int best = 0;
+  float bestd = INFINITY;
+  for (int c = 0; c < 8; ++c) {
+    float d = fabsf(a - orc_e2m1_to_f32((uint8_t)c));
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      bestd = d;
+      best = c;
+    }
+  }
+  if (a > 6.0f) best = 7; /* saturate: ties above 6 cannot occur, 6 is the top code */
+  return (uint8_t)(best | (signbit(y) ? 8 : 0));
+}
+
+/*
+ * UE8M0 scale byte of a 32-value group with largest magnitude amax (OCP
+ * Microscaling rule, a reading: the pages print no quantizer): the shared
+ * scale is 2^(floor(log2(amax)) - 2), 2 being the exponent of E2M1's largest
+ * power of two, clamped to the finite bytes [0, 254]; an all-zero group gets
+ * byte 0.
+ */
+uint8_t orc_mx_scale_byte(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e;
+  frexpf(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2(amax)) = e - 1 */
+  int b = (e - 1) - 2 + 127;
+  return (uint8_t)(b < 0 ? 0 : (b > 254 ? 254 : b));
+}
+
 /* ------------------------------------------------------------------ */
 /* Paged KV element access                                             */
 /* ------------------------------------------------------------------ */
@@ -462,6 +499,56 @@ int orc_kv_insert(uint8_t* k_cache, uint8_t* v_cache, int kv_kind, const uint16_
                    scale_of(k_scale, k_scale_mode, hk, d, D), k[idx]);
         store_code(v_cache, kv_kind, blk, off, hk, d, bs, Hkv, D, in_value(v, in_is_bf16, idx),
                    scale_of(v_scale, v_scale_mode, hk, d, D), v[idx]);
+      }
+    }
+  }
+  return 0;
+}
+
+/*
+ * MXFP4 insert into the kv_fused layout [P5, kv_fused; is_kv_sf_interleaved]:
+ * row i of k ([T, D], fp16 or bf16) goes to token slot_mapping[i] (block =
+ * slot / bs, position = slot % bs); rows with i >= num_slots or slot < 0 are
+ * skipped [P4, Design]. Each group of sf_vec values takes the scale byte of
+ * orc_mx_scale_byte and E2M1 codes of x / 2^(byte - 127) (an exact power-of-two
+ * division); element 2j is the low nibble. The group bytes go to
+ * [bs * D/2 data][bs * D/sf_vec scales] of the block, the scales of the token
+ * at its token-order slot or its interleaved slot (sf_slot_of_token).
+ */
+int orc_mxfp4_insert(uint8_t* kv_fused, const uint16_t* k, int in_is_bf16,
+                     const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots, int D,
+                     int bs, int64_t num_blocks, int sf_vec, int sf_interleaved) {
+  int spi = D / sf_vec;
+  int64_t block_bytes = (int64_t)bs * (D / 2 + D / sf_vec);
+  if (D % sf_vec != 0 || sf_vec % 2 != 0) return -1;
+  if (sf_interleaved && bs % spi != 0) return -3;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    if (i >= num_slots) continue;
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    int64_t blk = slot / bs;
+    int pos = (int)(slot % bs);
+    if (blk >= num_blocks) return -2;
+    uint8_t* base = kv_fused + blk * block_bytes;
+    uint8_t* data = base + (int64_t)pos * (D / 2);
+    uint8_t* sf = base + (int64_t)bs * (D / 2) +
+                  (int64_t)sf_slot_of_token(pos, bs, spi, sf_interleaved) * spi;
+    for (int g = 0; g < spi; ++g) {
+      float amax = 0.0f;
+      for (int j = 0; j < sf_vec; ++j) {
+        float x = in_value(k, in_is_bf16, i * D + g * sf_vec + j);
+        if (fabsf(x) > amax) amax = fabsf(x);
+      }
+      uint8_t byte = orc_mx_scale_byte(amax);
+      sf[g] = byte;
+      for (int j = 0; j < sf_vec; ++j) {
+        int d = g * sf_vec + j;
+        float x = in_value(k, in_is_bf16, i * D + d);
+        uint8_t c = orc_f32_to_e2m1(ldexpf(x, 127 - (int)byte));
+        if (d % 2 == 0)
+          data[d / 2] = (uint8_t)((data[d / 2] & 0xF0) | c);
+        else
+          data[d / 2] = (uint8_t)((data[d / 2] & 0x0F) | (c << 4));
       }
     }
   }

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from tests import test_oracle_attn, test_oracle_insert, test_oracle_logits
+from tests import test_oracle_attn, test_oracle_insert, test_oracle_logits, test_oracle_mxfp4
 
 
 def pin_codec_e4m3(lib):
@@ -38,7 +38,7 @@ def pin_codec_round(lib):
 
 
 PINS = ([pin_codec_e4m3, pin_codec_round] + test_oracle_attn.ALL_PINS +
-        test_oracle_logits.ALL_PINS + test_oracle_insert.ALL_PINS)
+        test_oracle_logits.ALL_PINS + test_oracle_insert.ALL_PINS + test_oracle_mxfp4.ALL_PINS)
 
 MUTATIONS = {
     "gqa_head_map": ("int hk = h / group;", "int hk = h % Hkv;"),
@@ -52,7 +52,8 @@ MUTATIONS = {
     "per_channel_transposed": ("if (mode == ORC_SCALE_PER_CHANNEL) return scale[hk * D + d];",
                                "if (mode == ORC_SCALE_PER_CHANNEL) return scale[d * 2 + hk];"),
     "e4m3_bias": ("v = ldexpf(8.0f + (float)m, e - 10);", "v = ldexpf(8.0f + (float)m, e - 9);"),
-    "e4m3_ties_up": ("(d == bestd && (c & 1) == 0)", "(d == bestd)"),
+    "e4m3_ties_up": ("- a);\n    if (d < bestd || (d == bestd && (c & 1) == 0)) {",
+                     "- a);\n    if (d < bestd || (d == bestd)) {"),
     "int4_nibble_order": ("int nib = (d % 2 == 0) ? (byte & 15) : (byte >> 4);\n    return",
                           "int nib = (d % 2 == 0) ? (byte >> 4) : (byte & 15);\n    return"),
     "v_slot_index": ("int slot = t % bs;\n          for (int d = 0; d < D; ++d) {\n"
@@ -72,6 +73,15 @@ MUTATIONS = {
     "logits_tail_zero": ("orow[t] = -INFINITY;", "orow[t] = 0.0f;"),
     "logits_q_scale_byte": ("((qsf >> (8 * g)) & 0xFF)", "((qsf >> (8 * (3 - g))) & 0xFF)"),
     "insert_offset": ("int off = (int)(slot % bs);", "int off = (int)(slot % bs) ^ 1;"),
+    "mx_scale_offset": ("int b = (e - 1) - 2 + 127;", "int b = (e - 1) - 1 + 127;"),
+    "e2m1_ties_odd": ("float d = fabsf(a - orc_e2m1_to_f32((uint8_t)c));\n"
+                      "    if (d < bestd || (d == bestd && (c & 1) == 0)) {",
+                      "float d = fabsf(a - orc_e2m1_to_f32((uint8_t)c));\n"
+                      "    if (d < bestd || (d == bestd && (c & 1) == 1)) {"),
+    "mx_nibble_order": ("data[d / 2] = (uint8_t)((data[d / 2] & 0xF0) | c);",
+                        "data[d / 2] = (uint8_t)((data[d / 2] & 0x0F) | (c << 4));"),
+    "mx_sf_token_order": ("(int64_t)sf_slot_of_token(pos, bs, spi, sf_interleaved) * spi;",
+                          "(int64_t)pos * spi;"),
 }
 
 

@@ -484,3 +484,37 @@ def insert_case(seed, *, T, Hkv, D, bs, kv_kind, scale_mode, slotless_tail=0, ne
     return InsertCase(k=k, v=v, slot_mapping=slots, num_blocks=nb, block_size=bs,
                       kv_kind=kv_kind, k_scale=k_scale, v_scale=v_scale, scale_mode=scale_mode,
                       k_cache=kc, v_cache=vc)
+
+
+@dataclasses.dataclass
+class Mxfp4InsertCase:
+    k_bits: np.ndarray         # [T, D] uint16 bits of fp16 or bf16 values
+    in_dtype: str              # "f16" or "bf16"
+    slot_mapping: np.ndarray   # [num_slots] int64 (num_slots <= T; -1 = no slot)
+    kv_fused: np.ndarray       # [num_blocks, bs, 1, D/2 + D/32] uint8, prefilled with 0xFF
+    sf_interleaved: bool
+
+
+def mxfp4_insert_case(seed, *, T, D=128, bs=64, in_dtype="f16", slotless_tail=0, neg_slots=0,
+                      sf_interleaved=False, spread=8.0) -> Mxfp4InsertCase:
+    """New key rows [T, D]: N(0, 1) values times a per-row factor 2^u, u uniform
+    in [-spread, spread], as fp16 or bf16 bits; a few exact zeros and one
+    all-zero row. Distinct random slots in blocks 1..; the last `slotless_tail`
+    rows have no slot and `neg_slots` rows have slot -1. The destination is
+    prefilled with 0xFF so untouched bytes are visible."""
+    import torch
+    rng = np.random.default_rng(seed)
+    num_slots = T - slotless_tail
+    nb = (T + bs - 1) // bs + 3
+    slots = rng.choice(np.arange(bs, nb * bs), num_slots, replace=False).astype(np.int64)
+    if neg_slots:
+        slots[rng.choice(num_slots, neg_slots, replace=False)] = -1
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    x *= np.exp2(rng.uniform(-spread, spread, (T, 1))).astype(np.float32)
+    x[rng.random((T, D)) < 0.02] = 0.0
+    x[0] = 0.0
+    t = torch.from_numpy(x).to(torch.bfloat16 if in_dtype == "bf16" else torch.float16)
+    bits = t.view(torch.int16).numpy().view(np.uint16).copy()
+    kv = np.full((nb, bs, 1, D // 2 + D // 32), 0xFF, np.uint8)
+    return Mxfp4InsertCase(k_bits=bits, in_dtype=in_dtype, slot_mapping=slots, kv_fused=kv,
+                           sf_interleaved=sf_interleaved)
