@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0
 
-WORKLOADS = ("fp8_decode", "int8_perchan", "int4_perchan", "fp8_verify", "mxfp4_logits")
+WORKLOADS = ("fp8_decode", "int8_perchan", "int4_perchan", "fp8_verify", "mxfp4_logits",
+             "mxfp4_insert")
 
 
 class Hip:
@@ -67,6 +68,8 @@ def make_case(name):
         return W.fp8_verify()
     if name == "mxfp4_logits":
         return W.mxfp4_logits()
+    if name == "mxfp4_insert":
+        return W.mxfp4_insert_case(1005, T=32768, in_dtype="f16")
     raise ValueError(name)
 
 
@@ -128,6 +131,8 @@ def kernel_sources(kernel_tag):
     """The source files a kernel is built from (its traffic record is tied to them)."""
     if kernel_tag.startswith("logits"):
         return ["pa_device.hpp", "pa_logits.hip"]
+    if kernel_tag.startswith("mxfp4_insert"):
+        return ["pa_device.hpp", "pa_insert_mxfp4.hip"]
     return ["pa_device.hpp", "pa_attn.hpp", "pa_attn.hip", "pa_attn_e4m3.hip", "pa_attn_f16.hip",
             "pa_attn_int4.hip", "pa_attn_int8.hip"]
 
@@ -228,6 +233,28 @@ def bench_logits(args, torch, pa, hip, case):
                             "kv_tokens": int(case.context_lens.astype("int64").sum())})
 
 
+def bench_mxfp4_insert(args, torch, pa, hip, case):
+    """MXFP4 insert of T rows: algorithmic bytes are the fp16 input rows, the
+    68 written bytes per row and the 8-byte slots."""
+    import numpy as np
+
+    T, D = case.k_bits.shape
+    alg_bytes = T * (2 * D + D // 2 + D // 32 + 8)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kv = dev(case.kv_fused)
+    k = dev(case.k_bits.view(np.int16)).view(torch.float16)
+    sm = dev(case.slot_mapping)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    call = pa.prepare_kv_insert_mxfp4(kv, k, sm, stream=stream)
+
+    def step(_k):
+        call()
+
+    return run_timed(args, torch, pa, hip, step, alg_bytes, 0,
+                     extra={"npools": 1, "query_tokens": T, "kv_tokens": T})
+
+
 def run_timed(args, torch, pa, hip, step, alg_bytes, qo_bytes, extra):
     for k in range(args.warmup):
         step(k)
@@ -292,7 +319,14 @@ def main():
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     case = make_case(args.workload)
     print("[bench] timing", file=sys.stderr, flush=True)
-    if args.workload == "mxfp4_logits":
+    if args.workload == "mxfp4_insert":
+        r = bench_mxfp4_insert(args, torch, pa, hip, case)
+        tag = "mxfp4_insert"
+        config = {"workload": args.workload, "rows": int(case.k_bits.shape[0]), "head_dim": 128,
+                  "block_size": int(case.kv_fused.shape[1]), "in_dtype": "fp16",
+                  "sf_vec_size": 32, "slots": "random distinct, seed 1005"}
+        dtype = "f16->mxfp4"
+    elif args.workload == "mxfp4_logits":
         r = bench_logits(args, torch, pa, hip, case)
         tag = "logits_" + args.workload
         config = {"workload": args.workload, "batch": case.batch, "next_n": case.next_n,
@@ -333,7 +367,7 @@ def main():
                      "traffic": traffic, "kernel": tag,
                      "alg_bytes_per_launch": r["alg_bytes"]},
     }
-    if not args.no_cpu_baseline and args.workload != "mxfp4_logits":
+    if not args.no_cpu_baseline and args.workload not in ("mxfp4_logits", "mxfp4_insert"):
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)

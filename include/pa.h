@@ -223,6 +223,49 @@ pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace, size_t work
                            void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* kv_insert_mxfp4 [FP4API] [INSERT]                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For each row i < num_tokens with i < num_slots and slot_mapping[i] >= 0, the
+ * 128 values k[i, :] are quantized to MXFP4 and written to token position
+ * slot % block_size of block slot / block_size of kv_fused (the layout of
+ * paged_mqa_logits: [block_size * 64 FP4 bytes][block_size * 4 scale bytes]).
+ * Rows without a slot are skipped and their destination left untouched
+ * [INSERT, Design: the KV-only mode skips rows that have no slot]; so are rows
+ * whose slot lies past num_blocks * block_size.
+ *
+ * Quantizer (the pages print none; the OCP Microscaling rule): per group of 32
+ * values with largest magnitude amax, the UE8M0 scale byte is
+ * floor(log2(amax)) - 2 + 127 clamped to [0, 254] (0 for an all-zero group),
+ * and each value divided by 2^(byte - 127) is rounded to the nearest E2M1
+ * value, ties to the even code, saturating at +-6; the sign bit is the
+ * input's. Element 2j is the low nibble. The token's 4 scale bytes go to slot
+ * pos in token order, or with sf_interleaved != 0 to the slot k with
+ * (k % 4) * (block_size / 4) + k / 4 == pos [FP4API, is_kv_sf_interleaved].
+ *
+ * Layouts: k [num_tokens, 128] fp16 or bf16 (in_dtype); slot_mapping
+ * [num_slots] int64; kv_fused [num_blocks, block_size, 1, 68] uint8.
+ * Inputs must be finite. Supported: head_dim 128, sf_vec_size 32, block_size a
+ * multiple of 4. Errors: status codes, nothing enqueued.
+ */
+typedef struct pa_mxfp4_insert_args {
+  uint8_t* kv_fused;
+  const void* k;
+  pa_dtype in_dtype;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t num_slots;
+  int32_t head_dim;
+  int32_t block_size;
+  int64_t num_blocks;
+  int32_t sf_vec_size;
+  int32_t sf_interleaved;
+} pa_mxfp4_insert_args;
+
+pa_status kv_insert_mxfp4(const pa_mxfp4_insert_args* a, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* kv_insert [INSERT]                                                        */
 /* ------------------------------------------------------------------------ */
 

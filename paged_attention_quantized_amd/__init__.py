@@ -14,6 +14,7 @@ __all__ = [
     "load", "paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
     "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "pa_set_profile_events",
     "prepare_paged_attn_fwd", "prepare_paged_mqa_logits", "Prepared", "PaError",
+    "kv_insert_mxfp4", "prepare_kv_insert_mxfp4",
     "KV_F16", "KV_BF16", "KV_E4M3", "KV_INT8", "KV_INT4",
     "SCALE_NONE", "SCALE_PER_TENSOR", "SCALE_PER_CHANNEL",
 ]
@@ -58,6 +59,13 @@ class InsertArgs(ctypes.Structure):
                 ("k_scale_mode", _i32), ("v_scale", _vp), ("v_scale_mode", _i32)]
 
 
+class Mxfp4InsertArgs(ctypes.Structure):
+    _fields_ = [("kv_fused", _vp), ("k", _vp), ("in_dtype", _i32), ("slot_mapping", _vp),
+                ("num_tokens", _i64), ("num_slots", _i64), ("head_dim", _i32),
+                ("block_size", _i32), ("num_blocks", _i64), ("sf_vec_size", _i32),
+                ("sf_interleaved", _i32)]
+
+
 class PaError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -67,8 +75,8 @@ class PaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
-           "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "pa_last_error",
-           "pa_set_profile_events"]
+           "paged_mqa_logits_workspace_size", "kv_insert", "kv_insert_mxfp4", "pa_dequantize",
+           "pa_last_error", "pa_set_profile_events"]
 
 
 def load(path: str | None = None):
@@ -92,6 +100,8 @@ def load(path: str | None = None):
     lib.paged_mqa_logits_workspace_size.restype = ctypes.c_size_t
     lib.kv_insert.argtypes = [ctypes.POINTER(InsertArgs), _vp]
     lib.kv_insert.restype = _i32
+    lib.kv_insert_mxfp4.argtypes = [ctypes.POINTER(Mxfp4InsertArgs), _vp]
+    lib.kv_insert_mxfp4.restype = _i32
     lib.pa_dequantize.argtypes = [_i32, _vp, _i64, _vp, _i32, _i64, _vp, _vp]
     lib.pa_dequantize.restype = _i32
     lib.pa_last_error.argtypes = []
@@ -318,6 +328,28 @@ def kv_insert(k_cache, v_cache, k, v, slot_mapping, *, kv_kind, k_scale=None, v_
                    k_scale=_ptr(k_scale), k_scale_mode=_mode(k_scale, k_scale_mode),
                    v_scale=_ptr(v_scale), v_scale_mode=_mode(v_scale, v_scale_mode))
     _check(load().kv_insert(ctypes.byref(a), _stream(stream)))
+
+
+def prepare_kv_insert_mxfp4(kv_fused, k, slot_mapping, *, sf_interleaved=False, stream=None):
+    """kv_insert_mxfp4 with its argument struct built once (see prepare_paged_attn_fwd)."""
+    import torch
+    dt = {torch.float16: DT_F16, torch.bfloat16: DT_BF16}.get(k.dtype)
+    if dt is None:
+        raise PaError(2, f"kv_insert_mxfp4: k must be float16 or bfloat16, got {k.dtype}")
+    a = Mxfp4InsertArgs(kv_fused=_ptr(kv_fused), k=_ptr(k), in_dtype=dt,
+                        slot_mapping=_ptr(slot_mapping), num_tokens=k.shape[0],
+                        num_slots=slot_mapping.shape[0], head_dim=k.shape[1],
+                        block_size=kv_fused.shape[1], num_blocks=kv_fused.shape[0],
+                        sf_vec_size=32, sf_interleaved=int(bool(sf_interleaved)))
+    return Prepared(load().kv_insert_mxfp4, a, (kv_fused, k, slot_mapping), _stream(stream))
+
+
+def kv_insert_mxfp4(kv_fused, k, slot_mapping, *, sf_interleaved=False, stream=None):
+    """Quantize rows k [T, 128] (fp16 or bf16) to MXFP4 into kv_fused
+    [num_blocks, block_size, 1, 68] uint8 at slot_mapping (int64), the layout
+    paged_mqa_logits reads (include/pa.h)."""
+    prepare_kv_insert_mxfp4(kv_fused, k, slot_mapping, sf_interleaved=sf_interleaved,
+                            stream=stream)()
 
 
 def pa_set_profile_events(start_event, stop_event):
