@@ -80,6 +80,11 @@ def _bind(lib):
     lib.orc_paged_attn.argtypes = [P, P, P, P, i32, P, i32, P, i32, P, P,
                                    i32, i32, i32, i32, i32, i32, i64, i32, f32, i32]
     lib.orc_paged_attn.restype = i32
+    lib.orc_paged_attn_sparse.argtypes = [P, P, P, P, i32, P, i32, P, i32, P, P, P, i32,
+                                          i32, i32, i32, i32, i32, i32, i64, i32, f32]
+    lib.orc_paged_attn_sparse.restype = i32
+    lib.orc_sparse_plan.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32]
+    lib.orc_sparse_plan.restype = i32
     lib.orc_mqa_logits.argtypes = [P, i64, P, P, P, P, P, P,
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.orc_f32_to_bf16_array.argtypes = [P, P, i64]
@@ -174,6 +179,59 @@ def paged_attn(q, k_cache, v_cache, kv_kind, block_table, context_lens, *,
     if rc != 0:
         raise ValueError(f"orc_paged_attn failed with code {rc}")
     return out
+
+
+def paged_attn_sparse(q, k_cache, v_cache, kv_kind, block_table, context_lens, sel, *,
+                      k_scale=None, k_scale_mode=SCALE_NONE, v_scale=None,
+                      v_scale_mode=SCALE_NONE, num_kv_heads, head_dim, block_size,
+                      softmax_scale, causal=None, lib=None):
+    """Reference selection-driven sparse paged attention (see orc_paged_attn_sparse).
+
+    sel: int32 [B, next_n, topk] logical token ids (entries outside [0, L_b)
+    select nothing). Returns float64 [B, next_n, Hq, D]. `causal` is accepted
+    for keyword compatibility with paged_attn and ignored.
+    """
+    lib = lib or load()
+    q16 = _bits16(q)
+    B, next_n, Hq, D = q16.shape
+    assert D == head_dim
+    sl = _c(sel, np.int32)
+    assert sl.shape[:2] == (B, next_n)
+    kc = np.ascontiguousarray(k_cache).view(np.uint8)
+    vc = np.ascontiguousarray(v_cache).view(np.uint8)
+    bt = _c(block_table, np.int32)
+    cl = _c(context_lens, np.int32)
+    ks = _c(k_scale if k_scale is not None else np.ones(1, np.float32), np.float32)
+    vs = _c(v_scale if v_scale is not None else np.ones(1, np.float32), np.float32)
+    out = np.empty((B, next_n, Hq, D), np.float64)
+    rc = lib.orc_paged_attn_sparse(_ptr(out), _ptr(q16), _ptr(kc), _ptr(vc), kv_kind,
+                                   _ptr(ks), k_scale_mode, _ptr(vs), v_scale_mode, _ptr(bt),
+                                   _ptr(cl), _ptr(sl), sl.shape[2], B, next_n, Hq, num_kv_heads,
+                                   D, block_size, k_cache.shape[0], bt.shape[1],
+                                   float(softmax_scale))
+    if rc != 0:
+        raise ValueError(f"orc_paged_attn_sparse failed with code {rc}")
+    return out
+
+
+def sparse_plan(sel, block_table, context_lens, block_size, cap=None, lib=None):
+    """Reference grouped union plan (see orc_sparse_plan): returns (entries int32
+    [B, cap, 2] of {physical, logical block}, masks uint32 [B, cap, next_n],
+    count int32 [B]); entries past count[b] are left 0."""
+    lib = lib or load()
+    sl = _c(sel, np.int32)
+    B, next_n, topk = sl.shape
+    bt = _c(block_table, np.int32)
+    cl = _c(context_lens, np.int32)
+    cap = cap or bt.shape[1]
+    entries = np.zeros((B, cap, 2), np.int32)
+    masks = np.zeros((B, cap, next_n), np.uint32)
+    count = np.zeros(B, np.int32)
+    rc = lib.orc_sparse_plan(_ptr(entries), _ptr(masks), _ptr(count), _ptr(sl), topk, _ptr(bt),
+                             _ptr(cl), B, next_n, block_size, bt.shape[1], cap)
+    if rc != 0:
+        raise ValueError(f"orc_sparse_plan failed with code {rc}")
+    return entries, masks, count
 
 
 def mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len, *,

@@ -354,6 +354,139 @@ done:
 }
 
 /* ------------------------------------------------------------------ */
+/* Selection-driven sparse paged attention [P3] [P1]                   */
+/* ------------------------------------------------------------------ */
+
+/* mark[t] = 1 for every entry t of the topk entries of sel_row with
+ * 0 <= t < L, else 0 (entries outside [0, L), -1 padding included, select
+ * nothing; a repeated entry selects its token once). */
+static void mark_selection(unsigned char* mark, const int32_t* sel_row, int topk, int L) {
+  memset(mark, 0, (size_t)(L > 0 ? L : 1));
+  for (int j = 0; j < topk; ++j)
+    if (sel_row[j] >= 0 && sel_row[j] < L) mark[sel_row[j]] = 1;
+}
+
+/*
+ * out[b, i, h, :] = softmax over the selected tokens S_{b,i} of
+ * softmax_scale * q[b,i,h,:] . K_t, times V_t, summed over S_{b,i} in
+ * ascending token order; dequantize first as in orc_paged_attn. S_{b,i} is the
+ * set of sel[b, i, :] entries in [0, L_b) [P3, Investigation: the selected
+ * token ids of a query row]. All heads of a row share its selection. An empty
+ * selection gives +0. No causal limit is applied: the selection alone decides
+ * what a row sees. Tokens outside every selection are never read, so tail
+ * slots and the null block cannot reach the output [P1, Fix].
+ */
+int orc_paged_attn_sparse(double* out, const uint16_t* q, const uint8_t* k_cache,
+                          const uint8_t* v_cache, int kv_kind, const float* k_scale,
+                          int k_scale_mode, const float* v_scale, int v_scale_mode,
+                          const int32_t* block_table, const int32_t* context_lens,
+                          const int32_t* sel, int topk, int B, int next_n, int Hq, int Hkv, int D,
+                          int bs, int64_t num_blocks, int max_blocks, float softmax_scale) {
+  int group = Hq / Hkv;
+  int max_len = max_blocks * bs;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+  unsigned char* mark = (unsigned char*)malloc((size_t)(max_len > 0 ? max_len : 1));
+  int rc = 0;
+  for (int b = 0; b < B; ++b) {
+    int L = context_lens[b];
+    if (L > max_len) { rc = -2; goto done; }
+    for (int i = 0; i < next_n; ++i) {
+      mark_selection(mark, sel + ((int64_t)b * next_n + i) * topk, topk, L);
+      for (int h = 0; h < Hq; ++h) {
+        int hk = h / group;
+        const uint16_t* qrow = q + (((int64_t)b * next_n + i) * Hq + h) * D;
+        double* orow = out + (((int64_t)b * next_n + i) * Hq + h) * D;
+        for (int d = 0; d < D; ++d) orow[d] = 0.0;
+        double m = -INFINITY;
+        int n = 0;
+        for (int t = 0; t < L; ++t) {
+          if (!mark[t]) continue;
+          int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
+          if (blk <= 0 || blk >= num_blocks) { rc = -1; goto done; }
+          double acc = 0.0;
+          for (int d = 0; d < D; ++d) {
+            float kv = deq(k_cache, kv_kind, k_scale, k_scale_mode, blk, t % bs, hk, d, bs, Hkv, D);
+            acc += (double)orc_f16_to_f32(qrow[d]) * (double)kv;
+          }
+          s[t] = (double)softmax_scale * acc;
+          if (s[t] > m) m = s[t];
+          ++n;
+        }
+        if (n == 0) continue;
+        double l = 0.0;
+        for (int t = 0; t < L; ++t) {
+          if (!mark[t]) continue;
+          s[t] = exp(s[t] - m);
+          l += s[t];
+        }
+        for (int t = 0; t < L; ++t) {
+          if (!mark[t]) continue;
+          int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
+          for (int d = 0; d < D; ++d) {
+            float vv = deq(v_cache, kv_kind, v_scale, v_scale_mode, blk, t % bs, hk, d, bs, Hkv, D);
+            orow[d] += s[t] * (double)vv;
+          }
+        }
+        for (int d = 0; d < D; ++d) orow[d] /= l;
+      }
+    }
+  }
+done:
+  free(s);
+  free(mark);
+  return rc;
+}
+
+/*
+ * Grouped union plan of a selection [P3, Summary: the grouped planner keeps
+ * its physical-page union and token masks, sorted with the logical page as the
+ * key and the physical address as payload]: for sequence b, the logical pages
+ * holding at least one selected token of any row, in ascending logical order;
+ * entry e is {physical block, logical block} and mask[b, e, i] has bit j set
+ * when row i selected token (logical block) * bs + j. count[b] is the number
+ * of entries; entries are written up to cap per sequence (returns -3 when a
+ * sequence needs more). Reading: one group per sequence (all its rows), so
+ * the row-category and first-query keys of the pages' sort are constant and
+ * the order is the logical page order.
+ */
+int orc_sparse_plan(int32_t* entries, uint32_t* masks, int32_t* count, const int32_t* sel,
+                    int topk, const int32_t* block_table, const int32_t* context_lens, int B,
+                    int next_n, int bs, int max_blocks, int cap) {
+  if (next_n > 64 || bs > 32) return -1;
+  int rc = 0;
+  unsigned char* mark = (unsigned char*)malloc((size_t)(max_blocks * bs > 0 ? max_blocks * bs : 1) * 64);
+  for (int b = 0; b < B; ++b) {
+    int L = context_lens[b];
+    if (L > max_blocks * bs) { rc = -2; break; }
+    for (int i = 0; i < next_n; ++i)
+      mark_selection(mark + (size_t)i * max_blocks * bs, sel + ((int64_t)b * next_n + i) * topk,
+                     topk, L);
+    int n = 0;
+    for (int lp = 0; lp < max_blocks && lp * bs < L; ++lp) {
+      uint32_t rowmask[64] = {0};
+      int any = 0;
+      for (int i = 0; i < next_n; ++i)
+        for (int j = 0; j < bs && lp * bs + j < L; ++j)
+          if (mark[(size_t)i * max_blocks * bs + lp * bs + j]) {
+            rowmask[i] |= 1u << j;
+            any = 1;
+          }
+      if (!any) continue;
+      if (n >= cap) { rc = -3; break; }
+      int64_t e = (int64_t)b * cap + n;
+      entries[2 * e + 0] = block_table[(int64_t)b * max_blocks + lp];
+      entries[2 * e + 1] = lp;
+      for (int i = 0; i < next_n; ++i) masks[e * next_n + i] = rowmask[i];
+      ++n;
+    }
+    if (rc) break;
+    count[b] = n;
+  }
+  free(mark);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ */
 /* MXFP4 paged MQA logits [P5]                                         */
 /* ------------------------------------------------------------------ */
 

@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from tests import test_oracle_attn, test_oracle_insert, test_oracle_logits, test_oracle_mxfp4
+from tests import (test_oracle_attn, test_oracle_insert, test_oracle_logits, test_oracle_mxfp4,
+                   test_oracle_sparse)
 
 
 def pin_codec_e4m3(lib):
@@ -38,15 +39,16 @@ def pin_codec_round(lib):
 
 
 PINS = ([pin_codec_e4m3, pin_codec_round] + test_oracle_attn.ALL_PINS +
-        test_oracle_logits.ALL_PINS + test_oracle_insert.ALL_PINS + test_oracle_mxfp4.ALL_PINS)
+        test_oracle_logits.ALL_PINS + test_oracle_insert.ALL_PINS + test_oracle_mxfp4.ALL_PINS +
+        test_oracle_sparse.ALL_PINS)
 
 MUTATIONS = {
-    "gqa_head_map": ("int hk = h / group;", "int hk = h % Hkv;"),
+    "gqa_head_map": ("int hk = h / group;", "int hk = h % Hkv;", 0),
     "causal_off_by_one": ("if (causal && pos + 1 < nvis) nvis = pos + 1;",
                           "if (causal && pos < nvis) nvis = pos;"),
-    "softmax_sign": ("s[t] = exp(s[t] - m);", "s[t] = exp(m - s[t]);"),
-    "dropped_normalizer": ("for (int d = 0; d < D; ++d) orow[d] /= l;", ""),
-    "dropped_softmax_scale": ("s[t] = (double)softmax_scale * acc;", "s[t] = acc;"),
+    "softmax_sign": ("s[t] = exp(s[t] - m);", "s[t] = exp(m - s[t]);", 0),
+    "dropped_normalizer": ("for (int d = 0; d < D; ++d) orow[d] /= l;", "", 0),
+    "dropped_softmax_scale": ("s[t] = (double)softmax_scale * acc;", "s[t] = acc;", 0),
     # reads the [Hkv, D] scale as [D, Hkv]; every per-channel pin uses Hkv = 2, so it stays
     # in bounds
     "per_channel_transposed": ("if (mode == ORC_SCALE_PER_CHANNEL) return scale[hk * D + d];",
@@ -80,6 +82,11 @@ MUTATIONS = {
                       "    if (d < bestd || (d == bestd && (c & 1) == 1)) {"),
     "mx_nibble_order": ("data[d / 2] = (uint8_t)((data[d / 2] & 0xF0) | c);",
                         "data[d / 2] = (uint8_t)((data[d / 2] & 0x0F) | (c << 4));"),
+    "sparse_range_unchecked": ("if (sel_row[j] >= 0 && sel_row[j] < L) mark[sel_row[j]] = 1;",
+                               "if (sel_row[j] >= 0 && sel_row[j] < L - 1) mark[sel_row[j]] = 1;"),
+    "sparse_plan_mask_bit": ("rowmask[i] |= 1u << j;", "rowmask[i] |= 1u << (j ^ 1);"),
+    "sparse_score_scale": ("          s[t] = (double)softmax_scale * acc;\n          if (s[t] > m) m = s[t];\n          ++n;",
+                           "          s[t] = acc;\n          if (s[t] > m) m = s[t];\n          ++n;"),
     "mx_sf_token_order": ("(int64_t)sf_slot_of_token(pos, bs, spi, sf_interleaved) * spi;",
                           "(int64_t)pos * spi;"),
 }
@@ -93,10 +100,17 @@ def test_unmutated_passes_all_pins(orc):
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(tmp_path, name):
     src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
-    old, new = MUTATIONS[name]
-    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    old, new, *which = MUTATIONS[name]
+    if which:  # the anchor recurs (dense and sparse attention): mutate occurrence which[0]
+        at = -1
+        for _ in range(which[0] + 1):
+            at = src.index(old, at + 1)
+        mutated = src[:at] + new + src[at + len(old):]
+    else:
+        assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+        mutated = src.replace(old, new)
     path = tmp_path / "oracle_mut.c"
-    path.write_text(src.replace(old, new))
+    path.write_text(mutated)
     so = str(tmp_path / "liboracle_mut.so")
     subprocess.run(["gcc", *oracle.CFLAGS, str(path), "-o", so, "-lm"], check=True)
     lib = oracle.load(so)

@@ -518,3 +518,30 @@ def mxfp4_insert_case(seed, *, T, D=128, bs=64, in_dtype="f16", slotless_tail=0,
     kv = np.full((nb, bs, 1, D // 2 + D // 32), 0xFF, np.uint8)
     return Mxfp4InsertCase(k_bits=bits, in_dtype=in_dtype, slot_mapping=slots, kv_fused=kv,
                            sf_interleaved=sf_interleaved)
+
+
+def with_selection(case: AttnCase, seed: int, topk: int, window: int = 128,
+                   junk: int = 4) -> tuple:
+    """A selection for every query row of `case`, as a top-k over indexer
+    logits would give it: the last `window` tokens of the sequence plus random
+    earlier ones, at most topk distinct ids per row in random order, padded
+    with -1. `junk` extra entries per row repeat an id or fall outside [0, L)
+    (they must select nothing more). Returns (case, sel int32 [B, next_n, topk + junk])."""
+    rng = np.random.default_rng(seed)
+    B, N = case.batch, case.next_n
+    sel = np.full((B, N, topk + junk), -1, np.int32)
+    for b in range(B):
+        L = int(case.context_lens[b])
+        for i in range(N):
+            if L == 0:
+                continue
+            recent = np.arange(max(0, L - window), L)
+            k = min(topk, L)
+            rest = np.setdiff1d(np.arange(L), recent)
+            extra = rng.choice(rest, min(max(0, k - recent.size), rest.size), replace=False)
+            ids = np.concatenate([recent[-k:], extra])[:k]
+            rng.shuffle(ids)
+            sel[b, i, :ids.size] = ids
+            j = [ids[0] if ids.size else -1, L, L + 17, -5][:junk]
+            sel[b, i, topk:topk + len(j)] = j
+    return case, sel
