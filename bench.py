@@ -27,8 +27,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0
 
-WORKLOADS = ("fp8_decode", "int8_perchan", "int4_perchan", "fp8_verify", "mxfp4_logits",
-             "mxfp4_insert")
+WORKLOADS = ("fp8_decode", "int8_perchan", "int4_perchan", "fp8_verify", "fp8_sparse_verify",
+             "mxfp4_logits", "mxfp4_insert")
 
 
 class Hip:
@@ -66,6 +66,8 @@ def make_case(name):
         return W.int_perchan(W.KV_INT4)
     if name == "fp8_verify":
         return W.fp8_verify()
+    if name == "fp8_sparse_verify":
+        return W.fp8_sparse_verify()
     if name == "mxfp4_logits":
         return W.mxfp4_logits()
     if name == "mxfp4_insert":
@@ -206,6 +208,67 @@ def bench_attn(args, torch, pa, hip, case):
                             "kv_tokens": int(case.context_lens.astype("int64").sum())})
 
 
+def sparse_bytes(case, sel):
+    """Algorithmic bytes of one sparse call: K+V codes of every page in the union
+    of the rows' selections (whole pages are read), the selection, and the plan
+    entries and masks the attention kernel reads (q and out apart)."""
+    import numpy as np
+
+    import workloads as W
+
+    bs = case.block_size
+    pages = 0
+    for b in range(case.batch):
+        L = int(case.context_lens[b])
+        t = sel[b].ravel()
+        pages += np.unique(t[(t >= 0) & (t < L)] // bs).size
+    per_page = bs * case.num_kv_heads * W.row_bytes(case.kv_kind, case.head_dim) * 2
+    scales = sum(0 if s is None else s.nbytes for s in (case.k_scale, case.v_scale))
+    plan = pages * (8 + 4 * case.next_n)
+    return pages * per_page + plan + scales, case.q.nbytes * 2 + sel.nbytes, pages
+
+
+def bench_sparse(args, torch, pa, hip, case_sel):
+    import numpy as np
+
+    case, sel = case_sel
+    alg_bytes, other, pages = sparse_bytes(case, sel)
+    pool_bytes = case.k_cache.nbytes + case.v_cache.nbytes
+    npools = max(1, math.ceil((1 << 30) / pool_bytes)) if not args.no_rotate else 1
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kc = dev(case.k_cache)
+    vc = dev(case.v_cache)
+    pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(npools - 1)]
+    q, bt, cl, sl = dev(case.q), dev(case.block_table), dev(case.context_lens), dev(sel)
+    ks = None if case.k_scale is None else dev(case.k_scale)
+    vs = None if case.v_scale is None else dev(case.v_scale)
+    out = torch.empty(case.q.shape, dtype=torch.float16, device="cuda")
+    ws_n = pa.paged_attn_sparse_workspace_size(q, kc, bt, case.max_context_len, case.kv_kind,
+                                               sel.shape[2], case.k_scale_mode,
+                                               case.v_scale_mode)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = [pa.prepare_paged_attn_sparse(out, q, kk, vv, bt, cl, case.max_context_len, sl,
+                                          kv_kind=case.kv_kind, k_scale=ks, v_scale=vs,
+                                          k_scale_mode=case.k_scale_mode,
+                                          v_scale_mode=case.v_scale_mode,
+                                          softmax_scale=case.softmax_scale, workspace=ws,
+                                          stream=stream) for kk, vv in pools]
+
+    def step(k):
+        calls[k % npools]()
+
+    selected = 0
+    for b in range(case.batch):
+        L = int(case.context_lens[b])
+        for i in range(case.next_n):
+            t = sel[b, i]
+            selected += np.unique(t[(t >= 0) & (t < L)]).size
+    return run_timed(args, torch, pa, hip, step, alg_bytes, other,
+                     extra={"npools": npools, "query_tokens": case.batch * case.next_n,
+                            "kv_tokens": int(selected), "union_pages": int(pages)})
+
+
 def bench_logits(args, torch, pa, hip, case):
     import numpy as np
 
@@ -334,6 +397,17 @@ def main():
                   "block_size": case.block_size, "max_context_len": case.max_context_len,
                   "context_lens": "uniform [1, 32768], seed 1004", "kv_dtype": "mxfp4"}
         dtype = "fp4xfp4->f32"
+    elif args.workload == "fp8_sparse_verify":
+        r = bench_sparse(args, torch, pa, hip, case)
+        c, sel = case
+        tag = "attn_ring_" + args.workload
+        config = {"workload": args.workload, "batch": c.batch, "next_n": c.next_n,
+                  "q_heads": c.num_q_heads, "kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+                  "block_size": c.block_size, "max_context_len": c.max_context_len,
+                  "kv_dtype": "e4m3", "scales": "per_tensor", "topk": 2048,
+                  "selection": "last 512 tokens + uniform earlier ones per row, seed 1006",
+                  "union_pages": r["union_pages"]}
+        dtype = "f16xf16->f32"
     else:
         r = bench_attn(args, torch, pa, hip, case)
         tag = "attn_ring_" + args.workload
@@ -367,7 +441,8 @@ def main():
                      "traffic": traffic, "kernel": tag,
                      "alg_bytes_per_launch": r["alg_bytes"]},
     }
-    if not args.no_cpu_baseline and args.workload not in ("mxfp4_logits", "mxfp4_insert"):
+    if not args.no_cpu_baseline and args.workload not in ("mxfp4_logits", "mxfp4_insert",
+                                                          "fp8_sparse_verify"):
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)

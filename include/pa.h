@@ -156,6 +156,50 @@ pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace, size_t workspac
 pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t max_entries, int32_t* info,
                   void* stream);
 
+/*
+ * paged_attn_sparse -- selection-driven sparse paged attention, the QSA route
+ * of [RELOC] (Summary and Fix: a physical-page union with per-row token masks,
+ * walked in logical page order) with the unattended-row rule of [NULLPAD]
+ * (Fix: rows that select nothing are written as zeros).
+ *
+ * sel: DEVICE int32 [batch, next_n, topk] logical token ids per query row
+ *   (row i of sequence b attends to the distinct ids t of sel[b, i, :] with
+ *   0 <= t < context_lens[b]; other ids, and repeats, add nothing). May be
+ *   NULL when topk == 0.
+ * The attention itself is the one of paged_attn_fwd restricted to each row's
+ * selected set: scores are scale * q.k over the selected tokens only (no
+ * causal rule: `causal` is ignored), softmax over them, and the values are
+ * summed in ascending token order, so the output is bit-identical under any
+ * physical relocation of pages. A row with an empty set outputs +0 and reads
+ * no KV byte; KV bytes of unselected tokens are never part of a result (NaN
+ * there cannot leak).
+ * Supported: KV kinds F16 and E4M3 with per-tensor or no scales, next_n <= 4,
+ * next_n * (num_q_heads / num_kv_heads) <= 32, max_blocks_per_seq <= 16384,
+ * plus the shapes paged_attn_fwd supports.
+ * Workspace: paged_attn_sparse_workspace_size(a, topk) bytes (0 when the
+ * arguments are rejected); it holds the per-call union plan and split
+ * partials, and its prior contents do not matter. Three kernels are enqueued
+ * on `stream`: planner, attention, merge.
+ */
+size_t paged_attn_sparse_workspace_size(const pa_attn_args* a, int32_t topk);
+pa_status paged_attn_sparse(const pa_attn_args* a, const int32_t* sel, int32_t topk,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test probe of the sparse union planner: for each sequence b writes
+ * count[b] = number of distinct logical pages that hold a selected token,
+ * entries[(b * cap + e) * 2 + {0, 1}] = {block_table[b, page], page} for
+ * e < count[b] in ascending page order, and
+ * masks[(b * cap + e) * next_n + i] = bit (t % block_size) set for every
+ * token t of page e that row i selected (all cap * next_n mask words of each
+ * sequence are written; entries past count[b] are not). Pages beyond cap are
+ * dropped from entries and masks but counted only up to cap. Buffers are
+ * DEVICE memory; cap >= 1.
+ */
+pa_status pa_sparse_plan(const pa_attn_args* a, const int32_t* sel, int32_t topk,
+                         int32_t* entries, uint32_t* masks, int32_t* count, int32_t cap,
+                         void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* paged_mqa_logits [FP4API]                                                 */
 /* ------------------------------------------------------------------------ */

@@ -74,7 +74,8 @@ class PaError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
+EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_attn_sparse",
+           "paged_attn_sparse_workspace_size", "pa_sparse_plan", "paged_mqa_logits",
            "paged_mqa_logits_workspace_size", "kv_insert", "kv_insert_mxfp4", "pa_dequantize",
            "pa_last_error", "pa_set_profile_events"]
 
@@ -94,6 +95,13 @@ def load(path: str | None = None):
     lib.paged_attn_workspace_size.restype = ctypes.c_size_t
     lib.pa_plan.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i64, _vp, _vp]
     lib.pa_plan.restype = _i32
+    lib.paged_attn_sparse.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i32, _vp, ctypes.c_size_t,
+                                      _vp]
+    lib.paged_attn_sparse.restype = _i32
+    lib.paged_attn_sparse_workspace_size.argtypes = [ctypes.POINTER(AttnArgs), _i32]
+    lib.paged_attn_sparse_workspace_size.restype = ctypes.c_size_t
+    lib.pa_sparse_plan.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i32, _vp, _vp, _vp, _i32, _vp]
+    lib.pa_sparse_plan.restype = _i32
     lib.paged_mqa_logits.argtypes = [ctypes.POINTER(LogitsArgs), _vp, ctypes.c_size_t, _vp]
     lib.paged_mqa_logits.restype = _i32
     lib.paged_mqa_logits_workspace_size.argtypes = [ctypes.POINTER(LogitsArgs)]
@@ -232,6 +240,86 @@ def pa_plan(block_table, context_lens, max_context_len, *, q_shape, k_cache_shap
     _check(lib.pa_plan(ctypes.byref(a), _ptr(entries), entries.numel() // 3,
                        ctypes.cast(info, _vp), _stream(stream)))
     return entries, {"split_tokens": split, "nsplit": nsplit, "entries_per_unit": epu}
+
+
+# ---------------------------------------------------------------------------
+# selection-driven sparse paged attention
+# ---------------------------------------------------------------------------
+
+
+def _sel_topk(sel, q):
+    B, next_n = q.shape[0], q.shape[1]
+    if sel.dim() != 3 or tuple(sel.shape[:2]) != (B, next_n):
+        raise PaError(1, f"sel must be int32 [B, next_n, topk], got {tuple(sel.shape)}")
+    if not sel.is_contiguous():
+        raise PaError(1, "sel must be contiguous")
+    return sel.shape[2]
+
+
+def paged_attn_sparse_workspace_size(q, k_cache, block_table, max_context_len, kv_kind, topk,
+                                     k_scale_mode=SCALE_NONE, v_scale_mode=SCALE_NONE):
+    a = _attn_args(None, q, k_cache, k_cache, block_table, None, max_context_len, kv_kind, None,
+                   None, k_scale_mode, v_scale_mode, 0.0, False)
+    return load().paged_attn_sparse_workspace_size(ctypes.byref(a), int(topk))
+
+
+def prepare_paged_attn_sparse(out, q, k_cache, v_cache, block_table, context_lens,
+                              max_context_len, sel, *, kv_kind, k_scale=None, v_scale=None,
+                              k_scale_mode=None, v_scale_mode=None, softmax_scale=0.0,
+                              workspace=None, stream=None):
+    """paged_attn_sparse with its argument struct built once (see
+    prepare_paged_attn_fwd)."""
+    import torch
+    topk = _sel_topk(sel, q)
+    a = _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                   kv_kind, k_scale, v_scale, k_scale_mode, v_scale_mode, softmax_scale, False)
+    lib = load()
+    need = lib.paged_attn_sparse_workspace_size(ctypes.byref(a), topk)
+    if need == 0:
+        # the size query rejects these arguments: the call reports why
+        _check(lib.paged_attn_sparse(ctypes.byref(a), _ptr(sel), topk, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    return Prepared(lib.paged_attn_sparse, a, (out, q, k_cache, v_cache, sel, workspace),
+                    _ptr(sel), topk, _ptr(workspace), workspace.numel(), _stream(stream))
+
+
+def paged_attn_sparse(out, q, k_cache, v_cache, block_table, context_lens, max_context_len, sel,
+                      *, kv_kind, k_scale=None, v_scale=None, k_scale_mode=None,
+                      v_scale_mode=None, softmax_scale=0.0, workspace=None, stream=None):
+    """out[B, next_n, Hq, D] fp16 <- attention of each query row over the tokens
+    it selected (sel int32 [B, next_n, topk] logical token ids; see
+    paged_attn_sparse in include/pa.h). Other arguments as for paged_attn_fwd."""
+    prepare_paged_attn_sparse(out, q, k_cache, v_cache, block_table, context_lens,
+                              max_context_len, sel, kv_kind=kv_kind, k_scale=k_scale,
+                              v_scale=v_scale, k_scale_mode=k_scale_mode,
+                              v_scale_mode=v_scale_mode, softmax_scale=softmax_scale,
+                              workspace=workspace, stream=stream)()
+    return out
+
+
+def pa_sparse_plan(sel, block_table, context_lens, max_context_len, *, q_shape, k_cache_shape,
+                   kv_kind, k_scale_mode=SCALE_NONE, v_scale_mode=SCALE_NONE, cap=None,
+                   stream=None):
+    """Sparse planner probe: returns (entries int32 [B, cap, 2], masks int32
+    [B, cap, next_n] holding the uint32 bits, count int32 [B])."""
+    import torch
+    B, next_n, Hq, D = q_shape
+    nb, bs, Hkv, _ = k_cache_shape
+    cap = int(cap or block_table.shape[1])
+    a = AttnArgs(q_dtype=DT_F16, kv_kind=kv_kind, k_scale_mode=k_scale_mode,
+                 v_scale_mode=v_scale_mode, block_table=_ptr(block_table),
+                 context_lens=_ptr(context_lens), max_context_len=int(max_context_len), batch=B,
+                 next_n=next_n, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                 max_blocks_per_seq=block_table.shape[1], num_blocks=nb, softmax_scale=0.0,
+                 causal=0)
+    dev = block_table.device
+    entries = torch.zeros((B, cap, 2), dtype=torch.int32, device=dev)
+    masks = torch.zeros((B, cap, next_n), dtype=torch.int32, device=dev)
+    count = torch.zeros(B, dtype=torch.int32, device=dev)
+    _check(load().pa_sparse_plan(ctypes.byref(a), _ptr(sel), sel.shape[2], _ptr(entries),
+                                 _ptr(masks), _ptr(count), cap, _stream(stream)))
+    return entries, masks, count
 
 
 # ---------------------------------------------------------------------------

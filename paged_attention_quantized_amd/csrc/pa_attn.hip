@@ -132,6 +132,85 @@ __global__ void plan_dump_kernel(AttnParams p, int entries_per_seq, int pages_ma
   entries[idx * 3 + 2] = (int32_t)x.mask;
 }
 
+// Grouped union planner of a selection [RELOC, Summary: a physical-page union
+// with token masks, ordered with the logical page as the key and the physical
+// block as payload]. One workgroup per sequence b: every valid selected token
+// (0 <= t < L_b) sets the bit of its logical page in an LDS bitmap; a prefix
+// count of the bitmap words ranks the pages in logical order; entry e gets
+// {block_table[b, page], page}; then each (row i, token t) ORs bit t % bs into
+// mask[b, e(t), i]. Writes count[b] (entries) and vlen[b] = count * bs when
+// those pointers are set. Entries and masks are written for e < count only.
+__global__ __launch_bounds__(256) void sparse_plan_kernel(
+    const int32_t* __restrict__ sel, int topk, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ lens, int max_blocks, int bs, int next_n, int cap,
+    int32_t* __restrict__ entries, uint32_t* __restrict__ masks, int32_t* count, int32_t* vlen) {
+  __shared__ uint32_t bm[kPlanWords];
+  __shared__ int wrank[kPlanWords];
+  __shared__ int tsum[256];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  // tokens past the table's pages are never selectable (keeps the bitmap in bounds)
+  const int L = min(lens[b], max_blocks * bs);
+  const int npages = L > 0 ? (L + bs - 1) / bs : 0;
+  const int nw = (npages + 31) >> 5;
+  const int nsel = next_n * topk;
+  const int32_t* srow = sel + (size_t)b * nsel;
+  for (int w = tid; w < kPlanWords; w += 256) bm[w] = 0u;
+  for (int x = tid; x < cap * next_n; x += 256) masks[(size_t)b * cap * next_n + x] = 0u;
+  __syncthreads();
+  for (int x = tid; x < nsel; x += 256) {
+    const int t = srow[x];
+    if (t >= 0 && t < L) {
+      const int lp = t / bs;
+      atomicOr(&bm[lp >> 5], 1u << (lp & 31));
+    }
+  }
+  __syncthreads();
+  // exclusive prefix of the word popcounts: thread tid owns words 2 tid, 2 tid + 1
+  const int c0 = 2 * tid < nw ? __popc(bm[2 * tid]) : 0;
+  const int c1 = 2 * tid + 1 < nw ? __popc(bm[2 * tid + 1]) : 0;
+  tsum[tid] = c0 + c1;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? tsum[tid - off] : 0;
+    __syncthreads();
+    tsum[tid] += v;
+    __syncthreads();
+  }
+  const int excl = tsum[tid] - (c0 + c1);
+  if (2 * tid < kPlanWords) wrank[2 * tid] = excl;
+  if (2 * tid + 1 < kPlanWords) wrank[2 * tid + 1] = excl + c0;
+  const int total = tsum[255];
+  __syncthreads();
+  for (int w = tid; w < nw; w += 256) {
+    uint32_t bits = bm[w];
+    int e = wrank[w];
+    while (bits) {
+      const int lb = __builtin_ctz(bits);
+      bits &= bits - 1u;
+      const int lp = 32 * w + lb;
+      const size_t at = (size_t)b * cap + e;
+      if (e < cap) {
+        entries[2 * at + 0] = table[(size_t)b * max_blocks + lp];
+        entries[2 * at + 1] = lp;
+      }
+      ++e;
+    }
+  }
+  for (int x = tid; x < nsel; x += 256) {
+    const int t = srow[x];
+    if (t >= 0 && t < L) {
+      const int lp = t / bs, w = lp >> 5;
+      const int e = wrank[w] + __popc(bm[w] & ((1u << (lp & 31)) - 1u));
+      if (e < cap) atomicOr(&masks[((size_t)b * cap + e) * next_n + x / topk], 1u << (t % bs));
+    }
+  }
+  if (tid == 0) {
+    const int n = total < cap ? total : cap;
+    if (count) count[b] = n;
+    if (vlen) vlen[b] = n * bs;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -140,6 +219,8 @@ namespace {
 
 struct Shape {
   int R, RT, RB, hpu, hgroups, ts, nw, nsub, nwg;
+  int sparse, sp_cap;                    // selection-driven mode: plan entries per sequence
+  size_t sp_entries_bytes, sp_masks_bytes, sp_vlen_bytes;
   int pages_max, entries_per_seq;
   int wgmerge;
   int64_t parts;
@@ -169,7 +250,7 @@ int device_cus() {
   return cache[dev];
 }
 
-pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs) {
+pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int sparse_topk = -1) {
   if (!a) return fail(PA_ERR_INVALID_ARG, "paged_attn: args is NULL");
   if (a->batch < 0 || a->next_n < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1 ||
       a->max_context_len < 0 || a->max_blocks_per_seq < 1 || a->num_blocks < 1)
@@ -210,11 +291,28 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs) {
   // of row bytes per token) and ts tokens, so that one stage (K and V) is at
   // most 32 KiB and a workgroup has at most 8 waves of 16-token sub-tiles.
   int hpu = gcd_int(a->num_kv_heads, kMaxWaves);
-  while (hpu > 1 && hpu * rb > 1024) hpu /= 2;
-  int ts = kStageMax / 2 / (hpu * rb);
-  if (ts > 64) ts = 64;
-  if (ts > 16 * kMaxWaves / hpu) ts = 16 * kMaxWaves / hpu;
-  if (ts < 16) ts = 16;
+  int ts;
+  if (sparse_topk >= 0) {
+    // selection-driven mode: an item is one page of the union plan
+    if (a->kv_kind != PA_KV_F16 && a->kv_kind != PA_KV_E4M3)
+      return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: KV kind must be F16 or E4M3");
+    if (a->k_scale_mode == PA_SCALE_PER_CHANNEL || a->v_scale_mode == PA_SCALE_PER_CHANNEL)
+      return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: per-channel scales unsupported");
+    if (a->next_n > kSparseRows || R > 32)
+      return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: next_n <= 4 and next_n * G <= 32");
+    if ((int64_t)a->max_blocks_per_seq > 32 * kPlanWords)
+      return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: max_blocks_per_seq > 16384");
+    ts = a->block_size;
+    while (hpu > 1 && (2 * ts * hpu * rb > kStageMax || hpu * (ts / 16) > kMaxWaves)) hpu /= 2;
+    if (2 * ts * hpu * rb > kStageMax)
+      return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: one page exceeds a ring stage");
+  } else {
+    while (hpu > 1 && hpu * rb > 1024) hpu /= 2;
+    ts = kStageMax / 2 / (hpu * rb);
+    if (ts > 64) ts = 64;
+    if (ts > 16 * kMaxWaves / hpu) ts = 16 * kMaxWaves / hpu;
+    if (ts < 16) ts = 16;
+  }
   sh->hpu = hpu;
   sh->hgroups = a->num_kv_heads / hpu;
   sh->ts = ts;
@@ -235,6 +333,17 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs) {
   sh->ml_bytes = (size_t)round_up(sh->parts * R * 16, 256);
   sh->o_bytes = (size_t)round_up(sh->parts * R * a->head_dim * 4, 256);
   sh->seq_bytes = (size_t)round_up(((int64_t)a->batch + 1) * 4, 256);
+  sh->sparse = sparse_topk >= 0 ? 1 : 0;
+  sh->sp_cap = 0;
+  sh->sp_entries_bytes = sh->sp_masks_bytes = sh->sp_vlen_bytes = 0;
+  if (sh->sparse) {
+    const int64_t cap64 = (int64_t)a->next_n * sparse_topk;
+    sh->sp_cap = (int)(cap64 < a->max_blocks_per_seq ? cap64 : a->max_blocks_per_seq);
+    if (sh->sp_cap < 1) sh->sp_cap = 1;
+    sh->sp_entries_bytes = (size_t)round_up((int64_t)a->batch * sh->sp_cap * 8, 256);
+    sh->sp_masks_bytes = (size_t)round_up((int64_t)a->batch * sh->sp_cap * a->next_n * 4, 256);
+    sh->sp_vlen_bytes = (size_t)round_up((int64_t)a->batch * 4, 256);
+  }
   return PA_OK;
 }
 
@@ -276,12 +385,12 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   return p;
 }
 
-RingFn pick_ring(int kind, int D, int nw, int RT, bool hilo) {
+RingFn pick_ring(int kind, int D, int nw, int RT, bool hilo, bool sparse = false) {
   switch (kind) {
-    case PA_KV_F16: return pick_ring_f16(D, nw, RT, hilo);
-    case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, hilo);
-    case PA_KV_INT8: return pick_ring_int8(D, nw, RT, hilo);
-    case PA_KV_INT4: return pick_ring_int4(D, nw, RT, hilo);
+    case PA_KV_F16: return pick_ring_f16(D, nw, RT, hilo, sparse);
+    case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, hilo, sparse);
+    case PA_KV_INT8: return pick_ring_int8(D, nw, RT, hilo, sparse);
+    case PA_KV_INT4: return pick_ring_int4(D, nw, RT, hilo, sparse);
   }
   return nullptr;
 }
@@ -293,7 +402,7 @@ pa_status launch_attn(const pa_attn_args* a, const Shape& sh, void* workspace, h
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
   AttnParams p = make_params(a, sh, workspace);
   launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), s, p, a->block_table,
-               a->context_lens);
+               a->context_lens, (const uint32_t*)nullptr);
   pa_status st = launch_status("paged_attn ring kernel");
   if (st != PA_OK) return st;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(a->batch * a->num_kv_heads),
@@ -351,4 +460,81 @@ extern "C" pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t ma
     hipLaunchKernelGGL(plan_dump_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
                        (hipStream_t)stream, p, sh.entries_per_seq, sh.pages_max, entries);
   return launch_status("pa_plan kernel");
+}
+
+// ---------------------------------------------------------------------------
+// selection-driven sparse attention [RELOC] [NULLPAD]
+// ---------------------------------------------------------------------------
+
+namespace {
+
+size_t sparse_ws_bytes(const Shape& sh) {
+  return sh.ml_bytes + sh.o_bytes + sh.seq_bytes + sh.sp_entries_bytes + sh.sp_masks_bytes +
+         sh.sp_vlen_bytes;
+}
+
+}  // namespace
+
+extern "C" size_t paged_attn_sparse_workspace_size(const pa_attn_args* a, int32_t topk) {
+  Shape sh;
+  if (topk < 0 || check_args(a, &sh, false, topk) != PA_OK) return 0;
+  return sparse_ws_bytes(sh);
+}
+
+extern "C" pa_status paged_attn_sparse(const pa_attn_args* a, const int32_t* sel, int32_t topk,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (topk < 0) return fail(PA_ERR_INVALID_ARG, "paged_attn_sparse: topk < 0");
+  Shape sh;
+  pa_status st = check_args(a, &sh, true, topk);
+  if (st != PA_OK) return st;
+  const size_t need = sparse_ws_bytes(sh);
+  if (workspace_bytes < need || !workspace)
+    return fail(PA_ERR_WORKSPACE, "paged_attn_sparse: workspace needs %zu bytes, got %zu", need,
+                workspace_bytes);
+  if (a->batch == 0) return PA_OK;
+  if (topk > 0 && !sel) return fail(PA_ERR_INVALID_ARG, "paged_attn_sparse: sel is NULL");
+  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, false, true);
+  if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: no kernel for this kind/shape");
+  char* base = (char*)workspace + sh.ml_bytes + sh.o_bytes + sh.seq_bytes;
+  int32_t* entries = (int32_t*)base;
+  uint32_t* masks = (uint32_t*)(base + sh.sp_entries_bytes);
+  int32_t* vlen = (int32_t*)(base + sh.sp_entries_bytes + sh.sp_masks_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3((unsigned)a->batch), dim3(256), 0, s, sel,
+                     topk > 0 ? topk : 0, a->block_table, a->context_lens, a->max_blocks_per_seq,
+                     a->block_size, a->next_n, sh.sp_cap, entries, masks, (int32_t*)nullptr,
+                     vlen);
+  st = launch_status("paged_attn_sparse plan kernel");
+  if (st != PA_OK) return st;
+  AttnParams p = make_params(a, sh, workspace);
+  p.context_lens = vlen;  // the merge kernel counts a sequence's items from it
+  p.causal = 0;           // the selection alone decides what a row sees
+  p.sp_entries = entries;
+  p.sp_masks = masks;
+  p.sp_cap = sh.sp_cap;
+  launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), s, p, (const int32_t*)entries,
+               (const int32_t*)vlen, (const uint32_t*)masks);
+  st = launch_status("paged_attn_sparse ring kernel");
+  if (st != PA_OK) return st;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(a->batch * a->num_kv_heads),
+                     (unsigned)ceil_div((int64_t)sh.R * a->head_dim / 4, 256)), dim3(256), 0, s,
+                     p, a->head_dim);
+  return launch_status("paged_attn_sparse merge kernel");
+}
+
+extern "C" pa_status pa_sparse_plan(const pa_attn_args* a, const int32_t* sel, int32_t topk,
+                                    int32_t* entries, uint32_t* masks, int32_t* count,
+                                    int32_t cap, void* stream) {
+  if (topk < 0 || cap < 1) return fail(PA_ERR_INVALID_ARG, "pa_sparse_plan: topk < 0 or cap < 1");
+  Shape sh;
+  pa_status st = check_args(a, &sh, false, topk);
+  if (st != PA_OK) return st;
+  if (a->batch == 0) return PA_OK;
+  if (!entries || !masks || !count || !a->block_table || !a->context_lens || (topk > 0 && !sel))
+    return fail(PA_ERR_INVALID_ARG, "pa_sparse_plan: null pointer");
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3((unsigned)a->batch), dim3(256), 0,
+                     (hipStream_t)stream, sel, topk, a->block_table, a->context_lens,
+                     a->max_blocks_per_seq, a->block_size, a->next_n, cap, entries, masks, count,
+                     (int32_t*)nullptr);
+  return launch_status("pa_sparse_plan kernel");
 }

@@ -36,6 +36,12 @@ struct AttnParams {
   int wgmerge;                     // sub-tile states merged in the workgroup: one partial per head
   int k_scale_mode, v_scale_mode, causal;
   float softmax_scale;
+  // selection-driven sparse mode: union plan of each sequence (entry k =
+  // {physical block, logical block}, row masks [entries][next_n]); an item is
+  // one plan entry and context_lens holds entries * block_size
+  const int32_t* sp_entries;
+  const uint32_t* sp_masks;
+  int sp_cap;
 };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -162,10 +168,17 @@ struct PageSet {
   uint32_t phys[Geo<KIND, D>::NL];  // block ids are >= 0: zero-extended, no use right after the load
 };
 
-template <int KIND, int D>
+template <int KIND, int D, bool SPARSE = false>
 __device__ __forceinline__ void load_pages(const AttnParams& p, const int32_t* __restrict__ table,
                                            const ItemPos& it, const LoadPlan<KIND, D>& lp,
                                            PageSet<KIND, D>& pg) {
+  if constexpr (SPARSE) {
+    // an item is one plan entry (one page): every load of it reads that page
+    const uint32_t phys = (uint32_t)p.sp_entries[2 * ((size_t)it.b * p.sp_cap + it.k)];
+#pragma unroll
+    for (int l = 0; l < Geo<KIND, D>::NL; ++l) pg.phys[l] = phys;
+    return;
+  }
   const int blk0 = (it.k << p.lts) >> p.lbs;
   const int last_blk = (it.L - 1) >> p.lbs;
   const int32_t* table_row = table + (size_t)it.b * p.max_blocks;
@@ -320,17 +333,15 @@ __device__ __forceinline__ void pair_tokens(uint32_t xa, uint32_t xb, uint32_t& 
 // operand of the PV product. MASK = false when every query row sees all 16
 // tokens (none past the end or past a row's causal limit): no selects then.
 template <bool MASK>
-__device__ __forceinline__ void tile_softmax(const f4 s, int t0, int L, int lim, float c2,
-                                             float& m_run, float& alpha, bool& rescale, h4& pb) {
-  const int g = (threadIdx.x & 63) >> 4;
+__device__ __forceinline__ void tile_softmax(const f4 s, uint32_t okbits, float c2, float& m_run,
+                                             float& alpha, bool& rescale, h4& pb) {
   bool okv[4];
   float mx;
   if constexpr (MASK) {
     mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = t0 + 4 * g + e;
-      okv[e] = t < L && t <= lim;
+      okv[e] = (okbits >> e) & 1u;
       mx = okv[e] ? fmaxf(mx, s[e]) : mx;
     }
   } else {
@@ -357,11 +368,16 @@ __device__ __forceinline__ void tile_softmax(const f4 s, int t0, int L, int lim,
 
 // One 16-token sub-tile (tokens t0 .. t0 + 15) of the wave's head from a ring
 // slot. full: every query row sees all 16 tokens (wave-uniform), so the
-// softmax and the V codes need no masking.
-template <int KIND, int D, int RT, bool HILO>
+// softmax and the V codes need no masking. SPARSE: token 4g + e of the
+// sub-tile is valid for the lane's row when bit tin + 4g + e of rmask[rt] is
+// set (tin = the sub-tile's first token in its page), and its V codes are
+// kept when that bit is set in umask (some row selected it).
+template <int KIND, int D, int RT, bool HILO, bool SPARSE = false>
 __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs<KIND, D>& to,
                                              int t0, int L, bool full, float c2,
-                                             WaveState<KIND, D, RT, HILO>& w) {
+                                             WaveState<KIND, D, RT, HILO>& w,
+                                             const uint32_t* rmask = nullptr, uint32_t umask = 0,
+                                             int tin = 0) {
   using G_ = Geo<KIND, D>;
   constexpr int KS = G_::KS, NJ = G_::NJ, KPC = G_::KPC, EPC = G_::EPC, DV = G_::DV;
   constexpr int VDW = G_::VDW, VB = G_::VB;
@@ -402,11 +418,15 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
     }
   }
   if (!full) {
-    // tokens past the end: zero their V codes by select, so no 0 * NaN can
-    // reach O [NULLPAD, Fix]
+    // tokens past the end (or selected by no row): zero their V codes by
+    // select, so no 0 * NaN can reach O [NULLPAD, Fix]
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool ok = t0 + 4 * g + e < L;
+      bool ok;
+      if constexpr (SPARSE)
+        ok = (umask >> (tin + 4 * g + e)) & 1u;
+      else
+        ok = t0 + 4 * g + e < L;
 #pragma unroll
       for (int k = 0; k < VDW; ++k) vraw[e][k] = ok ? vraw[e][k] : 0u;
     }
@@ -432,11 +452,22 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
   if (full) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
-      tile_softmax<false>(sacc[rt], t0, L, w.lim[rt], c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+      tile_softmax<false>(sacc[rt], 0xFu, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
   } else {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      tile_softmax<true>(sacc[rt], t0, L, w.lim[rt], c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+    for (int rt = 0; rt < RT; ++rt) {
+      uint32_t okbits = 0;
+      if constexpr (SPARSE) {
+        okbits = (rmask[rt] >> (tin + 4 * g)) & 0xFu;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = t0 + 4 * g + e;
+          okbits |= (uint32_t)(t < L && t <= w.lim[rt]) << e;
+        }
+      }
+      tile_softmax<true>(sacc[rt], okbits, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+    }
   }
   if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
@@ -559,9 +590,24 @@ __device__ __forceinline__ void write_partial(const AttnParams& p, size_t u, flo
   }
 }
 
-template <int KIND, int D, int RT, bool HILO, int NWB>
+// Row masks of one plan entry (sparse mode): next_n words, scalar loads.
+constexpr int kSparseRows = 4;  // next_n limit of the sparse mode
+constexpr int kPlanWords = 512; // page bitmap words of the union planner (16384 pages)
+
+__device__ __forceinline__ void load_row_masks(const AttnParams& p,
+                                               const uint32_t* __restrict__ masks,
+                                               const ItemPos& it, uint32_t* m) {
+  const size_t base = ((size_t)it.b * p.sp_cap + it.k) * p.next_n;
+#pragma unroll
+  for (int i = 0; i < kSparseRows; ++i) m[i] = i < p.next_n ? masks[base + i] : 0u;
+}
+
+// SPARSE: table holds the union plan entries ({physical, logical} per page),
+// lens the per-sequence entry count times block_size, masks the row masks.
+template <int KIND, int D, int RT, bool HILO, int NWB, bool SPARSE>
 __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
-    AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens) {
+    AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
+    const uint32_t* __restrict__ masks) {
   using G_ = Geo<KIND, D>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageMax];
   const int lane = threadIdx.x & 63, wv = uni(threadIdx.x >> 6);  // wave-uniform
@@ -695,14 +741,22 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     q.nst = in ? pos[j].nst : pos[0].nst;
     q.hg = in ? pos[j].hg : pos[0].hg;
     q.k = in ? pos[j].k : pos[0].k;
-    load_pages<KIND, D>(p, table, q, lp, pgs[j]);
+    load_pages<KIND, D, SPARSE>(p, table, q, lp, pgs[j]);
   }
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j)
     issue_stage<KIND, D>(p, pos[j], pgs[j], j < nitems, lp, ring + j * stage_bytes);
   ItemPos ld = pos[kStages - 1];
   PageSet<KIND, D> pg;
-  if (kStages - 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
+  if (kStages - 1 < nitems) load_pages<KIND, D, SPARSE>(p, table, ld, lp, pg);
+  // SPARSE: row masks of the item being computed (mc) and of the next (mn),
+  // loaded one iteration ahead; mp is the position of mn
+  uint32_t mc[kSparseRows] = {0u, 0u, 0u, 0u}, mn[kSparseRows] = {0u, 0u, 0u, 0u};
+  ItemPos mp = pos[1];
+  if constexpr (SPARSE) {
+    load_row_masks(p, masks, cp, mc);
+    if (1 < nitems) load_row_masks(p, masks, mp, mn);
+  }
 
   for (int j = 0; j < nitems; ++j) {
     // item j has landed for every wave, and every wave is done with item j - 1
@@ -714,9 +768,25 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     issue_stage<KIND, D>(p, ld, pg, live_n, lp, ring + (jn % kStages) * stage_bytes);
     if (live_n) item_next(p, lens, ld);
     const int t0 = (cp.k << p.lts) + 16 * st;
-    if (t0 < cp.L)
+    if constexpr (SPARSE) {
+      // the lane's query row r = 16 rt + n reads the mask of step i = r / G
+      uint32_t rm[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = 16 * rt + (lane & 15);
+        const int i = r / p.G;
+        uint32_t m = 0u;
+#pragma unroll
+        for (int k = 0; k < kSparseRows; ++k) m = i == k ? mc[k] : m;
+        rm[rt] = r < p.R ? m : 0u;
+      }
+      compute_tile<KIND, D, RT, HILO, true>(ring + (j % kStages) * stage_bytes, to, t0, cp.L,
+                                            false, c2, w, rm, mc[0] | mc[1] | mc[2] | mc[3],
+                                            16 * st);
+    } else if (t0 < cp.L) {
       compute_tile<KIND, D, RT, HILO>(ring + (j % kStages) * stage_bytes, to, t0, cp.L,
                                       t0 + 16 <= cp.L - (p.causal ? p.next_n - 1 : 0), c2, w);
+    }
     // end of a (sequence, head group) run inside this range: write the partial
     const int b = cp.b, hg = cp.hg;
     item_next(p, lens, cp);
@@ -741,47 +811,64 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
         start_run<KIND, D, RT, HILO>(p, cp.b, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
     }
     // pages of the item the next iteration issues
-    if (jn + 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
+    if (jn + 1 < nitems) load_pages<KIND, D, SPARSE>(p, table, ld, lp, pg);
+    if constexpr (SPARSE) {
+#pragma unroll
+      for (int k = 0; k < kSparseRows; ++k) mc[k] = mn[k];
+      if (j + 2 < nitems) {
+        item_next(p, lens, mp);
+        load_row_masks(p, masks, mp, mn);
+      }
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-typedef void (*RingFn)(AttnParams, const int32_t*, const int32_t*);
+typedef void (*RingFn)(AttnParams, const int32_t*, const int32_t*, const uint32_t*);
 
 // NWB: the launch bound in waves (4 or 8); a 4-wave workgroup gets twice the
-// registers per wave.
+// registers per wave. The sparse mode exists for FP16 and per-tensor E4M3
+// caches, up to 32 query rows per KV head.
 template <int KIND, int D, int NWB>
-RingFn pick_rt(int RT, bool hilo) {
+RingFn pick_rt(int RT, bool hilo, bool sparse) {
+  if (sparse) {
+    if constexpr (KIND == PA_KV_F16 || KIND == PA_KV_E4M3) {
+      if (hilo) return nullptr;
+      if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, true>;
+      if (RT == 2) return attn_ring_kernel<KIND, D, 2, false, NWB, true>;
+    }
+    return nullptr;
+  }
   if (hilo) {
     if constexpr (KIND == PA_KV_F16) return nullptr;
     else {
-      if (RT == 1) return attn_ring_kernel<KIND, D, 1, true, NWB>;
-      if (RT == 2) return attn_ring_kernel<KIND, D, 2, true, NWB>;
-      return attn_ring_kernel<KIND, D, 4, true, NWB>;
+      if (RT == 1) return attn_ring_kernel<KIND, D, 1, true, NWB, false>;
+      if (RT == 2) return attn_ring_kernel<KIND, D, 2, true, NWB, false>;
+      return attn_ring_kernel<KIND, D, 4, true, NWB, false>;
     }
   }
-  if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB>;
-  if (RT == 2) return attn_ring_kernel<KIND, D, 2, false, NWB>;
-  return attn_ring_kernel<KIND, D, 4, false, NWB>;
+  if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, false>;
+  if (RT == 2) return attn_ring_kernel<KIND, D, 2, false, NWB, false>;
+  return attn_ring_kernel<KIND, D, 4, false, NWB, false>;
 }
 
 template <int KIND, int D>
-RingFn pick_nw(int nw, int RT, bool hilo) {
-  return nw <= 4 ? pick_rt<KIND, D, 4>(RT, hilo) : pick_rt<KIND, D, 8>(RT, hilo);
+RingFn pick_nw(int nw, int RT, bool hilo, bool sparse) {
+  return nw <= 4 ? pick_rt<KIND, D, 4>(RT, hilo, sparse) : pick_rt<KIND, D, 8>(RT, hilo, sparse);
 }
 
 template <int KIND>
-RingFn pick_d(int D, int nw, int RT, bool hilo) {
+RingFn pick_d(int D, int nw, int RT, bool hilo, bool sparse) {
   if constexpr (KIND != PA_KV_INT4)
-    if (D == 64) return pick_nw<KIND, 64>(nw, RT, hilo);
-  if (D == 128) return pick_nw<KIND, 128>(nw, RT, hilo);
-  return pick_nw<KIND, 256>(nw, RT, hilo);
+    if (D == 64) return pick_nw<KIND, 64>(nw, RT, hilo, sparse);
+  if (D == 128) return pick_nw<KIND, 128>(nw, RT, hilo, sparse);
+  return pick_nw<KIND, 256>(nw, RT, hilo, sparse);
 }
 
 // Ring kernel of one KV kind (each defined in its own translation unit).
-RingFn pick_ring_f16(int D, int nw, int RT, bool hilo);
-RingFn pick_ring_e4m3(int D, int nw, int RT, bool hilo);
-RingFn pick_ring_int8(int D, int nw, int RT, bool hilo);
-RingFn pick_ring_int4(int D, int nw, int RT, bool hilo);
+RingFn pick_ring_f16(int D, int nw, int RT, bool hilo, bool sparse);
+RingFn pick_ring_e4m3(int D, int nw, int RT, bool hilo, bool sparse);
+RingFn pick_ring_int8(int D, int nw, int RT, bool hilo, bool sparse);
+RingFn pick_ring_int4(int D, int nw, int RT, bool hilo, bool sparse);
 
 }  // namespace pa

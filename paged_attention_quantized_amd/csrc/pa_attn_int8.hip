@@ -3,6 +3,6 @@
 
 namespace pa {
 
-RingFn pick_ring_int8(int D, int nw, int RT, bool hilo) { return pick_d<PA_KV_INT8>(D, nw, RT, hilo); }
+RingFn pick_ring_int8(int D, int nw, int RT, bool hilo, bool sparse) { return pick_d<PA_KV_INT8>(D, nw, RT, hilo, sparse); }
 
 }  // namespace pa

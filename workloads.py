@@ -545,3 +545,12 @@ def with_selection(case: AttnCase, seed: int, topk: int, window: int = 128,
             j = [ids[0] if ids.size else -1, L, L + 17, -5][:junk]
             sel[b, i, topk:topk + len(j)] = j
     return case, sel
+
+
+def fp8_sparse_verify(seed=SEED_BASE + 6, topk=2048, window=512):
+    """The E4M3 verify workload (B 16, next_n 4, 64 q / 8 KV heads, D 128,
+    block 32, lens uniform in [4096, 16384]) with a token selection per query
+    row: the last 512 tokens plus random earlier ones, 2048 distinct ids per
+    row, 4 junk entries. Returns (case, sel)."""
+    case = dataclasses.replace(fp8_verify(), name="fp8_sparse_verify")
+    return with_selection(case, seed, topk, window=window)
