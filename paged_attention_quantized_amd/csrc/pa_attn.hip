@@ -134,78 +134,112 @@ __global__ void plan_dump_kernel(AttnParams p, int entries_per_seq, int pages_ma
 
 // Grouped union planner of a selection [RELOC, Summary: a physical-page union
 // with token masks, ordered with the logical page as the key and the physical
-// block as payload]. One workgroup per sequence b: every valid selected token
-// (0 <= t < L_b) sets the bit of its logical page in an LDS bitmap; a prefix
-// count of the bitmap words ranks the pages in logical order; entry e gets
-// {block_table[b, page], page}; then each (row i, token t) ORs bit t % bs into
-// mask[b, e(t), i]. Writes count[b] (entries) and vlen[b] = count * bs when
-// those pointers are set. Entries and masks are written for e < count only.
-__global__ __launch_bounds__(256) void sparse_plan_kernel(
+// block as payload]. One 1024-thread workgroup per sequence b: every valid
+// selected token (0 <= t < L_b) sets the bit of its logical page in an LDS
+// bitmap; a wave scan of the word popcounts ranks the pages in logical order;
+// entry e gets {block_table[b, page], page}; the row masks are ORed together
+// in LDS (bit t % bs of word (e(t), row)) and written out coalesced, in chunks
+// of entries when cap * next_n exceeds the LDS buffer. Every selection pass
+// issues all of a thread's loads before it uses any. Writes count[b]
+// (entries) and vlen[b] = count * bs when those pointers are set; entries for
+// e < count, masks for all e < cap.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanUnroll = 8;         // selection entries per thread per pass
+constexpr int kPlanMaskWords = 8192;   // LDS mask words per chunk of entries
+
+__device__ __forceinline__ void plan_load_sel(const int32_t* __restrict__ srow, int nsel, int base,
+                                              int32_t (&tv)[kPlanUnroll]) {
+#pragma unroll
+  for (int u = 0; u < kPlanUnroll; ++u) {
+    const int x = base + u * kPlanThreads + (int)threadIdx.x;
+    tv[u] = x < nsel ? srow[x] : -1;
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void sparse_plan_kernel(
     const int32_t* __restrict__ sel, int topk, const int32_t* __restrict__ table,
-    const int32_t* __restrict__ lens, int max_blocks, int bs, int next_n, int cap,
+    const int32_t* __restrict__ lens, int max_blocks, int lbs, int next_n, int cap,
     int32_t* __restrict__ entries, uint32_t* __restrict__ masks, int32_t* count, int32_t* vlen) {
   __shared__ uint32_t bm[kPlanWords];
   __shared__ int wrank[kPlanWords];
-  __shared__ int tsum[256];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ int wsum[kPlanThreads / 64];
+  __shared__ uint32_t mbuf[kPlanMaskWords];
+  static_assert(kPlanWords <= kPlanThreads, "one bitmap word per thread in the rank scan");
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int bs = 1 << lbs;
   // tokens past the table's pages are never selectable (keeps the bitmap in bounds)
-  const int L = min(lens[b], max_blocks * bs);
-  const int npages = L > 0 ? (L + bs - 1) / bs : 0;
+  const int L = min(lens[b], max_blocks << lbs);
+  const int npages = L > 0 ? (L + bs - 1) >> lbs : 0;
   const int nw = (npages + 31) >> 5;
   const int nsel = next_n * topk;
   const int32_t* srow = sel + (size_t)b * nsel;
-  for (int w = tid; w < kPlanWords; w += 256) bm[w] = 0u;
-  for (int x = tid; x < cap * next_n; x += 256) masks[(size_t)b * cap * next_n + x] = 0u;
+  if (tid < kPlanWords) bm[tid] = 0u;
   __syncthreads();
-  for (int x = tid; x < nsel; x += 256) {
-    const int t = srow[x];
-    if (t >= 0 && t < L) {
-      const int lp = t / bs;
-      atomicOr(&bm[lp >> 5], 1u << (lp & 31));
-    }
+  for (int base = 0; base < nsel; base += kPlanUnroll * kPlanThreads) {
+    int32_t tv[kPlanUnroll];
+    plan_load_sel(srow, nsel, base, tv);
+#pragma unroll
+    for (int u = 0; u < kPlanUnroll; ++u)
+      if (tv[u] >= 0 && tv[u] < L) {
+        const int lp = tv[u] >> lbs;
+        atomicOr(&bm[lp >> 5], 1u << (lp & 31));
+      }
   }
   __syncthreads();
-  // exclusive prefix of the word popcounts: thread tid owns words 2 tid, 2 tid + 1
-  const int c0 = 2 * tid < nw ? __popc(bm[2 * tid]) : 0;
-  const int c1 = 2 * tid + 1 < nw ? __popc(bm[2 * tid + 1]) : 0;
-  tsum[tid] = c0 + c1;
+  // exclusive rank of bitmap word tid: wave scans, then the wave totals
+  const int c = tid < nw ? __popc(bm[tid]) : 0;
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) wsum[wv] = incl;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = tid >= off ? tsum[tid - off] : 0;
-    __syncthreads();
-    tsum[tid] += v;
-    __syncthreads();
+  int off = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanThreads / 64; ++i) {
+    off += i < wv ? wsum[i] : 0;
+    total += wsum[i];
   }
-  const int excl = tsum[tid] - (c0 + c1);
-  if (2 * tid < kPlanWords) wrank[2 * tid] = excl;
-  if (2 * tid + 1 < kPlanWords) wrank[2 * tid + 1] = excl + c0;
-  const int total = tsum[255];
+  if (tid < kPlanWords) wrank[tid] = off + incl - c;
   __syncthreads();
-  for (int w = tid; w < nw; w += 256) {
-    uint32_t bits = bm[w];
-    int e = wrank[w];
-    while (bits) {
-      const int lb = __builtin_ctz(bits);
-      bits &= bits - 1u;
-      const int lp = 32 * w + lb;
-      const size_t at = (size_t)b * cap + e;
+  // entries: one thread per logical page
+  for (int lp = tid; lp < npages; lp += kPlanThreads) {
+    const uint32_t word = bm[lp >> 5];
+    if ((word >> (lp & 31)) & 1u) {
+      const int e = wrank[lp >> 5] + __popc(word & ((1u << (lp & 31)) - 1u));
       if (e < cap) {
+        const size_t at = (size_t)b * cap + e;
         entries[2 * at + 0] = table[(size_t)b * max_blocks + lp];
         entries[2 * at + 1] = lp;
       }
-      ++e;
     }
   }
-  for (int x = tid; x < nsel; x += 256) {
-    const int t = srow[x];
-    if (t >= 0 && t < L) {
-      const int lp = t / bs, w = lp >> 5;
-      const int e = wrank[w] + __popc(bm[w] & ((1u << (lp & 31)) - 1u));
-      if (e < cap) atomicOr(&masks[((size_t)b * cap + e) * next_n + x / topk], 1u << (t % bs));
+  // row masks, a chunk of entries at a time
+  const int n = total < cap ? total : cap;
+  const int cw = kPlanMaskWords / next_n;
+  for (int e0 = 0; e0 < cap; e0 += cw) {
+    const int ne = min(cw, cap - e0);
+    for (int x = tid; x < ne * next_n; x += kPlanThreads) mbuf[x] = 0u;
+    __syncthreads();
+    if (e0 < n) {
+      for (int base = 0; base < nsel; base += kPlanUnroll * kPlanThreads) {
+        int32_t tv[kPlanUnroll];
+        plan_load_sel(srow, nsel, base, tv);
+#pragma unroll
+        for (int u = 0; u < kPlanUnroll; ++u) {
+          const int t = tv[u];
+          if (t >= 0 && t < L) {
+            const int lp = t >> lbs, w = lp >> 5;
+            const int e = wrank[w] + __popc(bm[w] & ((1u << (lp & 31)) - 1u)) - e0;
+            const int row = (base + u * kPlanThreads + tid) / topk;
+            if (e >= 0 && e < ne) atomicOr(&mbuf[e * next_n + row], 1u << (t & (bs - 1)));
+          }
+        }
+      }
     }
+    __syncthreads();
+    uint32_t* mrow = masks + ((size_t)b * cap + e0) * next_n;
+    for (int x = tid; x < ne * next_n; x += kPlanThreads) mrow[x] = mbuf[x];
+    __syncthreads();
   }
   if (tid == 0) {
-    const int n = total < cap ? total : cap;
     if (count) count[b] = n;
     if (vlen) vlen[b] = n * bs;
   }
@@ -500,10 +534,10 @@ extern "C" pa_status paged_attn_sparse(const pa_attn_args* a, const int32_t* sel
   uint32_t* masks = (uint32_t*)(base + sh.sp_entries_bytes);
   int32_t* vlen = (int32_t*)(base + sh.sp_entries_bytes + sh.sp_masks_bytes);
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(sparse_plan_kernel, dim3((unsigned)a->batch), dim3(256), 0, s, sel,
-                     topk > 0 ? topk : 0, a->block_table, a->context_lens, a->max_blocks_per_seq,
-                     a->block_size, a->next_n, sh.sp_cap, entries, masks, (int32_t*)nullptr,
-                     vlen);
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3((unsigned)a->batch), dim3(kPlanThreads), 0, s, sel,
+                     topk, a->block_table, a->context_lens, a->max_blocks_per_seq,
+                     ilog2(a->block_size), a->next_n, sh.sp_cap, entries, masks,
+                     (int32_t*)nullptr, vlen);
   st = launch_status("paged_attn_sparse plan kernel");
   if (st != PA_OK) return st;
   AttnParams p = make_params(a, sh, workspace);
@@ -532,9 +566,9 @@ extern "C" pa_status pa_sparse_plan(const pa_attn_args* a, const int32_t* sel, i
   if (a->batch == 0) return PA_OK;
   if (!entries || !masks || !count || !a->block_table || !a->context_lens || (topk > 0 && !sel))
     return fail(PA_ERR_INVALID_ARG, "pa_sparse_plan: null pointer");
-  hipLaunchKernelGGL(sparse_plan_kernel, dim3((unsigned)a->batch), dim3(256), 0,
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3((unsigned)a->batch), dim3(kPlanThreads), 0,
                      (hipStream_t)stream, sel, topk, a->block_table, a->context_lens,
-                     a->max_blocks_per_seq, a->block_size, a->next_n, cap, entries, masks, count,
-                     (int32_t*)nullptr);
+                     a->max_blocks_per_seq, ilog2(a->block_size), a->next_n, cap, entries, masks,
+                     count, (int32_t*)nullptr);
   return launch_status("pa_sparse_plan kernel");
 }
