@@ -25,10 +25,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 FP4_PEAK_TFLOPS = 10100.0
 
 WORKLOADS = ("fp8_decode", "int8_perchan", "int4_perchan", "fp8_verify", "fp8_sparse_verify",
-             "mxfp4_logits", "mxfp4_insert")
+             "fp8_prefill", "mxfp4_logits", "mxfp4_insert")
 
 
 class Hip:
@@ -68,6 +69,8 @@ def make_case(name):
         return W.fp8_verify()
     if name == "fp8_sparse_verify":
         return W.fp8_sparse_verify()
+    if name == "fp8_prefill":
+        return W.fp8_prefill()
     if name == "mxfp4_logits":
         return W.mxfp4_logits()
     if name == "mxfp4_insert":
@@ -86,6 +89,18 @@ def attn_bytes(case):
     scales = sum(0 if s is None else s.nbytes for s in (case.k_scale, case.v_scale))
     qo = case.q.nbytes * 2
     return kv + 4 * pages + scales, qo
+
+
+def attn_flops(case):
+    """Matrix flops of one call: 2 D for q.k and 2 D for p.v per (query row,
+    head, visible token), the visible tokens of row i being those t <= L - next_n + i
+    under the causal rule (all L otherwise)."""
+    import numpy as np
+
+    L = case.context_lens.astype(np.int64)[:, None]
+    i = np.arange(case.next_n, dtype=np.int64)[None, :]
+    vis = np.clip(L - case.next_n + i + 1, 0, L) if case.causal else np.broadcast_to(L, (len(L), case.next_n))
+    return int(vis.sum()) * case.num_q_heads * 4 * case.head_dim
 
 
 def logits_bytes(case):
@@ -419,6 +434,8 @@ def main():
                   "scales": {0: "none", 1: "per_tensor", 2: "per_channel"}[case.k_scale_mode],
                   "causal": bool(case.causal)}
         dtype = "f16xf16->f32"
+        if case.next_n * case.num_q_heads // case.num_kv_heads > 32:
+            config["row_blocks"] = -(-case.next_n * case.num_q_heads // case.num_kv_heads // 32)
     copy_gbps = copy_ceiling_gbps(torch)
     value = r["alg_bytes"] / r["wall_s"] / 1e9
     achieved = r["alg_bytes"] / r["kernel_s"] / 1e9
@@ -441,8 +458,17 @@ def main():
                      "traffic": traffic, "kernel": tag,
                      "alg_bytes_per_launch": r["alg_bytes"]},
     }
+    if args.workload == "fp8_prefill":
+        # many query rows per KV token: the matrix cores bound this kernel
+        flops = attn_flops(case)
+        tf = flops / r["kernel_s"] / 1e12
+        line["roofline"] = {"bound": "mfma", "achieved": round(tf, 1),
+                            "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tf / F16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                            "kernel": tag, "alg_flops_per_launch": flops,
+                            "kv_GBps_per_launch": round(achieved, 1)}
     if not args.no_cpu_baseline and args.workload not in ("mxfp4_logits", "mxfp4_insert",
-                                                          "fp8_sparse_verify"):
+                                                          "fp8_sparse_verify", "fp8_prefill"):
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)

@@ -109,7 +109,11 @@ typedef enum {
  *
  * softmax_scale: 0 selects 1/sqrt(head_dim); otherwise it must be > 0.
  * Supported: head_dim 64/128/256 (INT4: 128/256), block_size 16/32,
- * num_q_heads / num_kv_heads * next_n <= 64, q_dtype F16; KV kinds F16, E4M3,
+ * next_n <= 4096 and next_n * num_q_heads / num_kv_heads <= 8192 query rows
+ * per KV head (beyond 32 rows -- long verify, chunked prefill -- the rows are
+ * processed in blocks of 32, each block walking only the tokens its last row
+ * can see; the workspace grows with the number of blocks), q_dtype F16; KV
+ * kinds F16, E4M3,
  * INT8, INT4. Workspace: paged_attn_workspace_size(a) bytes, 256-byte aligned.
  */
 typedef struct pa_attn_args {

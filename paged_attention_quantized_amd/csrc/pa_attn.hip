@@ -47,32 +47,38 @@
 
 namespace pa {
 
-// Combine the partials of each (sequence b, KV head hk) in a fixed order
-// (workgroup, then sub-tile), which depends on logical positions only [RELOC],
-// and apply the V scale and 1/l. A row with no visible token is +0. One thread
-// per 4 output channels; the item ranges of the ring kernel follow from the
-// sequence starts it published.
+// Combine the partials of each (sequence b, KV head hk, query row) in a fixed
+// order (workgroup, then sub-tile), which depends on logical positions only
+// [RELOC], and apply the V scale and 1/l. A row with no visible token is +0.
+// One thread per 4 output channels; the item ranges of the ring kernel follow
+// from the sequence starts it published.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
   const int bh = blockIdx.x;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
   const int hg = hk >> p.lhpu, hl = hk & (p.hpu - 1);
   const int idx = blockIdx.y * 256 + threadIdx.x;
   if (4 * idx >= p.R * D) return;
-  // the ring kernel's split: item k of run (b, hg) sits at cost slot
-  // first_slot(b) + hg * (nst + kRunCost) + kRunCost + k, and workgroup w owns
-  // slots [w * qc, (w + 1) * qc)
+  // the ring kernel's split: item k of run (b, rb, hg) sits at cost slot
+  // first_slot(b) + (slots of row blocks before rb) + hg * (nst + kRunCost) +
+  // kRunCost + k, and workgroup w owns slots [w * qc, (w + 1) * qc)
   const int qc = max(1, (p.ws_seq[p.B] + p.nwg - 1) / p.nwg);
   const int L = p.context_lens[b];
-  const int nst = seq_stages(p, L);
-  const int slot0 = p.ws_seq[b] + hg * (nst + kRunCost) + kRunCost;
   const int r = 4 * idx / D, d = 4 * idx % D;
+  const int rb = r / p.rpb, rl = r % p.rpb;
+  int slot0 = p.ws_seq[b];
+  for (int x = 0; x < rb; ++x) {
+    const int n = run_stages(p, L, x);
+    slot0 += n > 0 ? p.hgroups * (n + kRunCost) : 0;
+  }
+  const int nst = run_stages(p, L, rb);
+  slot0 += hg * (nst + kRunCost) + kRunCost;
   const int i = r / p.G, h = hk * p.G + r % p.G;
   const int nsub = p.wgmerge ? 1 : p.nsub;
   float m = -INFINITY, l = 0.f;
   f4 o = {0.f, 0.f, 0.f, 0.f};
   if (nst > 0) {
     const int w_first = slot0 / qc, w_last = (slot0 + nst - 1) / qc;
-    const int run = b * p.hgroups + hg;
+    const int run = (b * p.nrb + rb) * p.hgroups + hg;
     const int nparts = (w_last - w_first + 1) * nsub;
     constexpr int U = 8;
     for (int k0 = 0; k0 < nparts; k0 += U) {
@@ -82,8 +88,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
         if (k0 + k < nparts) {
           const int part = k0 + k;
           const size_t u = part_index(p, run, w_first + part / nsub, hl, part % nsub);
-          rec[k] = p.ws_ml[u * p.R + r];
-          x[k] = *reinterpret_cast<const f4*>(p.ws_o + (u * p.R + r) * D + d);
+          rec[k] = p.ws_ml[u * p.rpb + rl];
+          x[k] = *reinterpret_cast<const f4*>(p.ws_o + (u * p.rpb + rl) * D + d);
         } else {
           rec[k] = f4{-INFINITY, 0.f, 0.f, 0.f};
           x[k] = f4{0.f, 0.f, 0.f, 0.f};
@@ -253,6 +259,7 @@ namespace {
 
 struct Shape {
   int R, RT, RB, hpu, hgroups, ts, nw, nsub, nwg;
+  int nrb, rpb;                          // query row blocks and rows per block
   int sparse, sp_cap;                    // selection-driven mode: plan entries per sequence
   size_t sp_entries_bytes, sp_masks_bytes, sp_vlen_bytes;
   int pages_max, entries_per_seq;
@@ -306,8 +313,11 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
     return fail(PA_ERR_UNSUPPORTED, "paged_attn: F16 KV takes no scales");
   if (a->softmax_scale < 0.f || !(a->softmax_scale == a->softmax_scale))
     return fail(PA_ERR_INVALID_ARG, "paged_attn: softmax_scale must be >= 0");
-  const int R = a->next_n * (a->num_q_heads / a->num_kv_heads);
-  if (R > 64) return fail(PA_ERR_UNSUPPORTED, "paged_attn: next_n * q heads per kv head > 64");
+  const int G = a->num_q_heads / a->num_kv_heads;
+  if (a->next_n > kMaxNextN || (int64_t)a->next_n * G > kMaxRows)
+    return fail(PA_ERR_UNSUPPORTED, "paged_attn: next_n > %d or next_n * q heads per kv head > %d",
+                kMaxNextN, kMaxRows);
+  const int R = a->next_n * G;
   if ((int64_t)a->max_blocks_per_seq * a->block_size < a->max_context_len)
     return fail(PA_ERR_PRECONDITION,
                 "paged_attn: max_blocks_per_seq * block_size < max_context_len");
@@ -319,7 +329,10 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
       return fail(PA_ERR_INVALID_ARG, "paged_attn: scale mode set but scale pointer is NULL");
   }
   sh->R = R;
-  sh->RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
+  // more than 32 rows: blocks of 32 rows (two row tiles), one run each
+  sh->rpb = R <= 32 ? R : 32;
+  sh->nrb = (int)ceil_div(R, sh->rpb);
+  sh->RT = sh->rpb <= 16 ? 1 : 2;
   sh->RB = rb;
   // An item spans hpu KV heads (a divisor of the KV head count, at most 1 KiB
   // of row bytes per token) and ts tokens, so that one stage (K and V) is at
@@ -362,10 +375,10 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   sh->wgmerge = (sh->nsub > 1 && xch_per_head <= kXchBytes) ? 1 : 0;
   // partial slots: one per (run, workgroup) pair a run can span, at most
   // runs + workgroups of them, each with one partial per head and sub-tile
-  const int64_t slots = (int64_t)a->batch * sh->hgroups + sh->nwg;
+  const int64_t slots = (int64_t)a->batch * sh->nrb * sh->hgroups + sh->nwg;
   sh->parts = slots * sh->nw;
-  sh->ml_bytes = (size_t)round_up(sh->parts * R * 16, 256);
-  sh->o_bytes = (size_t)round_up(sh->parts * R * a->head_dim * 4, 256);
+  sh->ml_bytes = (size_t)round_up(sh->parts * sh->rpb * 16, 256);
+  sh->o_bytes = (size_t)round_up(sh->parts * sh->rpb * a->head_dim * 4, 256);
   sh->seq_bytes = (size_t)round_up(((int64_t)a->batch + 1) * 4, 256);
   sh->sparse = sparse_topk >= 0 ? 1 : 0;
   sh->sp_cap = 0;
@@ -400,6 +413,8 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   p.Hkv = a->num_kv_heads;
   p.G = a->num_q_heads / a->num_kv_heads;
   p.R = sh.R;
+  p.nrb = sh.nrb;
+  p.rpb = sh.rpb;
   p.bs = a->block_size;
   p.max_blocks = a->max_blocks_per_seq;
   p.hpu = sh.hpu;
@@ -419,12 +434,12 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   return p;
 }
 
-RingFn pick_ring(int kind, int D, int nw, int RT, bool hilo, bool sparse = false) {
+RingFn pick_ring(int kind, int D, int nw, int RT, bool hilo, int mode) {
   switch (kind) {
-    case PA_KV_F16: return pick_ring_f16(D, nw, RT, hilo, sparse);
-    case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, hilo, sparse);
-    case PA_KV_INT8: return pick_ring_int8(D, nw, RT, hilo, sparse);
-    case PA_KV_INT4: return pick_ring_int4(D, nw, RT, hilo, sparse);
+    case PA_KV_F16: return pick_ring_f16(D, nw, RT, hilo, mode);
+    case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, hilo, mode);
+    case PA_KV_INT8: return pick_ring_int8(D, nw, RT, hilo, mode);
+    case PA_KV_INT4: return pick_ring_int4(D, nw, RT, hilo, mode);
   }
   return nullptr;
 }
@@ -432,7 +447,8 @@ RingFn pick_ring(int kind, int D, int nw, int RT, bool hilo, bool sparse = false
 // Enqueue the ring kernel and the merge for checked arguments.
 pa_status launch_attn(const pa_attn_args* a, const Shape& sh, void* workspace, hipStream_t s) {
   const bool hilo = a->k_scale_mode == PA_SCALE_PER_CHANNEL;
-  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, hilo);
+  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, hilo,
+                        sh.nrb > 1 ? kModeRows : kModeDense);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
   AttnParams p = make_params(a, sh, workspace);
   launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), s, p, a->block_table,
@@ -527,7 +543,7 @@ extern "C" pa_status paged_attn_sparse(const pa_attn_args* a, const int32_t* sel
                 workspace_bytes);
   if (a->batch == 0) return PA_OK;
   if (topk > 0 && !sel) return fail(PA_ERR_INVALID_ARG, "paged_attn_sparse: sel is NULL");
-  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, false, true);
+  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, false, kModeSparse);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: no kernel for this kind/shape");
   char* base = (char*)workspace + sh.ml_bytes + sh.o_bytes + sh.seq_bytes;
   int32_t* entries = (int32_t*)base;

@@ -13,6 +13,8 @@ constexpr int kStages = 4;             // LDS ring depth
 constexpr int kStageMax = 32 * 1024;   // bytes per stage (K and V planes)
 constexpr int kMaxWaves = 8;           // wavefronts per workgroup
 constexpr int kXchBytes = 32 * 1024;   // LDS exchange buffer (ring + exchange = 160 KiB)
+constexpr int kMaxNextN = 4096;        // query steps per sequence
+constexpr int kMaxRows = 8192;         // query rows per KV head (next_n * q heads per KV head)
 constexpr int kRunCost = 2;            // work split: items a run start costs (q reload, partial)
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -30,6 +32,10 @@ struct AttnParams {
   float* ws_o;   // [partials, R, D]
   int* ws_seq;   // [B + 1]: first cost slot of each sequence, then the slot total
   int B, next_n, Hq, Hkv, G, R, bs, max_blocks;
+  // query row blocks: rows r = i * G + g are cut into nrb blocks of rpb rows;
+  // one run of items per (sequence, row block, head group). nrb = 1 and
+  // rpb = R when R <= 32.
+  int nrb, rpb;
   int hpu, hgroups, ts, nw, nsub;  // heads per item, head groups, tokens per item, waves, sub-tiles
   int nwg;                         // workgroups of the persistent grid
   int lbs, lts, lhpu;              // log2 of bs, ts, hpu (all powers of two)
@@ -49,6 +55,60 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // items of one sequence for one head group
 __device__ __forceinline__ int seq_stages(const AttnParams& p, int L) {
   return (L + p.ts - 1) >> p.lts;
+}
+
+// Tokens row block rb (rows [rb * rpb, min((rb + 1) * rpb, R)), row r being
+// step r / G) can see: under the causal rule its last step i sees
+// t <= L - next_n + i; all L otherwise (and for a single block).
+__device__ __forceinline__ int run_len(const AttnParams& p, int L, int rb) {
+  if (!p.causal || p.nrb == 1) return L;
+  const int last = (min((rb + 1) * p.rpb, p.R) - 1) / p.G;
+  return max(0, min(L, L - p.next_n + last + 1));
+}
+
+// step of row block rb's first row
+__device__ __forceinline__ int first_step(const AttnParams& p, int rb) {
+  return p.nrb == 1 ? 0 : rb * p.rpb / p.G;
+}
+
+// The first item at or after cost slot `rel` of a sequence of length L (rel
+// below the sequence's cost): its row block, head group and stage, and its
+// index among the sequence's items.
+__device__ __forceinline__ int locate_slot(const AttnParams& p, int L, int rel, int& rb, int& hg,
+                                           int& k);
+
+// items of the run (sequence of length L, row block rb, one head group)
+__device__ __forceinline__ int run_stages(const AttnParams& p, int L, int rb) {
+  return seq_stages(p, run_len(p, L, rb));
+}
+
+__device__ __forceinline__ int locate_slot(const AttnParams& p, int L, int rel, int& rb, int& hg,
+                                           int& k) {
+  int before = 0, n = run_stages(p, L, 0);
+  rb = 0;
+  while (rb + 1 < p.nrb) {
+    const int c = n > 0 ? p.hgroups * (n + kRunCost) : 0;
+    if (rel < c) break;
+    rel -= c;
+    before += p.hgroups * n;
+    ++rb;
+    n = run_stages(p, L, rb);
+  }
+  hg = rel / (n + kRunCost);
+  k = max(rel % (n + kRunCost) - kRunCost, 0);
+  return before + hg * n + k;
+}
+
+// A sequence's cost-line slots and items over all its row blocks: each run
+// with items takes kRunCost slots and then one per item, per head group.
+__device__ __forceinline__ void seq_cost(const AttnParams& p, int L, int& cost, int& items) {
+  cost = 0;
+  items = 0;
+  for (int rb = 0; rb < p.nrb; ++rb) {
+    const int n = run_stages(p, L, rb);
+    cost += n > 0 ? p.hgroups * (n + kRunCost) : 0;
+    items += p.hgroups * n;
+  }
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
@@ -71,7 +131,7 @@ __device__ __forceinline__ int lane_val(int x, int l) { return __builtin_amdgcn_
 // Position of one item in the (sequence, head group, stage) order; all fields
 // are workgroup-uniform.
 struct ItemPos {
-  int b, L, nst, hg, k;
+  int b, L, nst, hg, k, rb;
 };
 
 __device__ __forceinline__ void item_next(const AttnParams& p, const int32_t* __restrict__ lens,
@@ -81,9 +141,12 @@ __device__ __forceinline__ void item_next(const AttnParams& p, const int32_t* __
   if (++it.hg < p.hgroups) return;
   it.hg = 0;
   do {
-    ++it.b;
-    it.L = it.b < p.B ? lens[uni(it.b)] : 0;
-    it.nst = seq_stages(p, it.L);
+    if (++it.rb >= p.nrb) {
+      it.rb = 0;
+      ++it.b;
+      it.L = it.b < p.B ? lens[uni(it.b)] : 0;
+    }
+    it.nst = run_stages(p, it.L, it.rb);
   } while (it.nst == 0 && it.b < p.B);
 }
 
@@ -230,16 +293,18 @@ struct WaveState {
   int lim[RT];  // query row 16*rt+n sees tokens t <= lim
 };
 
-// Load Q' of (sequence b, KV head hk) and reset the softmax state.
+// Load Q' of (sequence b, row block rb, KV head hk) and reset the softmax
+// state. Local row 16 rt + n is query row rb * rpb + 16 rt + n.
 template <int KIND, int D, int RT, bool HILO>
-__device__ __forceinline__ void start_run(const AttnParams& p, int b, int hk, int L, float inv_m,
-                                          float sgn, WaveState<KIND, D, RT, HILO>& w) {
+__device__ __forceinline__ void start_run(const AttnParams& p, int b, int rb, int hk, int L,
+                                          float inv_m, float sgn,
+                                          WaveState<KIND, D, RT, HILO>& w) {
   using G_ = Geo<KIND, D>;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int r = 16 * rt + n;
-    const bool rv = r < p.R;
+    const int rl = 16 * rt + n, r = rb * p.rpb + rl;
+    const bool rv = rl < p.rpb && r < p.R;
     const int i = r / p.G, hg = r % p.G;
     const _Float16* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
 #pragma unroll
@@ -558,7 +623,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Partial index of (run r, workgroup w, head-in-group hl, sub-tile st); run
-// r = b * hgroups + hg. Slot r + w is unique: a later workgroup only reaches
+// r = (b * nrb + rb) * hgroups + hg. Slot r + w is unique: a later workgroup only reaches
 // later runs, so (r, w) != (r', w') with r + w == r' + w' cannot both occur.
 __device__ __forceinline__ size_t part_index(const AttnParams& p, int r, int w, int hl, int st) {
   return ((size_t)(r + w) * p.hpu + hl) * p.nsub + st;
@@ -572,10 +637,10 @@ __device__ __forceinline__ void write_partial(const AttnParams& p, size_t u, flo
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float l = w.l_acc[rt][0];
-    const int r = 16 * rt + n;
-    if (r < p.R) {
-      if (g == 0) p.ws_ml[u * p.R + r] = f4{w.m_run[rt], l, c2, 0.f};
-      float* orow = p.ws_o + (u * p.R + r) * D;
+    const int r = 16 * rt + n;  // local row of the run's block
+    if (r < p.rpb) {
+      if (g == 0) p.ws_ml[u * p.rpb + r] = f4{w.m_run[rt], l, c2, 0.f};
+      float* orow = p.ws_o + (u * p.rpb + r) * D;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float tmp[DV];
@@ -602,12 +667,18 @@ __device__ __forceinline__ void load_row_masks(const AttnParams& p,
   for (int i = 0; i < kSparseRows; ++i) m[i] = i < p.next_n ? masks[base + i] : 0u;
 }
 
-// SPARSE: table holds the union plan entries ({physical, logical} per page),
-// lens the per-sequence entry count times block_size, masks the row masks.
-template <int KIND, int D, int RT, bool HILO, int NWB, bool SPARSE>
+// Ring kernel modes: dense (one row block), selection-driven sparse, and dense
+// with several query row blocks per sequence.
+enum RingMode { kModeDense = 0, kModeSparse = 1, kModeRows = 2 };
+
+// MODE kModeSparse: table holds the union plan entries ({physical, logical}
+// per page), lens the per-sequence entry count times block_size, masks the row
+// masks. kModeRows: query rows come in p.nrb blocks of p.rpb rows.
+template <int KIND, int D, int RT, bool HILO, int NWB, int MODE>
 __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
     const uint32_t* __restrict__ masks) {
+  constexpr bool SPARSE = MODE == kModeSparse;
   using G_ = Geo<KIND, D>;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageMax];
   const int lane = threadIdx.x & 63, wv = uni(threadIdx.x >> 6);  // wave-uniform
@@ -615,12 +686,17 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   const int stage_bytes = (2 * p.ts * G_::RB) << p.lhpu;
   __shared__ __attribute__((aligned(16))) float xbuf[kXchBytes / 4];
   int* xi = reinterpret_cast<int*>(xbuf);
+  // one row block outside kModeRows: the block logic folds away
+  if constexpr (MODE != kModeRows) {
+    p.nrb = 1;
+    p.rpb = p.R;
+  }
   // the per-tensor K scale is read first, so its latency overlaps the scan
   const float ks_tensor =
       (!HILO && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
 
   // ---- this workgroup's item range. Items are placed on a cost line where
-  // each (sequence, head group) run first takes kRunCost empty slots (the
+  // each (sequence, row block, head group) run first takes kRunCost empty slots (the
   // pipeline drain at a run start) and then one slot per item; workgroup w
   // takes the items whose slots fall in [w*Qc, (w+1)*Qc). One wave scans the
   // sequence lengths; workgroup 0 also publishes every sequence's first slot
@@ -630,8 +706,8 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     const int len_first = lane < p.B ? lens[lane] : 0;  // kept for the second pass
     for (int base = 0; base < p.B; base += 64) {
       const int b = base + lane;
-      const int nst = base == 0 ? seq_stages(p, len_first) : (b < p.B ? seq_stages(p, lens[b]) : 0);
-      const int cost = nst > 0 ? p.hgroups * (nst + kRunCost) : 0;
+      int cost, items;
+      seq_cost(p, base == 0 ? len_first : (b < p.B ? lens[b] : 0), cost, items);
       const int incl = wave_incl_scan(cost);
       if (blockIdx.x == 0 && b < p.B) p.ws_seq[b] = ccarry + incl - cost;
       ccarry += lane_val(incl, 63);
@@ -639,15 +715,15 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     if (blockIdx.x == 0 && lane == 0) p.ws_seq[p.B] = ccarry;
     const int qc = max(1, (ccarry + p.nwg - 1) / p.nwg);
     const int ta = (int)blockIdx.x * qc, tz = ta + qc;  // this workgroup's slots
-    // first item at or after slot ta (and tz): sequence, head group, stage, index
-    int fb = -1, fL = 0, fhg = 0, fk = 0, ia = -1, iz = -1;
+    // first item at or after slot ta (and tz): sequence, row block, head
+    // group, stage, index
+    int fb = -1, fL = 0, frb = 0, fhg = 0, fk = 0, ia = -1, iz = -1;
     int c0 = 0, n0 = 0;
     for (int base = 0; base < p.B; base += 64) {
       const int b = base + lane;
       const int len = base == 0 ? len_first : (b < p.B ? lens[b] : 0);
-      const int nst = seq_stages(p, len);
-      const int items = p.hgroups * nst;
-      const int cost = nst > 0 ? p.hgroups * (nst + kRunCost) : 0;
+      int cost, items;
+      seq_cost(p, len, cost, items);
       const int ic = wave_incl_scan(cost), ii = wave_incl_scan(items);
       const int ec = c0 + ic - cost, ei = n0 + ii - items;
       // the first non-empty sequence whose slots end past t holds slot t
@@ -655,19 +731,14 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
       const uint64_t hit_z = __builtin_amdgcn_ballot_w64(cost > 0 && ec + cost > tz);
       if (hit_a) {
         const int f = __builtin_ctzll(hit_a);
-        const int n = lane_val(nst, f), rel = ta - lane_val(ec, f);
-        const int hg = rel / (n + kRunCost), k = max(rel % (n + kRunCost) - kRunCost, 0);
         fb = base + f;
         fL = lane_val(len, f);
-        fhg = hg;
-        fk = k;
-        ia = lane_val(ei, f) + hg * n + k;
+        ia = lane_val(ei, f) + locate_slot(p, fL, ta - lane_val(ec, f), frb, fhg, fk);
       }
       if (hit_z) {
         const int f = __builtin_ctzll(hit_z);
-        const int n = lane_val(nst, f), rel = tz - lane_val(ec, f);
-        const int hg = rel / (n + kRunCost), k = max(rel % (n + kRunCost) - kRunCost, 0);
-        iz = lane_val(ei, f) + hg * n + k;
+        int zrb, zhg, zk;
+        iz = lane_val(ei, f) + locate_slot(p, lane_val(len, f), tz - lane_val(ec, f), zrb, zhg, zk);
         break;
       }
       c0 += lane_val(ic, 63);
@@ -682,6 +753,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
       xi[2] = fhg;
       xi[3] = fk;
       xi[4] = fL;
+      xi[5] = frb;
     }
   }
   __syncthreads();
@@ -691,7 +763,8 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   ItemPos cp;
   cp.b = uni(xi[1]);
   cp.L = uni(xi[4]);
-  cp.nst = seq_stages(p, cp.L);
+  cp.rb = MODE != kModeRows ? 0 : uni(xi[5]);
+  cp.nst = run_stages(p, cp.L, cp.rb);
   cp.hg = uni(xi[2]);
   cp.k = uni(xi[3]);
 
@@ -717,7 +790,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   // Q' of the first run is loaded before the ring starts, so waiting for it
   // never waits for ring loads.
   WaveState<KIND, D, RT, HILO> w;
-  start_run<KIND, D, RT, HILO>(p, cp.b, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
+  start_run<KIND, D, RT, HILO>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
 
   // ---- ring prologue: kStages - 1 items in flight; the block-table loads of
   // all of them (and of the next one) are issued before any is waited for ----
@@ -741,6 +814,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     q.nst = in ? pos[j].nst : pos[0].nst;
     q.hg = in ? pos[j].hg : pos[0].hg;
     q.k = in ? pos[j].k : pos[0].k;
+    q.rb = in ? pos[j].rb : pos[0].rb;
     load_pages<KIND, D, SPARSE>(p, table, q, lp, pgs[j]);
   }
 #pragma unroll
@@ -778,19 +852,22 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
         uint32_t m = 0u;
 #pragma unroll
         for (int k = 0; k < kSparseRows; ++k) m = i == k ? mc[k] : m;
-        rm[rt] = r < p.R ? m : 0u;
+        rm[rt] = r < p.rpb ? m : 0u;  // one row block in this mode
       }
       compute_tile<KIND, D, RT, HILO, true>(ring + (j % kStages) * stage_bytes, to, t0, cp.L,
                                             false, c2, w, rm, mc[0] | mc[1] | mc[2] | mc[3],
                                             16 * st);
-    } else if (t0 < cp.L) {
-      compute_tile<KIND, D, RT, HILO>(ring + (j % kStages) * stage_bytes, to, t0, cp.L,
-                                      t0 + 16 <= cp.L - (p.causal ? p.next_n - 1 : 0), c2, w);
+    } else if (t0 < run_len(p, cp.L, cp.rb)) {
+      // full: the block's first row (step first_step) sees all 16 tokens
+      compute_tile<KIND, D, RT, HILO>(
+          ring + (j % kStages) * stage_bytes, to, t0, cp.L,
+          t0 + 16 <= cp.L - (p.causal ? p.next_n - 1 - first_step(p, cp.rb) : 0), c2, w);
     }
     // end of a (sequence, head group) run inside this range: write the partial
-    const int b = cp.b, hg = cp.hg;
+    const int b = cp.b, hg = cp.hg, rb = cp.rb;
     item_next(p, lens, cp);
-    if (j + 1 == nitems || cp.b != b || cp.hg != hg) {
+    if (j + 1 == nitems || cp.b != b || cp.hg != hg || cp.rb != rb) {
+      const int run = (b * p.nrb + rb) * p.hgroups + hg;
       if (p.wgmerge) {
         // fold sub-tiles 1 .. nsub-1 of each head into sub-tile 0, in order
         for (int h = 0; h < p.hpu; ++h)
@@ -801,14 +878,14 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
             lds_barrier();
           }
         if (st == 0)
-          write_partial<KIND, D, RT, HILO>(p, part_index(p, b * p.hgroups + hg, blockIdx.x, hl, 0),
+          write_partial<KIND, D, RT, HILO>(p, part_index(p, run, blockIdx.x, hl, 0),
                                            c2, w);
       } else {
-        write_partial<KIND, D, RT, HILO>(p, part_index(p, b * p.hgroups + hg, blockIdx.x, hl, st),
+        write_partial<KIND, D, RT, HILO>(p, part_index(p, run, blockIdx.x, hl, st),
                                          c2, w);
       }
       if (j + 1 < nitems)
-        start_run<KIND, D, RT, HILO>(p, cp.b, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
+        start_run<KIND, D, RT, HILO>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
     }
     // pages of the item the next iteration issues
     if (jn + 1 < nitems) load_pages<KIND, D, SPARSE>(p, table, ld, lp, pg);
@@ -827,48 +904,56 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
 typedef void (*RingFn)(AttnParams, const int32_t*, const int32_t*, const uint32_t*);
 
 // NWB: the launch bound in waves (4 or 8); a 4-wave workgroup gets twice the
-// registers per wave. The sparse mode exists for FP16 and per-tensor E4M3
-// caches, up to 32 query rows per KV head.
+// registers per wave. Row tiles RT are 1 or 2 (16 or 32 rows): more rows come
+// in row blocks of 32 (kModeRows). The sparse mode exists for FP16 and
+// per-tensor E4M3 caches, up to 32 query rows per KV head.
 template <int KIND, int D, int NWB>
-RingFn pick_rt(int RT, bool hilo, bool sparse) {
-  if (sparse) {
+RingFn pick_rt(int RT, bool hilo, int mode) {
+  if (RT != 1 && RT != 2) return nullptr;
+  if (mode == kModeSparse) {
     if constexpr (KIND == PA_KV_F16 || KIND == PA_KV_E4M3) {
       if (hilo) return nullptr;
-      if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, true>;
-      if (RT == 2) return attn_ring_kernel<KIND, D, 2, false, NWB, true>;
+      if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, kModeSparse>;
+      return attn_ring_kernel<KIND, D, 2, false, NWB, kModeSparse>;
     }
     return nullptr;
+  }
+  if (mode == kModeRows) {
+    if (RT != 2) return nullptr;
+    if (hilo) {
+      if constexpr (KIND == PA_KV_F16) return nullptr;
+      else return attn_ring_kernel<KIND, D, 2, true, NWB, kModeRows>;
+    }
+    return attn_ring_kernel<KIND, D, 2, false, NWB, kModeRows>;
   }
   if (hilo) {
     if constexpr (KIND == PA_KV_F16) return nullptr;
     else {
-      if (RT == 1) return attn_ring_kernel<KIND, D, 1, true, NWB, false>;
-      if (RT == 2) return attn_ring_kernel<KIND, D, 2, true, NWB, false>;
-      return attn_ring_kernel<KIND, D, 4, true, NWB, false>;
+      if (RT == 1) return attn_ring_kernel<KIND, D, 1, true, NWB, kModeDense>;
+      return attn_ring_kernel<KIND, D, 2, true, NWB, kModeDense>;
     }
   }
-  if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, false>;
-  if (RT == 2) return attn_ring_kernel<KIND, D, 2, false, NWB, false>;
-  return attn_ring_kernel<KIND, D, 4, false, NWB, false>;
+  if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, kModeDense>;
+  return attn_ring_kernel<KIND, D, 2, false, NWB, kModeDense>;
 }
 
 template <int KIND, int D>
-RingFn pick_nw(int nw, int RT, bool hilo, bool sparse) {
-  return nw <= 4 ? pick_rt<KIND, D, 4>(RT, hilo, sparse) : pick_rt<KIND, D, 8>(RT, hilo, sparse);
+RingFn pick_nw(int nw, int RT, bool hilo, int mode) {
+  return nw <= 4 ? pick_rt<KIND, D, 4>(RT, hilo, mode) : pick_rt<KIND, D, 8>(RT, hilo, mode);
 }
 
 template <int KIND>
-RingFn pick_d(int D, int nw, int RT, bool hilo, bool sparse) {
+RingFn pick_d(int D, int nw, int RT, bool hilo, int mode) {
   if constexpr (KIND != PA_KV_INT4)
-    if (D == 64) return pick_nw<KIND, 64>(nw, RT, hilo, sparse);
-  if (D == 128) return pick_nw<KIND, 128>(nw, RT, hilo, sparse);
-  return pick_nw<KIND, 256>(nw, RT, hilo, sparse);
+    if (D == 64) return pick_nw<KIND, 64>(nw, RT, hilo, mode);
+  if (D == 128) return pick_nw<KIND, 128>(nw, RT, hilo, mode);
+  return pick_nw<KIND, 256>(nw, RT, hilo, mode);
 }
 
 // Ring kernel of one KV kind (each defined in its own translation unit).
-RingFn pick_ring_f16(int D, int nw, int RT, bool hilo, bool sparse);
-RingFn pick_ring_e4m3(int D, int nw, int RT, bool hilo, bool sparse);
-RingFn pick_ring_int8(int D, int nw, int RT, bool hilo, bool sparse);
-RingFn pick_ring_int4(int D, int nw, int RT, bool hilo, bool sparse);
+RingFn pick_ring_f16(int D, int nw, int RT, bool hilo, int mode);
+RingFn pick_ring_e4m3(int D, int nw, int RT, bool hilo, int mode);
+RingFn pick_ring_int8(int D, int nw, int RT, bool hilo, int mode);
+RingFn pick_ring_int4(int D, int nw, int RT, bool hilo, int mode);
 
 }  // namespace pa

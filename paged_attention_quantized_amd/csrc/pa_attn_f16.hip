@@ -3,6 +3,8 @@
 
 namespace pa {
 
-RingFn pick_ring_f16(int D, int nw, int RT, bool hilo, bool sparse) { return pick_d<PA_KV_F16>(D, nw, RT, hilo, sparse); }
+RingFn pick_ring_f16(int D, int nw, int RT, bool hilo, int mode) {
+  return pick_d<PA_KV_F16>(D, nw, RT, hilo, mode);
+}
 
 }  // namespace pa

@@ -323,6 +323,16 @@ def fp8_verify(seed=SEED_BASE + 3, B=16, lo=4096, hi=16384) -> AttnCase:
                      max_context_len=hi)
 
 
+def fp8_prefill(seed=SEED_BASE + 7, B=8, next_n=256, lo=4096, hi=16384) -> AttnCase:
+    """E4M3 chunked prefill: B 8, next_n 256 causal, 64 q / 8 KV heads, D 128,
+    block 32, lens uniform in [4096, 16384] (the chunk's 256 tokens included)."""
+    rng = np.random.default_rng(seed + 10_000)
+    lens = rng.integers(lo, hi + 1, B)
+    return attn_case("fp8_prefill", seed, B=B, next_n=next_n, Hq=64, Hkv=8, D=128, bs=32,
+                     lens=lens, kv_kind=KV_E4M3, scale_mode=SCALE_PER_TENSOR, causal=True,
+                     max_context_len=hi)
+
+
 # ---------------------------------------------------------------------------
 # MXFP4 paged MQA logits
 # ---------------------------------------------------------------------------
