@@ -57,19 +57,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
   const int hg = hk >> p.lhpu, hl = hk & (p.hpu - 1);
   const int idx = blockIdx.y * 256 + threadIdx.x;
-  if (4 * idx >= p.R * D) return;
   // the ring kernel's split: item k of run (b, rb, hg) sits at cost slot
   // first_slot(b) + (slots of row blocks before rb) + hg * (nst + kRunCost) +
   // kRunCost + k, and workgroup w owns slots [w * qc, (w + 1) * qc)
   const int qc = max(1, (p.ws_seq[p.B] + p.nwg - 1) / p.nwg);
   const int L = p.context_lens[b];
   const int r = 4 * idx / D, d = 4 * idx % D;
-  const int rb = r / p.rpb, rl = r % p.rpb;
-  int slot0 = p.ws_seq[b];
-  for (int x = 0; x < rb; ++x) {
-    const int n = run_stages(p, L, x);
-    slot0 += n > 0 ? p.hgroups * (n + kRunCost) : 0;
+  // a workgroup's 1024 / D rows never straddle a row block (32 rows, or all
+  // R rows when there is one block): its block is workgroup-uniform, and the
+  // slots of the blocks before it are summed 64 blocks at a time
+  const int rb = uni((int)blockIdx.y * (1024 / D) / p.rpb), rl = r - rb * p.rpb;
+  int before = 0;
+  for (int x0 = 0; x0 < rb; x0 += 64) {
+    const int x = x0 + (int)(threadIdx.x & 63);
+    const int n = x < rb ? run_stages(p, L, x) : 0;
+    before += lane_val(wave_incl_scan(n > 0 ? p.hgroups * (n + kRunCost) : 0), 63);
   }
+  int slot0 = p.ws_seq[b] + uni(before);
+  if (4 * idx >= p.R * D) return;  // after the wave-wide sums, which need every lane
   const int nst = run_stages(p, L, rb);
   slot0 += hg * (nst + kRunCost) + kRunCost;
   const int i = r / p.G, h = hk * p.G + r % p.G;
@@ -261,6 +266,7 @@ struct Shape {
   int R, RT, RB, hpu, hgroups, ts, nw, nsub, nwg;
   int nrb, rpb;                          // query row blocks and rows per block
   int sparse, sp_cap;                    // selection-driven mode: plan entries per sequence
+  int prefill;                           // the prefill layout (attn_prefill_kernel)
   size_t sp_entries_bytes, sp_masks_bytes, sp_vlen_bytes;
   int pages_max, entries_per_seq;
   int wgmerge;
@@ -289,6 +295,16 @@ int device_cus() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+PrefillFn pick_prefill_fn(int kind, int D, bool hilo) {
+  switch (kind) {
+    case PA_KV_F16: return pick_prefill_f16(D, hilo);
+    case PA_KV_E4M3: return pick_prefill_e4m3(D, hilo);
+    case PA_KV_INT8: return pick_prefill_int8(D, hilo);
+    case PA_KV_INT4: return pick_prefill_int4(D, hilo);
+  }
+  return nullptr;
 }
 
 pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int sparse_topk = -1) {
@@ -329,10 +345,15 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
       return fail(PA_ERR_INVALID_ARG, "paged_attn: scale mode set but scale pointer is NULL");
   }
   sh->R = R;
-  // more than 32 rows: blocks of 32 rows (two row tiles), one run each
-  sh->rpb = R <= 32 ? R : 32;
+  // at least kPfMinRows rows per KV head, where the layout fits: the prefill
+  // kernel, 256-row groups of one head
+  sh->prefill = sparse_topk < 0 && R >= kPfMinRows &&
+                pick_prefill_fn(a->kv_kind, a->head_dim,
+                                a->k_scale_mode == PA_SCALE_PER_CHANNEL) != nullptr;
+  // more than 32 rows otherwise: blocks of 32 rows (two row tiles), one run each
+  sh->rpb = sh->prefill ? 32 * kPfWaves : (R <= 32 ? R : 32);
   sh->nrb = (int)ceil_div(R, sh->rpb);
-  sh->RT = sh->rpb <= 16 ? 1 : 2;
+  sh->RT = sh->rpb <= 16 ? 1 : 2;  // the prefill kernel holds two row tiles per wave
   sh->RB = rb;
   // An item spans hpu KV heads (a divisor of the KV head count, at most 1 KiB
   // of row bytes per token) and ts tokens, so that one stage (K and V) is at
@@ -353,6 +374,9 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
     while (hpu > 1 && (2 * ts * hpu * rb > kStageMax || hpu * (ts / 16) > kMaxWaves)) hpu /= 2;
     if (2 * ts * hpu * rb > kStageMax)
       return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: one page exceeds a ring stage");
+  } else if (sh->prefill) {
+    hpu = 1;
+    ts = kPfTokens;
   } else {
     while (hpu > 1 && hpu * rb > 1024) hpu /= 2;
     ts = kStageMax / 2 / (hpu * rb);
@@ -373,10 +397,12 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   // buffer.
   const int xch_per_head = sh->RT * (a->head_dim / 16) * 1024 + sh->RT * 512;
   sh->wgmerge = (sh->nsub > 1 && xch_per_head <= kXchBytes) ? 1 : 0;
+  if (sh->prefill) sh->wgmerge = 1;  // one partial per group: the waves own disjoint rows
   // partial slots: one per (run, workgroup) pair a run can span, at most
-  // runs + workgroups of them, each with one partial per head and sub-tile
+  // runs + workgroups of them, each with one partial per head (and per
+  // sub-tile when sub-tiles are not merged in the workgroup)
   const int64_t slots = (int64_t)a->batch * sh->nrb * sh->hgroups + sh->nwg;
-  sh->parts = slots * sh->nw;
+  sh->parts = slots * (sh->wgmerge ? sh->hpu : sh->nw);
   sh->ml_bytes = (size_t)round_up(sh->parts * sh->rpb * 16, 256);
   sh->o_bytes = (size_t)round_up(sh->parts * sh->rpb * a->head_dim * 4, 256);
   sh->seq_bytes = (size_t)round_up(((int64_t)a->batch + 1) * 4, 256);
@@ -447,13 +473,20 @@ RingFn pick_ring(int kind, int D, int nw, int RT, bool hilo, int mode) {
 // Enqueue the ring kernel and the merge for checked arguments.
 pa_status launch_attn(const pa_attn_args* a, const Shape& sh, void* workspace, hipStream_t s) {
   const bool hilo = a->k_scale_mode == PA_SCALE_PER_CHANNEL;
-  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, hilo,
-                        sh.nrb > 1 ? kModeRows : kModeDense);
-  if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
   AttnParams p = make_params(a, sh, workspace);
-  launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), s, p, a->block_table,
-               a->context_lens, (const uint32_t*)nullptr);
-  pa_status st = launch_status("paged_attn ring kernel");
+  if (sh.prefill) {
+    PrefillFn fn = pick_prefill_fn(a->kv_kind, a->head_dim, hilo);
+    if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no prefill kernel for this kind/shape");
+    launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * kPfWaves), s, p, a->block_table,
+                 a->context_lens);
+  } else {
+    RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, hilo,
+                          sh.nrb > 1 ? kModeRows : kModeDense);
+    if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
+    launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), s, p, a->block_table,
+                 a->context_lens, (const uint32_t*)nullptr);
+  }
+  pa_status st = launch_status("paged_attn attention kernel");
   if (st != PA_OK) return st;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(a->batch * a->num_kv_heads),
                      (unsigned)ceil_div((int64_t)sh.R * a->head_dim / 4, 256)), dim3(256), 0, s,

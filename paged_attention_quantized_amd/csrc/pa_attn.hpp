@@ -626,18 +626,19 @@ __device__ __forceinline__ void lds_barrier() {
 // r = (b * nrb + rb) * hgroups + hg. Slot r + w is unique: a later workgroup only reaches
 // later runs, so (r, w) != (r', w') with r + w == r' + w' cannot both occur.
 __device__ __forceinline__ size_t part_index(const AttnParams& p, int r, int w, int hl, int st) {
-  return ((size_t)(r + w) * p.hpu + hl) * p.nsub + st;
+  return ((size_t)(r + w) * p.hpu + hl) * (p.wgmerge ? 1 : p.nsub) + st;
 }
 
 template <int KIND, int D, int RT, bool HILO>
 __device__ __forceinline__ void write_partial(const AttnParams& p, size_t u, float c2,
-                                              const WaveState<KIND, D, RT, HILO>& w) {
+                                              const WaveState<KIND, D, RT, HILO>& w,
+                                              int row0 = 0) {
   constexpr int DV = Geo<KIND, D>::DV;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float l = w.l_acc[rt][0];
-    const int r = 16 * rt + n;  // local row of the run's block
+    const int r = row0 + 16 * rt + n;  // row of the run's block
     if (r < p.rpb) {
       if (g == 0) p.ws_ml[u * p.rpb + r] = f4{w.m_run[rt], l, c2, 0.f};
       float* orow = p.ws_o + (u * p.rpb + r) * D;
@@ -665,6 +666,68 @@ __device__ __forceinline__ void load_row_masks(const AttnParams& p,
   const size_t base = ((size_t)it.b * p.sp_cap + it.k) * p.next_n;
 #pragma unroll
   for (int i = 0; i < kSparseRows; ++i) m[i] = i < p.next_n ? masks[base + i] : 0u;
+}
+
+// This workgroup's item range, computed by one wave (see the cost line in
+// the kernel below); lane 0 leaves {count, b, hg, k, L, rb} of the first item
+// in xi[0..5]. Workgroup 0 also publishes every sequence's first slot and the
+// slot total for the merge kernel.
+__device__ __forceinline__ void range_scan(const AttnParams& p, const int32_t* __restrict__ lens,
+                                           int* xi) {
+  const int lane = threadIdx.x & 63;
+  int ccarry = 0;
+  const int len_first = lane < p.B ? lens[lane] : 0;  // kept for the second pass
+  for (int base = 0; base < p.B; base += 64) {
+    const int b = base + lane;
+    int cost, items;
+    seq_cost(p, base == 0 ? len_first : (b < p.B ? lens[b] : 0), cost, items);
+    const int incl = wave_incl_scan(cost);
+    if (blockIdx.x == 0 && b < p.B) p.ws_seq[b] = ccarry + incl - cost;
+    ccarry += lane_val(incl, 63);
+  }
+  if (blockIdx.x == 0 && lane == 0) p.ws_seq[p.B] = ccarry;
+  const int qc = max(1, (ccarry + p.nwg - 1) / p.nwg);
+  const int ta = (int)blockIdx.x * qc, tz = ta + qc;  // this workgroup's slots
+  // first item at or after slot ta (and tz): sequence, row block, head
+  // group, stage, index
+  int fb = -1, fL = 0, frb = 0, fhg = 0, fk = 0, ia = -1, iz = -1;
+  int c0 = 0, n0 = 0;
+  for (int base = 0; base < p.B; base += 64) {
+    const int b = base + lane;
+    const int len = base == 0 ? len_first : (b < p.B ? lens[b] : 0);
+    int cost, items;
+    seq_cost(p, len, cost, items);
+    const int ic = wave_incl_scan(cost), ii = wave_incl_scan(items);
+    const int ec = c0 + ic - cost, ei = n0 + ii - items;
+    // the first non-empty sequence whose slots end past t holds slot t
+    const uint64_t hit_a = ia >= 0 ? 0 : __builtin_amdgcn_ballot_w64(cost > 0 && ec + cost > ta);
+    const uint64_t hit_z = __builtin_amdgcn_ballot_w64(cost > 0 && ec + cost > tz);
+    if (hit_a) {
+      const int f = __builtin_ctzll(hit_a);
+      fb = base + f;
+      fL = lane_val(len, f);
+      ia = lane_val(ei, f) + locate_slot(p, fL, ta - lane_val(ec, f), frb, fhg, fk);
+    }
+    if (hit_z) {
+      const int f = __builtin_ctzll(hit_z);
+      int zrb, zhg, zk;
+      iz = lane_val(ei, f) + locate_slot(p, lane_val(len, f), tz - lane_val(ec, f), zrb, zhg, zk);
+      break;
+    }
+    c0 += lane_val(ic, 63);
+    n0 += lane_val(ii, 63);
+  }
+  // slots past the last sequence: the range ends at the item total
+  if (ia < 0) ia = n0;
+  if (iz < 0) iz = n0;
+  if (lane == 0) {
+    xi[0] = iz - ia;
+    xi[1] = fb;
+    xi[2] = fhg;
+    xi[3] = fk;
+    xi[4] = fL;
+    xi[5] = frb;
+  }
 }
 
 // Ring kernel modes: dense (one row block), selection-driven sparse, and dense
@@ -701,61 +764,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   // takes the items whose slots fall in [w*Qc, (w+1)*Qc). One wave scans the
   // sequence lengths; workgroup 0 also publishes every sequence's first slot
   // and the total for the merge kernel ----
-  if (wv == 0) {
-    int ccarry = 0;
-    const int len_first = lane < p.B ? lens[lane] : 0;  // kept for the second pass
-    for (int base = 0; base < p.B; base += 64) {
-      const int b = base + lane;
-      int cost, items;
-      seq_cost(p, base == 0 ? len_first : (b < p.B ? lens[b] : 0), cost, items);
-      const int incl = wave_incl_scan(cost);
-      if (blockIdx.x == 0 && b < p.B) p.ws_seq[b] = ccarry + incl - cost;
-      ccarry += lane_val(incl, 63);
-    }
-    if (blockIdx.x == 0 && lane == 0) p.ws_seq[p.B] = ccarry;
-    const int qc = max(1, (ccarry + p.nwg - 1) / p.nwg);
-    const int ta = (int)blockIdx.x * qc, tz = ta + qc;  // this workgroup's slots
-    // first item at or after slot ta (and tz): sequence, row block, head
-    // group, stage, index
-    int fb = -1, fL = 0, frb = 0, fhg = 0, fk = 0, ia = -1, iz = -1;
-    int c0 = 0, n0 = 0;
-    for (int base = 0; base < p.B; base += 64) {
-      const int b = base + lane;
-      const int len = base == 0 ? len_first : (b < p.B ? lens[b] : 0);
-      int cost, items;
-      seq_cost(p, len, cost, items);
-      const int ic = wave_incl_scan(cost), ii = wave_incl_scan(items);
-      const int ec = c0 + ic - cost, ei = n0 + ii - items;
-      // the first non-empty sequence whose slots end past t holds slot t
-      const uint64_t hit_a = ia >= 0 ? 0 : __builtin_amdgcn_ballot_w64(cost > 0 && ec + cost > ta);
-      const uint64_t hit_z = __builtin_amdgcn_ballot_w64(cost > 0 && ec + cost > tz);
-      if (hit_a) {
-        const int f = __builtin_ctzll(hit_a);
-        fb = base + f;
-        fL = lane_val(len, f);
-        ia = lane_val(ei, f) + locate_slot(p, fL, ta - lane_val(ec, f), frb, fhg, fk);
-      }
-      if (hit_z) {
-        const int f = __builtin_ctzll(hit_z);
-        int zrb, zhg, zk;
-        iz = lane_val(ei, f) + locate_slot(p, lane_val(len, f), tz - lane_val(ec, f), zrb, zhg, zk);
-        break;
-      }
-      c0 += lane_val(ic, 63);
-      n0 += lane_val(ii, 63);
-    }
-    // slots past the last sequence: the range ends at the item total
-    if (ia < 0) ia = n0;
-    if (iz < 0) iz = n0;
-    if (lane == 0) {
-      xi[0] = iz - ia;
-      xi[1] = fb;
-      xi[2] = fhg;
-      xi[3] = fk;
-      xi[4] = fL;
-      xi[5] = frb;
-    }
-  }
+  if (wv == 0) range_scan(p, lens, xi);
   __syncthreads();
   // workgroup-uniform (read back from LDS, so say so to the compiler)
   const int nitems = uni(xi[0]);
@@ -901,6 +910,340 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Prefill layout: hundreds of query rows per KV head
+// ---------------------------------------------------------------------------
+// In the ring kernel's row-block mode every block of 32 rows decodes the same
+// K and V again. Here the 8 waves of a workgroup are 8 row blocks (a group of
+// 256 rows) of one KV head: a stage holds 128 tokens of that head, the waves
+// decode it once together into fp16 in LDS, and each wave then runs all 8
+// sub-tiles of 16 tokens for its own 32 rows from the decoded copy. Runs are
+// (sequence, row group, KV head) and items are 128-token stages: the cost
+// line, item order, partials and merge are those of the ring kernel with one
+// head per group (hpu 1), 128-token items and 256-row blocks.
+constexpr int kPfWaves = 8;
+constexpr int kPfTokens = 128;  // tokens per stage
+constexpr int kPfStages = 3;    // ring stages (two in flight while one is computed)
+constexpr int kPfMinRows = 128; // query rows per KV head from which the prefill layout is used
+
+template <int KIND, int D>
+struct PfGeo {
+  using G_ = Geo<KIND, D>;
+  static constexpr int PPR = D / 8;                    // 16-byte pieces of a decoded K row
+  static constexpr int SLOTS = kPfTokens / 4;          // 8-byte token quads of a decoded V row
+  static constexpr int STAGE = 2 * kPfTokens * G_::RB;  // K and V codes of one stage
+  static constexpr int KDEC = kPfTokens * D * 2;        // fp16 K, [token][channel]
+  static constexpr int VDEC = D * kPfTokens * 2;        // fp16 V, [channel][token]
+  static constexpr int BPE = G_::BITS;                  // code bytes of 8 channels of a token
+  static constexpr int LDS = kPfStages * STAGE + KDEC + VDEC;
+  static constexpr bool OK = D <= 128 && STAGE <= kStageMax && LDS <= 160 * 1024;
+};
+
+// Decode one landed stage into kdec / vdec. Block (tb, cb) = tokens 4 tb ..
+// 4 tb + 3, channels 8 cb .. 8 cb + 7 of both planes. In the ring slot the
+// piece j of token tau sits at j ^ (tau & (CPR - 1)); in kdec piece c (8
+// channels) of token tau sits at c ^ (tau & (PPR - 1)); in vdec the 4-token
+// quad s of channel ch sits at s ^ ((ch / DV) & 15). Both swizzles spread the
+// 16 lanes of a compute read over all banks.
+template <int KIND, int D>
+__device__ __forceinline__ void pf_decode(const uint8_t* slot, uint8_t* kdec, uint8_t* vdec) {
+  using G_ = Geo<KIND, D>;
+  using F_ = PfGeo<KIND, D>;
+  constexpr int NDW = F_::BPE / 4;
+  constexpr int PLANE = kPfTokens * G_::RB;
+  for (int blk = threadIdx.x; blk < (kPfTokens / 4) * F_::PPR; blk += 64 * kPfWaves) {
+    const int tb = blk / F_::PPR, cb = blk % F_::PPR;
+    const int byte = cb * F_::BPE;
+    h2 vv[4][4];  // V of token i: channel pairs (2m, 2m + 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tau = 4 * tb + i;
+      const int off = tau * G_::RB + 16 * ((byte / 16) ^ (tau & (G_::CPR - 1))) + byte % 16;
+      uint32_t kw[NDW], vw[NDW];
+#pragma unroll
+      for (int d = 0; d < NDW; ++d) {
+        kw[d] = *reinterpret_cast<const uint32_t*>(slot + off + 4 * d);
+        vw[d] = *reinterpret_cast<const uint32_t*>(slot + PLANE + off + 4 * d);
+      }
+      _Float16 kh[8], vh[8];  // natural channel order
+      {
+        _Float16 tk[2 * Kv<KIND>::kPairsPerDword * NDW], tv[2 * Kv<KIND>::kPairsPerDword * NDW];
+        decode_run<KIND, NDW>(kw, tk);
+        decode_run<KIND, NDW>(vw, tv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kh[run_elem<KIND>(e)] = tk[e];
+          vh[run_elem<KIND>(e)] = tv[e];
+        }
+      }
+      h8 kop;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kop[e] = kh[e];
+      *reinterpret_cast<h8*>(kdec + tau * (D * 2) + 16 * (cb ^ (tau & (F_::PPR - 1)))) = kop;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) vv[i][m] = h2{vh[2 * m], vh[2 * m + 1]};
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int ch = 8 * cb + c;
+      const h4 quad = {vv[0][c / 2][c % 2], vv[1][c / 2][c % 2], vv[2][c / 2][c % 2],
+                       vv[3][c / 2][c % 2]};
+      *reinterpret_cast<h4*>(vdec + ch * (kPfTokens * 2) +
+                             8 * (tb ^ ((ch / Geo<KIND, D>::DV) & 15))) = quad;
+    }
+  }
+}
+
+// Q of rows [row0, row0 + 32) of sequence b for KV head hk, in natural channel
+// order (k-step ks, lane group g: channels 32 ks + 8 g .. + 7), folded with a
+// PER_CHANNEL K scale as in start_run; resets the softmax state.
+template <int KIND, int D, bool HILO>
+__device__ __forceinline__ void pf_start_run(const AttnParams& p, int b, int row0, int hk, int L,
+                                             float inv_m, float sgn,
+                                             WaveState<KIND, D, 2, HILO>& w) {
+  using G_ = Geo<KIND, D>;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = row0 + 16 * rt + n;
+    const bool rv = r < p.R;
+    const int i = r / p.G, hg = r % p.G;
+    const _Float16* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
+#pragma unroll
+    for (int ks = 0; ks < G_::KS; ++ks) {
+      const int d0 = 32 * ks + 8 * g;
+      h8 v = {};
+      if (rv) v = *reinterpret_cast<const h8*>(qrow + d0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)v[e];
+        if constexpr (HILO) {
+          const float xf = x * (p.k_scale[hk * D + d0 + e] * inv_m) * sgn;
+          const _Float16 hi = (_Float16)xf;
+          w.qa[rt][ks][e] = hi;
+          w.qb[rt][ks][e] = (_Float16)(xf - (float)hi);
+        } else {
+          w.qa[rt][ks][e] = (_Float16)(x * sgn);
+        }
+      }
+    }
+    w.m_run[rt] = -INFINITY;
+    w.l_acc[rt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < G_::DV; ++q) w.o[rt][q] = f4{0.f, 0.f, 0.f, 0.f};
+    w.lim[rt] = p.causal ? (L - p.next_n + i) : 0x7fffffff;
+  }
+}
+
+// One 16-token sub-tile (stage tokens 16 st ..) for the wave's 32 rows from
+// the decoded stage. full: every row sees all 16 tokens.
+template <int KIND, int D, bool HILO>
+__device__ __forceinline__ void pf_tile(const uint8_t* kdec, const uint8_t* vdec, int st, int t0,
+                                        int L, bool full, float c2,
+                                        WaveState<KIND, D, 2, HILO>& w) {
+  using G_ = Geo<KIND, D>;
+  using F_ = PfGeo<KIND, D>;
+  constexpr int KS = G_::KS, DV = G_::DV;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int tau = 16 * st + n;
+  h8 kop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    kop[ks] = *reinterpret_cast<const h8*>(kdec + tau * (D * 2) +
+                                           16 * ((4 * ks + g) ^ (tau & (F_::PPR - 1))));
+  f4 sacc[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qa[rt][ks], acc, 0, 0, 0);
+      if constexpr (HILO)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qb[rt][ks], acc, 0, 0, 0);
+    }
+    sacc[rt] = acc;
+  }
+  h4 pb[2];
+  bool rescale = false;
+  float alpha[2];
+  if (full) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+      tile_softmax<false>(sacc[rt], 0xFu, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      uint32_t okbits = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + 4 * g + e;
+        okbits |= (uint32_t)(t < L && t <= w.lim[rt]) << e;
+      }
+      tile_softmax<true>(sacc[rt], okbits, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int q = 0; q < DV; ++q) w.o[rt][q] *= alpha[rt];
+      w.l_acc[rt] *= alpha[rt];
+    }
+  }
+  // O^T += V^T P^T: channel row n * DV + q, tokens 4 g .. 4 g + 3. Tokens past
+  // the end have p = 0 and decoded V bytes of real (if stale) codes; a NaN
+  // there is cleared below before it can meet p = 0.
+#pragma unroll
+  for (int q = 0; q < DV; ++q) {
+    const int ch = n * DV + q;
+    h4 va = *reinterpret_cast<const h4*>(vdec + ch * (kPfTokens * 2) +
+                                          8 * ((4 * st + g) ^ (ch / DV & 15)));
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) va[e] = t0 + 4 * g + e < L ? va[e] : (_Float16)0.0f;
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+      w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rt], w.o[rt][q], 0, 0, 0);
+  }
+  const h4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+    w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb[rt], w.l_acc[rt], 0, 0, 0);
+}
+
+template <int KIND, int D, bool HILO>
+__global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
+    AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens) {
+  using G_ = Geo<KIND, D>;
+  using F_ = PfGeo<KIND, D>;
+  static_assert(F_::OK, "prefill layout does not fit this kind and head_dim");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[F_::LDS];
+  uint8_t* ring = lds;
+  uint8_t* kdec = lds + kPfStages * F_::STAGE;
+  uint8_t* vdec = kdec + F_::KDEC;
+  int* xi = reinterpret_cast<int*>(kdec);  // the scan result, read before any decode
+  const int lane = threadIdx.x & 63, wv = uni(threadIdx.x >> 6);
+  const float ks_tensor = (!HILO && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
+  if (wv == 0) range_scan(p, lens, xi);
+  __syncthreads();
+  const int nitems = uni(xi[0]);
+  if (nitems <= 0) return;
+  ItemPos cp;
+  cp.b = uni(xi[1]);
+  cp.L = uni(xi[4]);
+  cp.rb = uni(xi[5]);
+  cp.nst = run_stages(p, cp.L, cp.rb);
+  cp.hg = uni(xi[2]);
+  cp.k = uni(xi[3]);
+  __syncthreads();  // xi lives in kdec
+
+  float qk, inv_m = 0.f;
+  if constexpr (HILO) {
+    float mx = 0.f;
+    for (int i = lane; i < p.Hkv * D; i += 64) mx = fmaxf(mx, fabsf(p.k_scale[i]));
+    mx = wave_max(mx);
+    inv_m = mx > 0.f ? 1.0f / mx : 0.f;
+    qk = p.softmax_scale * mx;
+  } else {
+    qk = p.softmax_scale * ks_tensor;
+  }
+  const float sgn = qk < 0.f ? -1.f : 1.f;
+  const float c2 = fabsf(qk) * kLog2e;
+
+  LoadPlan<KIND, D> lp;
+  make_load_plan<KIND, D>(p, lp);
+
+  // rows of this wave inside its run's group, and the steps they span
+  auto row0_of = [&](int rb) { return rb * p.rpb + 32 * wv; };
+  WaveState<KIND, D, 2, HILO> w;
+  pf_start_run<KIND, D, HILO>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
+
+  // ---- prologue: items 0 and 1 in flight, the pages of item 2 looked up ----
+  ItemPos pos[kPfStages];
+  pos[0] = cp;
+#pragma unroll
+  for (int j = 1; j < kPfStages; ++j) {
+    pos[j] = pos[j - 1];
+    if (j - 1 < nitems) item_next(p, lens, pos[j]);
+  }
+  PageSet<KIND, D> pgs[kPfStages - 1];
+#pragma unroll
+  for (int j = 0; j < kPfStages - 1; ++j) {
+    const ItemPos& q = j < nitems ? pos[j] : pos[0];
+    load_pages<KIND, D>(p, table, q, lp, pgs[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kPfStages - 1; ++j)
+    issue_stage<KIND, D>(p, pos[j], pgs[j], j < nitems, lp, ring + j * F_::STAGE);
+  ItemPos ld = pos[kPfStages - 1];
+  PageSet<KIND, D> pg;
+  if (kPfStages - 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
+
+  for (int j = 0; j < nitems; ++j) {
+    // item j has landed for every wave, and every wave is done with the
+    // decoded copy of item j - 1
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kPfStages - 2) * G_::NL) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int jn = j + kPfStages - 1;
+    const bool live_n = jn < nitems;
+    issue_stage<KIND, D>(p, ld, pg, live_n, lp, ring + (jn % kPfStages) * F_::STAGE);
+    if (live_n) item_next(p, lens, ld);
+    pf_decode<KIND, D>(ring + (j % kPfStages) * F_::STAGE, kdec, vdec);
+    lds_barrier();
+    // this wave's rows: steps i_first .. i_last
+    const int r0 = row0_of(cp.rb);
+    if (r0 < p.R) {
+      const int i_first = r0 / p.G, i_last = (min(r0 + 32, p.R) - 1) / p.G;
+      const int vis = p.causal ? max(0, min(cp.L, cp.L - p.next_n + i_last + 1)) : cp.L;
+      const int flim = cp.L - (p.causal ? p.next_n - 1 - i_first : 0);
+      const int tbase = cp.k * kPfTokens;
+      for (int st = 0; st < kPfTokens / 16; ++st) {
+        const int t0 = tbase + 16 * st;
+        if (t0 >= vis) break;
+        pf_tile<KIND, D, HILO>(kdec, vdec, st, t0, cp.L, t0 + 16 <= flim, c2, w);
+      }
+    }
+    // end of a run inside this range: write the wave's rows of its partial
+    const int b = cp.b, hg = cp.hg, rb = cp.rb;
+    item_next(p, lens, cp);
+    if (j + 1 == nitems || cp.b != b || cp.hg != hg || cp.rb != rb) {
+      const int run = (b * p.nrb + rb) * p.hgroups + hg;
+      if (row0_of(rb) < p.R)
+        write_partial<KIND, D, 2, HILO>(p, part_index(p, run, blockIdx.x, 0, 0), c2, w,
+                                        32 * wv);
+      if (j + 1 < nitems)
+        pf_start_run<KIND, D, HILO>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
+    }
+    if (jn + 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+typedef void (*PrefillFn)(AttnParams, const int32_t*, const int32_t*);
+
+template <int KIND, int D>
+PrefillFn pick_prefill_d(bool hilo) {
+  if constexpr (!PfGeo<KIND, D>::OK) {
+    return nullptr;
+  } else {
+    if (hilo) {
+      if constexpr (KIND == PA_KV_F16) return nullptr;
+      else return attn_prefill_kernel<KIND, D, true>;
+    }
+    return attn_prefill_kernel<KIND, D, false>;
+  }
+}
+
+template <int KIND>
+PrefillFn pick_prefill(int D, bool hilo) {
+  if constexpr (KIND != PA_KV_INT4)
+    if (D == 64) return pick_prefill_d<KIND, 64>(hilo);
+  if (D == 128) return pick_prefill_d<KIND, 128>(hilo);
+  return nullptr;
+}
+
 typedef void (*RingFn)(AttnParams, const int32_t*, const int32_t*, const uint32_t*);
 
 // NWB: the launch bound in waves (4 or 8); a 4-wave workgroup gets twice the
@@ -955,5 +1298,9 @@ RingFn pick_ring_f16(int D, int nw, int RT, bool hilo, int mode);
 RingFn pick_ring_e4m3(int D, int nw, int RT, bool hilo, int mode);
 RingFn pick_ring_int8(int D, int nw, int RT, bool hilo, int mode);
 RingFn pick_ring_int4(int D, int nw, int RT, bool hilo, int mode);
+PrefillFn pick_prefill_f16(int D, bool hilo);
+PrefillFn pick_prefill_e4m3(int D, bool hilo);
+PrefillFn pick_prefill_int8(int D, bool hilo);
+PrefillFn pick_prefill_int4(int D, bool hilo);
 
 }  // namespace pa

@@ -7,4 +7,6 @@ RingFn pick_ring_int4(int D, int nw, int RT, bool hilo, int mode) {
   return pick_d<PA_KV_INT4>(D, nw, RT, hilo, mode);
 }
 
+PrefillFn pick_prefill_int4(int D, bool hilo) { return pick_prefill<PA_KV_INT4>(D, hilo); }
+
 }  // namespace pa

@@ -42,10 +42,25 @@ def prefill_cases():
         W.attn_case("pf_e4m3_noncausal_n40", 3107, B=2, next_n=40, Hq=4, Hkv=2, D=64, bs=16,
                     lens=[90, 45], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR,
                     causal=False),
+        # 128 rows or more per KV head: the prefill layout (256-row groups, one
+        # head per workgroup, stages decoded once into LDS)
+        W.attn_case("pg_int8_perchan_n32_g8", 3108, B=2, next_n=32, Hq=16, Hkv=2, D=128, bs=32,
+                    lens=[700, 20], kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_CHANNEL,
+                    q_dist=(-100.0, 100.0), zero_k_channel_frac=0.1,
+                    v_scale_range=(1e-2, 65504.0 / 127)),
+        W.attn_case("pg_int4_n40_g4", 3109, B=3, next_n=40, Hq=8, Hkv=2, D=128, bs=32,
+                    lens=[260, 19, 45], kv_kind=W.KV_INT4, scale_mode=W.SCALE_PER_TENSOR),
+        W.attn_case("pg_f16_d64_n75_g4", 3110, B=2, next_n=75, Hq=8, Hkv=2, D=64, bs=16,
+                    lens=[500, 80], kv_kind=W.KV_F16, scale_mode=W.SCALE_NONE),
+        W.attn_case("pg_e4m3_d64_noncausal_n64", 3111, B=2, next_n=64, Hq=4, Hkv=2, D=64, bs=16,
+                    lens=[90, 130], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR,
+                    causal=False),
+        W.attn_case("pg_e4m3_n128_g1", 3112, B=3, next_n=128, Hq=4, Hkv=4, D=128, bs=32,
+                    lens=[1000, 128, 3], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR),
     ]
 
 
-@pytest.mark.parametrize("idx", range(7))
+@pytest.mark.parametrize("idx", range(12))
 def test_prefill_small_parity(pa, idx):
     case = prefill_cases()[idx]
     say(f"prefill parity {case.name} B={case.batch} next_n={case.next_n} "
@@ -62,7 +77,7 @@ def test_prefill_small_parity(pa, idx):
                     assert np.all(got[b, i].view(np.uint16) == 0)
 
 
-@pytest.mark.parametrize("idx", [0, 1])
+@pytest.mark.parametrize("idx", [0, 1, 7, 9])
 def test_prefill_relocation_bit_identical(pa, idx):
     case = prefill_cases()[idx]
     say(f"prefill relocation {case.name}")
