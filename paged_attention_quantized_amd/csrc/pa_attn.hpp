@@ -1035,51 +1035,85 @@ __device__ __forceinline__ void pf_start_run(const AttnParams& p, int b, int row
   }
 }
 
-// One 16-token sub-tile (stage tokens 16 st ..) for the wave's 32 rows from
-// the decoded stage. full: every row sees all 16 tokens.
+// Softmax step over a pair of 16-token tiles (sa: tokens 4g + e, sb: tokens
+// 16 + 4g + e of the pair): P of the pair as one k = 32 operand, token order
+// {4g .. 4g + 3, 16 + 4g .. 16 + 4g + 3} in lane group g.
+template <bool MASK>
+__device__ __forceinline__ void pair_softmax(const f4 sa, const f4 sb, uint32_t okbits, float c2,
+                                             float& m_run, float& alpha, bool& rescale, h8& pb) {
+  float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (MASK) mx = (okbits >> e) & 1u ? fmaxf(mx, s[e]) : mx;
+    else mx = fmaxf(mx, s[e]);
+  }
+  mx = rows_max(mx);
+  const float m_old = m_run;
+  const float m_new = fmaxf(m_old, mx);
+  alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - m_new) * c2);
+  rescale |= m_old != m_new && m_old != -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float pf = __builtin_amdgcn_exp2f((s[e] - m_new) * c2);
+    if constexpr (MASK) pf = (okbits >> e) & 1u ? pf : 0.f;
+    pb[e] = (_Float16)pf;
+  }
+  m_run = m_new;
+}
+
+// A pair of 16-token sub-tiles (stage tokens 32 u .. 32 u + 31, sequence
+// tokens t0 ..) for the wave's 32 rows from the decoded stage; P V and the row
+// sums run as k = 32 products over the pair. full: every row sees all 32
+// tokens.
 template <int KIND, int D, bool HILO>
-__device__ __forceinline__ void pf_tile(const uint8_t* kdec, const uint8_t* vdec, int st, int t0,
+__device__ __forceinline__ void pf_pair(const uint8_t* kdec, const uint8_t* vdec, int u, int t0,
                                         int L, bool full, float c2,
                                         WaveState<KIND, D, 2, HILO>& w) {
   using G_ = Geo<KIND, D>;
   using F_ = PfGeo<KIND, D>;
   constexpr int KS = G_::KS, DV = G_::DV;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int tau = 16 * st + n;
-  h8 kop[KS];
+  f4 sacc[2][2];  // [tile][row tile]
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    kop[ks] = *reinterpret_cast<const h8*>(kdec + tau * (D * 2) +
-                                           16 * ((4 * ks + g) ^ (tau & (F_::PPR - 1))));
-  f4 sacc[2];
+  for (int h = 0; h < 2; ++h) {
+    const int tau = 32 * u + 16 * h + n;
+    h8 kop[KS];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks)
+      kop[ks] = *reinterpret_cast<const h8*>(kdec + tau * (D * 2) +
+                                             16 * ((4 * ks + g) ^ (tau & (F_::PPR - 1))));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qa[rt][ks], acc, 0, 0, 0);
-      if constexpr (HILO)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qb[rt][ks], acc, 0, 0, 0);
+    for (int rt = 0; rt < 2; ++rt) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qa[rt][ks], acc, 0, 0, 0);
+        if constexpr (HILO)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qb[rt][ks], acc, 0, 0, 0);
+      }
+      sacc[h][rt] = acc;
     }
-    sacc[rt] = acc;
   }
-  h4 pb[2];
+  h8 pb[2];
   bool rescale = false;
   float alpha[2];
   if (full) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
-      tile_softmax<false>(sacc[rt], 0xFu, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+      pair_softmax<false>(sacc[0][rt], sacc[1][rt], 0xFFu, c2, w.m_run[rt], alpha[rt], rescale,
+                          pb[rt]);
   } else {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       uint32_t okbits = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t0 + 4 * g + e;
+      for (int e = 0; e < 8; ++e) {
+        const int t = t0 + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
         okbits |= (uint32_t)(t < L && t <= w.lim[rt]) << e;
       }
-      tile_softmax<true>(sacc[rt], okbits, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+      pair_softmax<true>(sacc[0][rt], sacc[1][rt], okbits, c2, w.m_run[rt], alpha[rt], rescale,
+                         pb[rt]);
     }
   }
   if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
@@ -1090,26 +1124,32 @@ __device__ __forceinline__ void pf_tile(const uint8_t* kdec, const uint8_t* vdec
       w.l_acc[rt] *= alpha[rt];
     }
   }
-  // O^T += V^T P^T: channel row n * DV + q, tokens 4 g .. 4 g + 3. Tokens past
-  // the end have p = 0 and decoded V bytes of real (if stale) codes; a NaN
-  // there is cleared below before it can meet p = 0.
+  // O^T += V^T P^T: channel row n * DV + q, the pair's tokens in P's order.
+  // Decoded V of tokens past the end (tail slots may hold NaN codes) is
+  // cleared by select before it can meet p = 0.
 #pragma unroll
   for (int q = 0; q < DV; ++q) {
     const int ch = n * DV + q;
-    h4 va = *reinterpret_cast<const h4*>(vdec + ch * (kPfTokens * 2) +
-                                          8 * ((4 * st + g) ^ (ch / DV & 15)));
+    const uint8_t* row = vdec + ch * (kPfTokens * 2);
+    const h4 va0 = *reinterpret_cast<const h4*>(row + 8 * ((8 * u + g) ^ (ch / DV & 15)));
+    const h4 va1 = *reinterpret_cast<const h4*>(row + 8 * ((8 * u + 4 + g) ^ (ch / DV & 15)));
+    h8 va = {va0[0], va0[1], va0[2], va0[3], va1[0], va1[1], va1[2], va1[3]};
     if (!full) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) va[e] = t0 + 4 * g + e < L ? va[e] : (_Float16)0.0f;
+      for (int e = 0; e < 8; ++e) {
+        const int t = t0 + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
+        va[e] = t < L ? va[e] : (_Float16)0.0f;
+      }
     }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
-      w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rt], w.o[rt][q], 0, 0, 0);
+      w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rt], w.o[rt][q], 0, 0, 0);
   }
-  const h4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  const h8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                   (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
-    w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb[rt], w.l_acc[rt], 0, 0, 0);
+    w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rt], w.l_acc[rt], 0, 0, 0);
 }
 
 template <int KIND, int D, bool HILO>
@@ -1199,10 +1239,10 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
       const int vis = p.causal ? max(0, min(cp.L, cp.L - p.next_n + i_last + 1)) : cp.L;
       const int flim = cp.L - (p.causal ? p.next_n - 1 - i_first : 0);
       const int tbase = cp.k * kPfTokens;
-      for (int st = 0; st < kPfTokens / 16; ++st) {
-        const int t0 = tbase + 16 * st;
+      for (int u = 0; u < kPfTokens / 32; ++u) {
+        const int t0 = tbase + 32 * u;
         if (t0 >= vis) break;
-        pf_tile<KIND, D, HILO>(kdec, vdec, st, t0, cp.L, t0 + 16 <= flim, c2, w);
+        pf_pair<KIND, D, HILO>(kdec, vdec, u, t0, cp.L, t0 + 32 <= flim, c2, w);
       }
     }
     // end of a run inside this range: write the wave's rows of its partial
