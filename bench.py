@@ -425,7 +425,10 @@ def main():
         dtype = "f16xf16->f32"
     else:
         r = bench_attn(args, torch, pa, hip, case)
-        tag = "attn_ring_" + args.workload
+        # the dominant kernel: the prefill layout from 128 query rows per KV head
+        rows = case.next_n * case.num_q_heads // case.num_kv_heads
+        tag = ("attn_prefill_" if rows >= 128 and case.head_dim <= 128 else "attn_ring_") + \
+            args.workload
         config = {"workload": args.workload, "batch": case.batch, "next_n": case.next_n,
                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
                   "head_dim": case.head_dim, "block_size": case.block_size,

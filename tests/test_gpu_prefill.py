@@ -57,10 +57,18 @@ def prefill_cases():
                     causal=False),
         W.attn_case("pg_e4m3_n128_g1", 3112, B=3, next_n=128, Hq=4, Hkv=4, D=128, bs=32,
                     lens=[1000, 128, 3], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR),
+        # one step's 64 heads span two waves; 5 steps = 320 rows = 2 groups
+        W.attn_case("pg_e4m3_g64_n5", 3113, B=2, next_n=5, Hq=64, Hkv=1, D=128, bs=16,
+                    lens=[333, 4], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR),
+        # INT8 per-channel at head_dim 64, 3 groups with a ragged last one
+        W.attn_case("pg_int8_perchan_d64_n100_g6", 3114, B=2, next_n=100, Hq=12, Hkv=2, D=64,
+                    bs=32, lens=[400, 150], kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_CHANNEL,
+                    q_dist=(-100.0, 100.0), zero_k_channel_frac=0.1,
+                    v_scale_range=(1e-2, 65504.0 / 127)),
     ]
 
 
-@pytest.mark.parametrize("idx", range(12))
+@pytest.mark.parametrize("idx", range(14))
 def test_prefill_small_parity(pa, idx):
     case = prefill_cases()[idx]
     say(f"prefill parity {case.name} B={case.batch} next_n={case.next_n} "
