@@ -108,13 +108,15 @@ def _poison_byte_pattern(kind: int, n: int, rng) -> np.ndarray:
 def attn_case(name, seed, *, B, next_n, Hq, Hkv, D, bs, lens, kv_kind, scale_mode,
               q_dist="normal", causal=True, num_blocks=None, max_blocks=None,
               max_context_len=None, zero_k_channel_frac=0.0, k_scale_range=(1e-2, 1e3),
-              v_scale_range=(1e-2, 1e3), poison=True) -> AttnCase:
+              v_scale_range=(1e-2, 1e3), pt_scale_range=(0.01, 2.0), poison=True) -> AttnCase:
     """Build one paged-attention input.
 
     Physical ids are a random permutation of 1..num_blocks-1 handed out in
     logical order; block 0 is the null block. Unused pages hold random bytes.
     The null block and the tail slots past each sequence's length hold NaN
-    bytes (poison=True), so a kernel that reads them shows it.
+    bytes (poison=True), so a kernel that reads them shows it. INT codes are
+    uniform; a per-tensor INT scale is uniform in pt_scale_range (per-channel
+    ones log-uniform in k_scale_range / v_scale_range).
     """
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int64)
@@ -187,8 +189,8 @@ def attn_case(name, seed, *, B, next_n, Hq, Hkv, D, bs, lens, kv_kind, scale_mod
             lo, hi = v_scale_range
             v_scale = np.exp(rng.uniform(math.log(lo), math.log(hi), (Hkv, D))).astype(np.float32)
         elif scale_mode == SCALE_PER_TENSOR:
-            k_scale = np.array([rng.uniform(0.01, 2.0)], np.float32)
-            v_scale = np.array([rng.uniform(0.01, 2.0)], np.float32)
+            k_scale = np.array([rng.uniform(*pt_scale_range)], np.float32)
+            v_scale = np.array([rng.uniform(*pt_scale_range)], np.float32)
         if kv_kind == KV_INT8:
             kc = kcodes.view(np.uint8)
             vc = vcodes.view(np.uint8)
