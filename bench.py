@@ -2,8 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one paged_attn_fwd call (planner, split-KV attention, merge) over the
-whole batch of the workload, inputs resident in HBM. The default workload is
+A step is one call of the workload's entry point over its whole batch, inputs
+resident in HBM: paged_attn_fwd (attention kernel and split merge),
+paged_attn_sparse (union planner, attention, merge), paged_mqa_logits or
+kv_insert_mxfp4. The default workload is
 FP8 E4M3 paged decode (batch 64, 32 query / 8 KV heads, head_dim 128,
 block 16, context lengths uniform in [512, 4096], seed 1001). KV pools are
 replicated and rotated so consecutive steps do not hit the 256 MB Infinity

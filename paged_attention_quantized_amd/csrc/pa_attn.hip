@@ -40,6 +40,19 @@
 // its (m, l, c) and unnormalized O as a partial; the merge kernel combines the
 // partials of a (sequence, KV head) in workgroup order, then sub-tile order,
 // and applies v_scale / l.
+//
+// Query rows. Up to 32 rows per KV head (next_n x q heads per KV head) sit in
+// one or two 16-row MFMA tiles of every wave. More rows are cut into row
+// blocks, each a run of its own on the cost line that walks only the tokens
+// its last row can see: blocks of 32 rows in the ring kernel, or, from 128
+// rows where it fits, 256-row groups in the prefill kernel, whose 8 waves are
+// the 8 row blocks of one KV head sharing each stage decoded once into fp16.
+//
+// Selection-driven sparse attention. A planner kernel turns each sequence's
+// selected token ids into a union of logical pages in ascending order with
+// one token mask per query row; the ring kernel then walks that plan as its
+// block table, one page per item, and keeps for each row exactly the tokens
+// its mask selects [RELOC] [NULLPAD].
 #include <math.h>
 
 #include "pa_attn.hpp"
