@@ -55,6 +55,8 @@
 // its mask selects [RELOC] [NULLPAD].
 #include <math.h>
 
+#include <atomic>
+
 #include "pa_attn.hpp"
 #include "pa_host.hpp"
 
@@ -295,19 +297,20 @@ int ilog2(int x) {  // x is a power of two
   return r;
 }
 
-// Compute units of the current device (the persistent grid size), cached.
+// Compute units of the current device (the persistent grid size), cached per
+// device; threads may race to fill an entry, all with the same value.
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 PrefillFn pick_prefill_fn(int kind, int D, bool hilo) {
