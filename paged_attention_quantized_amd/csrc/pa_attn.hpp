@@ -863,9 +863,19 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
         for (int k = 0; k < kSparseRows; ++k) m = i == k ? mc[k] : m;
         rm[rt] = r < p.rpb ? m : 0u;  // one row block in this mode
       }
-      compute_tile<KIND, D, RT, HILO, true>(ring + (j % kStages) * stage_bytes, to, t0, cp.L,
-                                            false, c2, w, rm, mc[0] | mc[1] | mc[2] | mc[3],
-                                            16 * st);
+      // this sub-tile's tokens: skipped when no row selected any, unmasked
+      // when every row selected all (wave-uniform: the masks are scalar)
+      uint32_t any = 0u, all = ~0u;
+#pragma unroll
+      for (int k = 0; k < kSparseRows; ++k) {
+        any |= mc[k];
+        all &= k < p.next_n ? mc[k] : ~0u;
+      }
+      const uint32_t sub_any = (any >> (16 * st)) & 0xFFFFu;
+      const uint32_t sub_all = (all >> (16 * st)) & 0xFFFFu;
+      if (sub_any != 0u)
+        compute_tile<KIND, D, RT, HILO, true>(ring + (j % kStages) * stage_bytes, to, t0, cp.L,
+                                              sub_all == 0xFFFFu, c2, w, rm, any, 16 * st);
     } else if (t0 < run_len(p, cp.L, cp.rb)) {
       // full: the block's first row (step first_step) sees all 16 tokens
       compute_tile<KIND, D, RT, HILO>(

@@ -192,3 +192,49 @@ def test_full_fp8_sparse_verify(pa):
     say(f"{case.name}: sampled max err/tol = {r:.3f}")
     other = run_sparse(pa, W.relocate(case, 21), sel)
     assert np.array_equal(other.view(np.uint16), got.view(np.uint16))
+
+
+def clustered_selection(case, seed):
+    """Selections made of spans, as a clustered top-k gives them: a head span
+    every row selects (whole 16-token sub-tiles), a span only some rows select,
+    and for each row its own recent tokens; pages whose second half nobody
+    selects and sub-tiles every row selects in full both occur."""
+    rng = np.random.default_rng(seed)
+    B, N = case.batch, case.next_n
+    rows = []
+    for b in range(B):
+        L = int(case.context_lens[b])
+        per = []
+        for i in range(N):
+            ids = set(range(min(L, 48)))                       # shared head: 3 full sub-tiles
+            if L > 200 and i % 2 == 0:
+                ids |= set(range(128, 144))                    # half a 32-token page, some rows
+            a = int(rng.integers(0, max(1, L - 20)))
+            ids |= set(range(a, min(L, a + int(rng.integers(1, 20)))))  # a short private span
+            ids |= set(range(max(0, L - 8 - i), L))            # the row's own recent tokens
+            per.append(sorted(ids))
+        rows.append(per)
+    topk = max(len(r) for per in rows for r in per)
+    sel = np.full((B, N, topk), -1, np.int32)
+    for b in range(B):
+        for i in range(N):
+            r = np.array(rows[b][i], np.int32)
+            rng.shuffle(r)
+            sel[b, i, :r.size] = r
+    return sel
+
+
+@pytest.mark.parametrize("kind,bs", [(W.KV_E4M3, 32), (W.KV_F16, 16), (W.KV_E4M3, 16)])
+def test_sparse_clustered_selection(pa, kind, bs):
+    """Sub-tiles no row selected are skipped and sub-tiles every row selected
+    run unmasked: the result still equals the oracle, and a relocation of the
+    pages leaves it bit-identical."""
+    case = W.attn_case(f"sp_cluster_{kind}_{bs}", 2301 + bs, B=3, next_n=4, Hq=16, Hkv=2,
+                       D=128, bs=bs, lens=[600, 260, 30], kv_kind=kind,
+                       scale_mode=W.SCALE_NONE if kind == W.KV_F16 else W.SCALE_PER_TENSOR)
+    sel = clustered_selection(case, 2400 + bs)
+    say(f"sparse clustered {case.name} topk={sel.shape[2]}")
+    got = run_sparse(pa, case, sel)
+    compare_attn(got, oracle_sparse(case, sel), case.name)
+    moved = run_sparse(pa, W.relocate(case, 77), sel)
+    assert np.array_equal(moved.view(np.uint16), got.view(np.uint16))
