@@ -796,10 +796,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   TileOffs<KIND, D> to;
   make_tile_offs<KIND, D>(p, st, hl, to);
 
-  // Q' of the first run is loaded before the ring starts, so waiting for it
-  // never waits for ring loads.
   WaveState<KIND, D, RT, HILO> w;
-  start_run<KIND, D, RT, HILO>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
 
   // ---- ring prologue: kStages - 1 items in flight; the block-table loads of
   // all of them (and of the next one) are issued before any is waited for ----
@@ -832,6 +829,10 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   ItemPos ld = pos[kStages - 1];
   PageSet<KIND, D> pg;
   if (kStages - 1 < nitems) load_pages<KIND, D, SPARSE>(p, table, ld, lp, pg);
+  // Q' of the first run: its loads follow the ring's first stages, so the
+  // ring does not wait for them (the conversion waits for both; the first
+  // compute needs the first stage anyway)
+  start_run<KIND, D, RT, HILO>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
   // SPARSE: row masks of the item being computed (mc) and of the next (mn),
   // loaded one iteration ahead; mp is the position of mn
   uint32_t mc[kSparseRows] = {0u, 0u, 0u, 0u}, mn[kSparseRows] = {0u, 0u, 0u, 0u};
