@@ -25,6 +25,10 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs even where one wave per SIMD would
+    # allow AGPRs: the compiler's AGPR form copies every accumulator out to
+    # VGPRs (and back) around each rescale and run-end check
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -405,6 +405,11 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   sh->ts = ts;
   sh->nsub = ts / 16;
   sh->nw = hpu * sh->nsub;
+  // a wave's ring loads of an item touch at most two pages (the kernel looks
+  // up two): with two or more waves they span 32 / hpu <= 2 * bs tokens, and a
+  // single wave holds a whole item, so the item must fit two pages
+  if (sh->nw == 1 && ts > 2 * a->block_size)
+    return fail(PA_ERR_UNSUPPORTED, "paged_attn: item spans more than two pages");
   sh->nwg = device_cus();
   sh->pages_max = (int)ceil_div(a->max_context_len > 0 ? a->max_context_len : 1, a->block_size);
   sh->entries_per_seq = (int)round_up(sh->pages_max, 8);
@@ -476,7 +481,7 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   return p;
 }
 
-RingFn pick_ring(int kind, int D, int nw, int RT, bool hilo, int mode) {
+RingFn pick_ring(int kind, int D, int nw, int RT, int hilo, int mode) {
   switch (kind) {
     case PA_KV_F16: return pick_ring_f16(D, nw, RT, hilo, mode);
     case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, hilo, mode);
@@ -496,7 +501,10 @@ pa_status launch_attn(const pa_attn_args* a, const Shape& sh, void* workspace, h
     launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * kPfWaves), s, p, a->block_table,
                  a->context_lens);
   } else {
-    RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, hilo,
+    // per-channel K scales: Q' hi/lo parts packed into one operand when a KV
+    // head has at most 8 query rows
+    const int qf = !hilo ? kQPlain : (sh.nrb == 1 && sh.RT == 1 && sh.R <= 8) ? kQPacked : kQSplit;
+    RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, qf,
                           sh.nrb > 1 ? kModeRows : kModeDense);
     if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
     launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), s, p, a->block_table,
@@ -592,7 +600,7 @@ extern "C" pa_status paged_attn_sparse(const pa_attn_args* a, const int32_t* sel
                 workspace_bytes);
   if (a->batch == 0) return PA_OK;
   if (topk > 0 && !sel) return fail(PA_ERR_INVALID_ARG, "paged_attn_sparse: sel is NULL");
-  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, false, kModeSparse);
+  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, kQPlain, kModeSparse);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: no kernel for this kind/shape");
   char* base = (char*)workspace + sh.ml_bytes + sh.o_bytes + sh.seq_bytes;
   int32_t* entries = (int32_t*)base;

@@ -17,6 +17,16 @@ constexpr int kMaxNextN = 4096;        // query steps per sequence
 constexpr int kMaxRows = 8192;         // query rows per KV head (next_n * q heads per KV head)
 constexpr int kRunCost = 2;            // work split: items a run start costs (q reload, partial)
 
+// Q' formats of the ring kernel. Per-tensor scales: Q' is q in fp16 (kQPlain).
+// Per-channel K scales: Q' = q * k_scale / max|k_scale| in fp32, split into an
+// fp16 high part and an fp16 remainder, so the folded scale keeps ~22 bits.
+// kQSplit: the parts are two B operands, each summed by its own MFMA.
+// kQPacked (at most 8 query rows per KV head): one B operand carries the high
+// parts of rows 0-7 in columns 0-7 and the remainders in columns 8-15; a
+// rotation by 8 lanes inside each 16-lane row adds the two halves, so one MFMA
+// per k-step does the work of two and the remainder needs no registers.
+constexpr int kQPlain = 0, kQSplit = 1, kQPacked = 2;
+
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 struct AttnParams {
@@ -51,6 +61,10 @@ struct AttnParams {
 };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uni64(uint64_t x) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32);
+}
 
 // items of one sequence for one head group
 __device__ __forceinline__ int seq_stages(const AttnParams& p, int L) {
@@ -177,25 +191,30 @@ struct Geo {
 // asm sets M0 itself; nothing else in these kernels uses M0.
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, const uint8_t* lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  // the base is uniform by construction; saying so keeps it in SGPRs
+  const uint64_t sb = uni64((uint64_t)(uintptr_t)sbase);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff),
-               "s"(sbase)
+               "s"(sb)
                : "memory");
 }
 
 // Per-thread constants of the ring loads. Load l of wave wv covers stage pieces
-// [(l*nw + wv)*64, +64): one plane, and whole rows of tpi = 1024 / (hpu*RB)
-// consecutive tokens starting at tau0 (tpi divides ts and bs, so the 1 KiB a
-// load covers never crosses a page). voff is the lane's byte offset from the
-// row block of token tau0, head 0 of the group; tau0 and plane are uniform.
+// [(wv*NL + l)*64, +64): whole rows of tpi = 1024 / (hpu*RB) consecutive
+// tokens of one plane (tpi divides ts and bs, so the 1 KiB a load covers never
+// crosses a page). A wave's NL loads are consecutive pieces: with nw >= 2 they
+// lie in one plane and span 32 / hpu tokens, so they touch at most two pages
+// of the item (one when bs >= 32 / hpu); with nw = 1 (one page per item) the
+// first half reads the K plane and the second half the V plane of that page.
+// voff is the lane's byte offset from the start of its page, minus the item's
+// offset inside the page (toff rows, when a page holds several items) and the
+// head group's offset; both are added per item as scalars.
 template <int KIND, int D>
 struct LoadPlan {
   uint32_t voff[Geo<KIND, D>::NL];
-  // uniform per wave: tau0 | plane << 8 | pi << 9, pi = page of the item the
-  // load reads (0 when a page holds the whole item)
-  int meta[Geo<KIND, D>::NL];
-  __device__ int tau0(int l) const { return meta[l] & 255; }
-  __device__ int plane(int l) const { return (meta[l] >> 8) & 1; }
-  __device__ int pi(int l) const { return meta[l] >> 9; }
+  int vplane;     // bit l: load l reads the V plane (uniform)
+  int second;     // bit l: load l reads the wave's second page (uniform)
+  int pi0, pi1;   // item-relative index of the first and second page (uniform)
+  bool one_base;  // every load reads the first page, all in one plane (uniform)
 };
 
 template <int KIND, int D>
@@ -204,9 +223,15 @@ __device__ __forceinline__ void make_load_plan(const AttnParams& p, LoadPlan<KIN
   const int lane = threadIdx.x & 63, wv = uni(threadIdx.x >> 6);
   const int plane_pieces = (p.ts * G_::CPR) << p.lhpu;
   const uint32_t tok_stride = (uint32_t)p.Hkv * G_::RB;
+  // items start on a page boundary when ts >= bs and inside one page otherwise
+  const bool paged = p.ts >= (1 << p.lbs);
+  lp.vplane = 0;
+  lp.second = 0;
+  lp.pi0 = 0;
+  lp.pi1 = 0;
 #pragma unroll
   for (int l = 0; l < G_::NL; ++l) {
-    const int cb = (l * p.nw + wv) * 64;                 // first piece of the load (uniform)
+    const int cb = (wv * G_::NL + l) * 64;               // first piece of the load (uniform)
     const int plane = cb >= plane_pieces ? 1 : 0;
     const int ccb = cb - plane * plane_pieces;
     const int tau0 = (ccb / G_::CPR) >> p.lhpu;
@@ -214,79 +239,95 @@ __device__ __forceinline__ void make_load_plan(const AttnParams& p, LoadPlan<KIN
     const int row = cc / G_::CPR, pos = cc % G_::CPR;
     const int tau = row >> p.lhpu, hl = row & ((1 << p.lhpu) - 1);
     const int j = pos ^ (tau & (G_::CPR - 1));
-    lp.voff[l] = (uint32_t)(tau - tau0) * tok_stride + (uint32_t)hl * G_::RB + 16u * j;
-    // items start on a page boundary when ts >= bs and inside one page otherwise
-    const int pi = p.ts >= (1 << p.lbs) ? tau0 >> p.lbs : 0;
-    lp.meta[l] = tau0 | (plane << 8) | (pi << 9);
+    const int pi = paged ? tau0 >> p.lbs : 0;
+    const int slot = paged ? tau & ((1 << p.lbs) - 1) : tau;  // token row inside the page
+    lp.voff[l] = (uint32_t)slot * tok_stride + (uint32_t)hl * G_::RB + 16u * j;
+    lp.vplane |= plane << l;
+    if (l == 0) lp.pi0 = pi;
+    if (pi != lp.pi0) {
+      lp.pi1 = pi;
+      lp.second |= 1 << l;
+    }
   }
+  lp.one_base = lp.second == 0 && (lp.vplane == 0 || lp.vplane == (1 << G_::NL) - 1);
 }
 
-// The page each ring load of an item reads, looked up one loop iteration
+// The two pages a wave's loads of an item read, looked up one loop iteration
 // before the loads are issued (scalar loads; the wait for them falls on the
 // next iteration's issue, not on the compute in between). A page index past
 // the sequence's last page is clamped to it: such a page only feeds masked
 // tokens.
-template <int KIND, int D>
 struct PageSet {
-  uint32_t phys[Geo<KIND, D>::NL];  // block ids are >= 0: zero-extended, no use right after the load
+  uint32_t phys0, phys1;  // block ids are >= 0: zero-extended, no use right after the load
 };
 
 template <int KIND, int D, bool SPARSE = false>
 __device__ __forceinline__ void load_pages(const AttnParams& p, const int32_t* __restrict__ table,
                                            const ItemPos& it, const LoadPlan<KIND, D>& lp,
-                                           PageSet<KIND, D>& pg) {
+                                           PageSet& pg) {
   if constexpr (SPARSE) {
     // an item is one plan entry (one page): every load of it reads that page
     const uint32_t phys = (uint32_t)p.sp_entries[2 * ((size_t)it.b * p.sp_cap + it.k)];
-#pragma unroll
-    for (int l = 0; l < Geo<KIND, D>::NL; ++l) pg.phys[l] = phys;
+    pg.phys0 = phys;
+    pg.phys1 = phys;
     return;
   }
   const int blk0 = (it.k << p.lts) >> p.lbs;
   const int last_blk = (it.L - 1) >> p.lbs;
   const int32_t* table_row = table + (size_t)it.b * p.max_blocks;
-#pragma unroll
-  for (int l = 0; l < Geo<KIND, D>::NL; ++l)
-    pg.phys[l] = (uint32_t)table_row[min(blk0 + lp.pi(l), last_blk)];
+  pg.phys0 = (uint32_t)table_row[min(blk0 + lp.pi0, last_blk)];
+  pg.phys1 = (uint32_t)table_row[min(blk0 + lp.pi1, last_blk)];
 }
 
 // Issue the ring loads of one item into `slot`. Every thread issues exactly NL
 // loads whether the item is live or not. Stage layout: K plane then V plane,
 // each [TS tokens][HPU heads][CPR pieces]; piece j of row (tau, hl) is stored
 // at position j ^ (tau & (CPR - 1)). Each load's address is a scalar page base
-// plus the lane's constant offset.
+// plus the lane's constant offset; the page bases are formed once per item in
+// 32 x 32 -> 64-bit products.
 template <int KIND, int D>
 __device__ __forceinline__ void issue_stage(const AttnParams& p, const ItemPos& it,
-                                            const PageSet<KIND, D>& pg, bool live,
+                                            const PageSet& pg, bool live,
                                             const LoadPlan<KIND, D>& lp, uint8_t* slot) {
   using G_ = Geo<KIND, D>;
   const int wv = uni(threadIdx.x >> 6);
+  uint8_t* dst = slot + wv * G_::NL * 1024;
   if (live) {
-    const int toff = (it.k << p.lts) & ((1 << p.lbs) - 1);  // 0 unless a page holds several items
-    const size_t tok_stride = (size_t)p.Hkv * G_::RB;
-    const size_t page_stride = tok_stride << p.lbs;
-    const size_t head_off = ((size_t)it.hg * G_::RB) << p.lhpu;
+    const uint32_t toff = (uint32_t)(it.k << p.lts) & ((1u << p.lbs) - 1u);  // 0 unless a page holds several items
+    const uint32_t tok_stride = (uint32_t)p.Hkv * G_::RB;
+    const uint32_t page_stride = tok_stride << p.lbs;
+    const uint32_t item_off = toff * tok_stride + (((uint32_t)it.hg * G_::RB) << p.lhpu);
+    uint64_t off0 = (uint64_t)pg.phys0 * page_stride + item_off;
+    if (lp.one_base) {
+      // the usual case: one page and one plane for all of the wave's loads
+      const uint8_t* base = (lp.vplane ? p.v_cache : p.k_cache) + off0;
 #pragma unroll
-    for (int l = 0; l < G_::NL; ++l) {
-      const int sl = (toff + lp.tau0(l)) & ((1 << p.lbs) - 1);
-      const uint8_t* sbase = (lp.plane(l) ? p.v_cache : p.k_cache) + (size_t)pg.phys[l] * page_stride +
-                             (size_t)sl * tok_stride + head_off;
-      dma16(sbase, lp.voff[l], slot + (l * p.nw + wv) * 1024);
+      for (int l = 0; l < G_::NL; ++l) dma16(base, lp.voff[l], dst + l * 1024);
+    } else {
+      // both products formed once (as uniform values): otherwise the compiler
+      // selects the page id per load and redoes the multiply
+      off0 = uni64(off0);
+      const uint64_t off1 = uni64((uint64_t)pg.phys1 * page_stride + item_off);
+#pragma unroll
+      for (int l = 0; l < G_::NL; ++l) {
+        const uint8_t* base = ((lp.vplane >> l) & 1) ? p.v_cache : p.k_cache;
+        dma16(base + (((lp.second >> l) & 1) ? off1 : off0), lp.voff[l], dst + l * 1024);
+      }
     }
   } else {
     // past the end of the range: the same number of loads, of 16 readable
     // bytes, into a slot nobody reads
     const uint8_t* sbase = reinterpret_cast<const uint8_t*>(p.q);
 #pragma unroll
-    for (int l = 0; l < G_::NL; ++l) dma16(sbase, 0u, slot + (l * p.nw + wv) * 1024);
+    for (int l = 0; l < G_::NL; ++l) dma16(sbase, 0u, dst + l * 1024);
   }
 }
 
 // Softmax state and Q' operands of one wave.
-template <int KIND, int D, int RT, bool HILO>
+template <int KIND, int D, int RT, int HILO>
 struct WaveState {
   h8 qa[RT][Geo<KIND, D>::KS];
-  h8 qb[RT][HILO ? Geo<KIND, D>::KS : 1];
+  h8 qb[RT][HILO == kQSplit ? Geo<KIND, D>::KS : 1];
   f4 o[RT][Geo<KIND, D>::DV];
   float m_run[RT];
   f4 l_acc[RT];  // row sums of P, accumulated by the matrix cores (all 4 lanes of a row equal)
@@ -295,7 +336,7 @@ struct WaveState {
 
 // Load Q' of (sequence b, row block rb, KV head hk) and reset the softmax
 // state. Local row 16 rt + n is query row rb * rpb + 16 rt + n.
-template <int KIND, int D, int RT, bool HILO>
+template <int KIND, int D, int RT, int HILO>
 __device__ __forceinline__ void start_run(const AttnParams& p, int b, int rb, int hk, int L,
                                           float inv_m, float sgn,
                                           WaveState<KIND, D, RT, HILO>& w) {
@@ -303,7 +344,8 @@ __device__ __forceinline__ void start_run(const AttnParams& p, int b, int rb, in
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int rl = 16 * rt + n, r = rb * p.rpb + rl;
+    // kQPacked: column n holds row n & 7 (its high part for n < 8)
+    const int rl = HILO == kQPacked ? (n & 7) : 16 * rt + n, r = rb * p.rpb + rl;
     const bool rv = rl < p.rpb && r < p.R;
     const int i = r / p.G, hg = r % p.G;
     const _Float16* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
@@ -320,8 +362,13 @@ __device__ __forceinline__ void start_run(const AttnParams& p, int b, int rb, in
         if constexpr (HILO) {
           const float xf = x * (p.k_scale[hk * D + d] * inv_m) * sgn;
           const _Float16 hi = (_Float16)xf;
-          w.qa[rt][ks][e] = hi;
-          w.qb[rt][ks][e] = (_Float16)(xf - (float)hi);
+          const _Float16 lo = (_Float16)(xf - (float)hi);
+          if constexpr (HILO == kQPacked) {
+            w.qa[rt][ks][e] = n < 8 ? hi : lo;
+          } else {
+            w.qa[rt][ks][e] = hi;
+            w.qb[rt][ks][e] = lo;
+          }
         } else {
           w.qa[rt][ks][e] = (_Float16)(x * sgn);
         }
@@ -437,7 +484,7 @@ __device__ __forceinline__ void tile_softmax(const f4 s, uint32_t okbits, float 
 // sub-tile is valid for the lane's row when bit tin + 4g + e of rmask[rt] is
 // set (tin = the sub-tile's first token in its page), and its V codes are
 // kept when that bit is set in umask (some row selected it).
-template <int KIND, int D, int RT, bool HILO, bool SPARSE = false>
+template <int KIND, int D, int RT, int HILO, bool SPARSE = false>
 __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs<KIND, D>& to,
                                              int t0, int L, bool full, float c2,
                                              WaveState<KIND, D, RT, HILO>& w,
@@ -504,8 +551,16 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qa[rt][ks], acc, 0, 0, 0);
-      if constexpr (HILO)
+      if constexpr (HILO == kQSplit)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qb[rt][ks], acc, 0, 0, 0);
+    }
+    if constexpr (HILO == kQPacked) {
+      // column n + high part of its row, from column (n + 8) mod 16 (row_ror:8);
+      // both halves of the row end up with the same sum
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[e] += __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(acc[e]), 0x128, 0xF, 0xF, false));
     }
     sacc[rt] = acc;
   }
@@ -574,7 +629,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
 // Exchange of a wave's softmax state through LDS, in the MFMA register layout
 // (lane-major), so the receiving wave of the same head combines element-wise:
 // o as [rt][q][lane] f4, then m and l as [rt][lane] floats.
-template <int KIND, int D, int RT, bool HILO>
+template <int KIND, int D, int RT, int HILO>
 __device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, HILO>& w, float* xbuf) {
   constexpr int DV = Geo<KIND, D>::DV;
   const int lane = threadIdx.x & 63;
@@ -589,7 +644,7 @@ __device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, HILO>& w, f
 }
 
 // Combine the state in xbuf into w (w first, then xbuf: a fixed order).
-template <int KIND, int D, int RT, bool HILO>
+template <int KIND, int D, int RT, int HILO>
 __device__ __forceinline__ void xch_merge(WaveState<KIND, D, RT, HILO>& w, const float* xbuf,
                                           float c2) {
   constexpr int DV = Geo<KIND, D>::DV;
@@ -629,7 +684,7 @@ __device__ __forceinline__ size_t part_index(const AttnParams& p, int r, int w, 
   return ((size_t)(r + w) * p.hpu + hl) * (p.wgmerge ? 1 : p.nsub) + st;
 }
 
-template <int KIND, int D, int RT, bool HILO>
+template <int KIND, int D, int RT, int HILO>
 __device__ __forceinline__ void write_partial(const AttnParams& p, size_t u, float c2,
                                               const WaveState<KIND, D, RT, HILO>& w,
                                               int row0 = 0) {
@@ -737,7 +792,7 @@ enum RingMode { kModeDense = 0, kModeSparse = 1, kModeRows = 2 };
 // MODE kModeSparse: table holds the union plan entries ({physical, logical}
 // per page), lens the per-sequence entry count times block_size, masks the row
 // masks. kModeRows: query rows come in p.nrb blocks of p.rpb rows.
-template <int KIND, int D, int RT, bool HILO, int NWB, int MODE>
+template <int KIND, int D, int RT, int HILO, int NWB, int MODE>
 __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
     const uint32_t* __restrict__ masks) {
@@ -810,7 +865,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   // Unconditional lookups (an item past the range looks up the range's first
   // item instead, which is always valid) let every table load of the
   // prologue be issued before the first wait.
-  PageSet<KIND, D> pgs[kStages - 1];
+  PageSet pgs[kStages - 1];
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j) {
     const bool in = j < nitems;
@@ -827,7 +882,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   for (int j = 0; j < kStages - 1; ++j)
     issue_stage<KIND, D>(p, pos[j], pgs[j], j < nitems, lp, ring + j * stage_bytes);
   ItemPos ld = pos[kStages - 1];
-  PageSet<KIND, D> pg;
+  PageSet pg;
   if (kStages - 1 < nitems) load_pages<KIND, D, SPARSE>(p, table, ld, lp, pg);
   // Q' of the first run: its loads follow the ring's first stages, so the
   // ring does not wait for them (the conversion waits for both; the first
@@ -1218,7 +1273,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
     pos[j] = pos[j - 1];
     if (j - 1 < nitems) item_next(p, lens, pos[j]);
   }
-  PageSet<KIND, D> pgs[kPfStages - 1];
+  PageSet pgs[kPfStages - 1];
 #pragma unroll
   for (int j = 0; j < kPfStages - 1; ++j) {
     const ItemPos& q = j < nitems ? pos[j] : pos[0];
@@ -1228,7 +1283,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
   for (int j = 0; j < kPfStages - 1; ++j)
     issue_stage<KIND, D>(p, pos[j], pgs[j], j < nitems, lp, ring + j * F_::STAGE);
   ItemPos ld = pos[kPfStages - 1];
-  PageSet<KIND, D> pg;
+  PageSet pg;
   if (kPfStages - 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
 
   for (int j = 0; j < nitems; ++j) {
@@ -1302,7 +1357,7 @@ typedef void (*RingFn)(AttnParams, const int32_t*, const int32_t*, const uint32_
 // in row blocks of 32 (kModeRows). The sparse mode exists for FP16 and
 // per-tensor E4M3 caches, up to 32 query rows per KV head.
 template <int KIND, int D, int NWB>
-RingFn pick_rt(int RT, bool hilo, int mode) {
+RingFn pick_rt(int RT, int hilo, int mode) {
   if (RT != 1 && RT != 2) return nullptr;
   if (mode == kModeSparse) {
     if constexpr (KIND == PA_KV_F16 || KIND == PA_KV_E4M3) {
@@ -1313,18 +1368,20 @@ RingFn pick_rt(int RT, bool hilo, int mode) {
     return nullptr;
   }
   if (mode == kModeRows) {
-    if (RT != 2) return nullptr;
+    if (RT != 2 || hilo == kQPacked) return nullptr;
     if (hilo) {
       if constexpr (KIND == PA_KV_F16) return nullptr;
-      else return attn_ring_kernel<KIND, D, 2, true, NWB, kModeRows>;
+      else return attn_ring_kernel<KIND, D, 2, kQSplit, NWB, kModeRows>;
     }
     return attn_ring_kernel<KIND, D, 2, false, NWB, kModeRows>;
   }
   if (hilo) {
     if constexpr (KIND == PA_KV_F16) return nullptr;
     else {
-      if (RT == 1) return attn_ring_kernel<KIND, D, 1, true, NWB, kModeDense>;
-      return attn_ring_kernel<KIND, D, 2, true, NWB, kModeDense>;
+      if (hilo == kQPacked)
+        return RT == 1 ? attn_ring_kernel<KIND, D, 1, kQPacked, NWB, kModeDense> : nullptr;
+      if (RT == 1) return attn_ring_kernel<KIND, D, 1, kQSplit, NWB, kModeDense>;
+      return attn_ring_kernel<KIND, D, 2, kQSplit, NWB, kModeDense>;
     }
   }
   if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, kModeDense>;
@@ -1332,12 +1389,12 @@ RingFn pick_rt(int RT, bool hilo, int mode) {
 }
 
 template <int KIND, int D>
-RingFn pick_nw(int nw, int RT, bool hilo, int mode) {
+RingFn pick_nw(int nw, int RT, int hilo, int mode) {
   return nw <= 4 ? pick_rt<KIND, D, 4>(RT, hilo, mode) : pick_rt<KIND, D, 8>(RT, hilo, mode);
 }
 
 template <int KIND>
-RingFn pick_d(int D, int nw, int RT, bool hilo, int mode) {
+RingFn pick_d(int D, int nw, int RT, int hilo, int mode) {
   if constexpr (KIND != PA_KV_INT4)
     if (D == 64) return pick_nw<KIND, 64>(nw, RT, hilo, mode);
   if (D == 128) return pick_nw<KIND, 128>(nw, RT, hilo, mode);
@@ -1345,10 +1402,10 @@ RingFn pick_d(int D, int nw, int RT, bool hilo, int mode) {
 }
 
 // Ring kernel of one KV kind (each defined in its own translation unit).
-RingFn pick_ring_f16(int D, int nw, int RT, bool hilo, int mode);
-RingFn pick_ring_e4m3(int D, int nw, int RT, bool hilo, int mode);
-RingFn pick_ring_int8(int D, int nw, int RT, bool hilo, int mode);
-RingFn pick_ring_int4(int D, int nw, int RT, bool hilo, int mode);
+RingFn pick_ring_f16(int D, int nw, int RT, int hilo, int mode);
+RingFn pick_ring_e4m3(int D, int nw, int RT, int hilo, int mode);
+RingFn pick_ring_int8(int D, int nw, int RT, int hilo, int mode);
+RingFn pick_ring_int4(int D, int nw, int RT, int hilo, int mode);
 PrefillFn pick_prefill_f16(int D, bool hilo);
 PrefillFn pick_prefill_e4m3(int D, bool hilo);
 PrefillFn pick_prefill_int8(int D, bool hilo);

@@ -3,7 +3,7 @@
 
 namespace pa {
 
-RingFn pick_ring_e4m3(int D, int nw, int RT, bool hilo, int mode) {
+RingFn pick_ring_e4m3(int D, int nw, int RT, int hilo, int mode) {
   return pick_d<PA_KV_E4M3>(D, nw, RT, hilo, mode);
 }
 

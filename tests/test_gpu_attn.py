@@ -250,6 +250,42 @@ def test_split_shapes_relocation(pa, idx):
     assert np.array_equal(got.view(np.uint16), base.view(np.uint16))
 
 
+def perchan_row_cases():
+    """Per-channel K scales at 1 to 16 query rows per KV head: up to 8 rows the
+    kernel packs the high and low fp16 parts of Q' = q * k_scale into the
+    columns of one MFMA operand, from 9 rows it keeps them as two operands.
+    Integer kinds through the workload generator; E4M3 codes with a
+    per-channel K scale set afterwards."""
+    out = []
+    seed = 1700
+    for kind in (W.KV_INT8, W.KV_INT4, W.KV_E4M3):
+        for G, nn, D in ((1, 1, 128), (4, 2, 256), (8, 1, 256), (3, 3, 128), (8, 2, 256),
+                         (16, 1, 128)):
+            seed += 1
+            case = W.attn_case(f"rows_k{kind}_g{G}_n{nn}_d{D}", seed, B=2, next_n=nn, Hq=2 * G,
+                               Hkv=2, D=D, bs=16, lens=[333, 41], kv_kind=kind,
+                               scale_mode=W.SCALE_PER_TENSOR if kind == W.KV_E4M3
+                               else W.SCALE_PER_CHANNEL,
+                               q_dist=(-30.0, 30.0), zero_k_channel_frac=0.1,
+                               v_scale_range=(1e-2, 65504.0 / 127))
+            if kind == W.KV_E4M3:
+                rng = np.random.default_rng(seed)
+                case.k_scale = np.exp(rng.uniform(np.log(1e-3), np.log(0.1), (2, D))).astype(
+                    np.float32)
+                case.k_scale_mode = W.SCALE_PER_CHANNEL
+            out.append(case)
+    return out
+
+
+@pytest.mark.parametrize("idx", range(18))
+def test_perchan_rows_parity(pa, idx):
+    case = perchan_row_cases()[idx]
+    say(f"per-channel rows {case.name}")
+    got = run_attn(pa, case)
+    r = compare_attn(got, oracle_attn(case), case.name)
+    say(f"{case.name}: max err/tol = {r:.3f}")
+
+
 def test_zero_per_channel_k_scale_is_uniform(pa):
     """max|k_scale| = 0: the folded q and the score scale are 0, every visible
     token gets the same weight (the mean of V), and no NaN appears."""
