@@ -72,18 +72,21 @@ struct Kv<PA_KV_INT8> {
 
 // INT4: eight signed nibbles per dword (element k at bits 4k..4k+3). Flipping
 // bit 3 of every nibble maps value v to v + 8 in [0, 15]; nibbles k and k+4 are
-// masked under the fp16 exponent of 1024 and 1032 is subtracted. The pairs come
+// masked under the fp16 exponent of 1024 and 1032 is subtracted. Mask, flip
+// and exponent are one 3-input bitwise op, (s & 0x000F000F) ^ 0x64086408 (the
+// exponent bits are zero after the mask, so the xor sets them). The pairs come
 // out as (e0,e4), (e1,e5), (e2,e6), (e3,e7).
 template <>
 struct Kv<PA_KV_INT4> {
   static constexpr int kBits = 4;
   static constexpr int kPairsPerDword = 4;
   __device__ static void decode(uint32_t w, h2* out) {
-    uint32_t x = w ^ 0x88888888u;
     const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      out[k] = as_h2(((x >> (4 * k)) & 0x000F000Fu) | 0x64006400u) - bias;
+      // truth table 0x6A: (a & b) ^ c, a = the shifted codes, b = mask, c = exponent | flip
+      out[k] = as_h2(__builtin_amdgcn_bitop3_b32(w >> (4 * k), 0x000F000Fu, 0x64086408u, 0x6A)) -
+               bias;
   }
   // slot e of the 8 fp16 values produced from one dword holds element order(e)
   __device__ static constexpr int order(int e) { return (e >> 1) + 4 * (e & 1); }
