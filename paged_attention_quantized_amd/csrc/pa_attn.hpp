@@ -832,20 +832,6 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   cp.hg = uni(xi[2]);
   cp.k = uni(xi[3]);
 
-  // ---- scale constants: fold normalizer for PER_CHANNEL K [FOLD, Approach] ----
-  float qk, inv_m = 0.f;
-  if constexpr (HILO) {
-    float mx = 0.f;
-    for (int i = lane; i < p.Hkv * D; i += 64) mx = fmaxf(mx, fabsf(p.k_scale[i]));
-    mx = wave_max(mx);
-    inv_m = mx > 0.f ? 1.0f / mx : 0.f;
-    qk = p.softmax_scale * mx;
-  } else {
-    qk = p.softmax_scale * ks_tensor;
-  }
-  const float sgn = qk < 0.f ? -1.f : 1.f;
-  const float c2 = fabsf(qk) * kLog2e;
-
   LoadPlan<KIND, D> lp;
   make_load_plan<KIND, D>(p, lp);
   TileOffs<KIND, D> to;
@@ -884,6 +870,33 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   ItemPos ld = pos[kStages - 1];
   PageSet pg;
   if (kStages - 1 < nitems) load_pages<KIND, D, SPARSE>(p, table, ld, lp, pg);
+
+  // ---- scale constants, after the ring's first loads are on their way:
+  // fold normalizer for PER_CHANNEL K [FOLD, Approach], max|k_scale| with 8
+  // loads in flight per lane ----
+  float qk, inv_m = 0.f;
+  if constexpr (HILO) {
+    float mx = 0.f;
+    const int nks = p.Hkv * D;
+    for (int i0 = 0; i0 < nks; i0 += 512) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + 64 * u + lane;
+        v[u] = i < nks ? p.k_scale[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mx = fmaxf(mx, fabsf(v[u]));
+    }
+    mx = wave_max(mx);
+    inv_m = mx > 0.f ? 1.0f / mx : 0.f;
+    qk = p.softmax_scale * mx;
+  } else {
+    qk = p.softmax_scale * ks_tensor;
+  }
+  const float sgn = qk < 0.f ? -1.f : 1.f;
+  const float c2 = fabsf(qk) * kLog2e;
+
   // Q' of the first run: its loads follow the ring's first stages, so the
   // ring does not wait for them (the conversion waits for both; the first
   // compute needs the first stage anyway)
@@ -1244,26 +1257,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
   cp.k = uni(xi[3]);
   __syncthreads();  // xi lives in kdec
 
-  float qk, inv_m = 0.f;
-  if constexpr (HILO) {
-    float mx = 0.f;
-    for (int i = lane; i < p.Hkv * D; i += 64) mx = fmaxf(mx, fabsf(p.k_scale[i]));
-    mx = wave_max(mx);
-    inv_m = mx > 0.f ? 1.0f / mx : 0.f;
-    qk = p.softmax_scale * mx;
-  } else {
-    qk = p.softmax_scale * ks_tensor;
-  }
-  const float sgn = qk < 0.f ? -1.f : 1.f;
-  const float c2 = fabsf(qk) * kLog2e;
-
   LoadPlan<KIND, D> lp;
   make_load_plan<KIND, D>(p, lp);
 
   // rows of this wave inside its run's group, and the steps they span
   auto row0_of = [&](int rb) { return rb * p.rpb + 32 * wv; };
   WaveState<KIND, D, 2, HILO> w;
-  pf_start_run<KIND, D, HILO>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
 
   // ---- prologue: items 0 and 1 in flight, the pages of item 2 looked up ----
   ItemPos pos[kPfStages];
@@ -1285,6 +1284,31 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
   ItemPos ld = pos[kPfStages - 1];
   PageSet pg;
   if (kPfStages - 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
+
+  // scale constants and the first run's Q', behind the ring's first loads
+  float qk, inv_m = 0.f;
+  if constexpr (HILO) {
+    float mx = 0.f;
+    const int nks = p.Hkv * D;
+    for (int i0 = 0; i0 < nks; i0 += 512) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + 64 * u + lane;
+        v[u] = i < nks ? p.k_scale[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mx = fmaxf(mx, fabsf(v[u]));
+    }
+    mx = wave_max(mx);
+    inv_m = mx > 0.f ? 1.0f / mx : 0.f;
+    qk = p.softmax_scale * mx;
+  } else {
+    qk = p.softmax_scale * ks_tensor;
+  }
+  const float sgn = qk < 0.f ? -1.f : 1.f;
+  const float c2 = fabsf(qk) * kLog2e;
+  pf_start_run<KIND, D, HILO>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
 
   for (int j = 0; j < nitems; ++j) {
     // item j has landed for every wave, and every wave is done with the
