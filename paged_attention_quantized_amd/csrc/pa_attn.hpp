@@ -323,6 +323,76 @@ __device__ __forceinline__ void issue_stage(const AttnParams& p, const ItemPos& 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ring kernel loads, one region per wave. Wave (hl, st) computes head hl of
+// the group for tokens [16 st, 16 st + 16) of an item; it also loads exactly
+// those K and V rows into a region of its own, [K: 16 rows][V: 16 rows] of RB
+// bytes, with the 16-byte pieces of row r stored at position j ^ (r & (CPR-1)).
+// No wave reads another wave's region, so a wave waits for its own loads only
+// and the ring needs no barrier per stage. The 16 tokens never cross a page
+// (bs >= 16), so every item costs a wave one block-table lookup.
+template <int KIND, int D>
+struct WaveLoads {
+  uint32_t voff[Geo<KIND, D>::NL];  // loads [0, NL/2) read K rows, the rest V rows
+  int pi;                           // item-relative page of the wave's tokens (uniform)
+};
+
+template <int KIND, int D>
+__device__ __forceinline__ void make_wave_loads(const AttnParams& p, int st, int hl,
+                                                WaveLoads<KIND, D>& wl) {
+  using G_ = Geo<KIND, D>;
+  constexpr int CPR = G_::CPR, RB = G_::RB, NL = G_::NL, HALF = NL / 2, TPR = 1024 / RB;
+  static_assert(NL % 2 == 0 && 16 % TPR == 0 && HALF * TPR == 16, "per-wave load geometry");
+  const int lane = threadIdx.x & 63;
+  const uint32_t tok_stride = (uint32_t)p.Hkv * RB;
+  const bool paged = p.ts >= (1 << p.lbs);  // items start on a page boundary
+  const int t0 = 16 * st;
+  wl.pi = paged ? t0 >> p.lbs : 0;
+  const int slot0 = paged ? t0 & ((1 << p.lbs) - 1) : t0;
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    const int r = (l % HALF) * TPR + lane / CPR, pos = lane % CPR;
+    const int j = pos ^ (r & (CPR - 1));
+    wl.voff[l] = (uint32_t)(slot0 + r) * tok_stride + (uint32_t)hl * RB + 16u * j;
+  }
+}
+
+template <int KIND, int D, bool SPARSE = false>
+__device__ __forceinline__ void load_page_w(const AttnParams& p, const int32_t* __restrict__ table,
+                                            const ItemPos& it, const WaveLoads<KIND, D>& wl,
+                                            PageSet& pg) {
+  if constexpr (SPARSE) {
+    pg.phys0 = (uint32_t)p.sp_entries[2 * ((size_t)it.b * p.sp_cap + it.k)];
+  } else {
+    const int blk0 = (it.k << p.lts) >> p.lbs;
+    const int last_blk = (it.L - 1) >> p.lbs;
+    pg.phys0 = (uint32_t)table[(size_t)it.b * p.max_blocks + min(blk0 + wl.pi, last_blk)];
+  }
+}
+
+// Issue a wave's NL loads of one item into its region `dst` (the same number
+// whether the item is live or not).
+template <int KIND, int D>
+__device__ __forceinline__ void issue_w(const AttnParams& p, const ItemPos& it, const PageSet& pg,
+                                        bool live, const WaveLoads<KIND, D>& wl, uint8_t* dst) {
+  using G_ = Geo<KIND, D>;
+  constexpr int NL = G_::NL;
+  if (live) {
+    const uint32_t toff = (uint32_t)(it.k << p.lts) & ((1u << p.lbs) - 1u);  // 0 unless a page holds several items
+    const uint32_t tok_stride = (uint32_t)p.Hkv * G_::RB;
+    const uint64_t off = (uint64_t)pg.phys0 * (tok_stride << p.lbs) + toff * tok_stride +
+                         (((uint32_t)it.hg * G_::RB) << p.lhpu);
+    const uint8_t* kb = p.k_cache + off;
+    const uint8_t* vb = p.v_cache + off;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) dma16(l < NL / 2 ? kb : vb, wl.voff[l], dst + l * 1024);
+  } else {
+    const uint8_t* sbase = reinterpret_cast<const uint8_t*>(p.q);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) dma16(sbase, 0u, dst + l * 1024);
+  }
+}
+
 // Softmax state and Q' operands of one wave.
 template <int KIND, int D, int RT, int HILO>
 struct WaveState {
@@ -382,9 +452,9 @@ __device__ __forceinline__ void start_run(const AttnParams& p, int b, int rb, in
   }
 }
 
-// LDS byte offsets (within a stage) of the pieces a lane reads in
-// compute_tile: K pieces g + 4j of token 16*st + n, and V bytes
-// [n*VB, n*VB + VB) of tokens 16*st + 4g + e, both for head hl.
+// LDS byte offsets (within a wave's region of a stage) of the pieces a lane
+// reads in compute_tile: K pieces g + 4j of the sub-tile's token n, and V
+// bytes [n*VB, n*VB + VB) of its tokens 4g + e.
 template <int KIND, int D>
 struct TileOffs {
   static constexpr int VP = Geo<KIND, D>::VB >= 16 ? Geo<KIND, D>::VB / 16 : 1;
@@ -392,23 +462,19 @@ struct TileOffs {
   int v[4][VP];
 };
 
+// Offsets inside a wave's own region (see make_wave_loads): K rows 0..15,
+// then V rows 0..15, RB bytes each.
 template <int KIND, int D>
-__device__ __forceinline__ void make_tile_offs(const AttnParams& p, int st, int hl,
-                                               TileOffs<KIND, D>& to) {
+__device__ __forceinline__ void make_tile_offs_w(TileOffs<KIND, D>& to) {
   using G_ = Geo<KIND, D>;
   constexpr int CPR = G_::CPR, RB = G_::RB, VB = G_::VB;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int plane_bytes = (p.ts * RB) << p.lhpu;
-  {
-    const int tau = 16 * st + n;
-    const int row = ((tau << p.lhpu) + hl) * RB;
 #pragma unroll
-    for (int j = 0; j < G_::NJ; ++j) to.k[j] = row + 16 * ((g + 4 * j) ^ (tau & (CPR - 1)));
-  }
+  for (int j = 0; j < G_::NJ; ++j) to.k[j] = n * RB + 16 * ((g + 4 * j) ^ (n & (CPR - 1)));
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int tau = 16 * st + 4 * g + e;
-    const int row = plane_bytes + ((tau << p.lhpu) + hl) * RB;
+    const int tau = 4 * g + e;
+    const int row = 16 * RB + tau * RB;
     const int byte = n * VB;
 #pragma unroll
     for (int pp = 0; pp < TileOffs<KIND, D>::VP; ++pp)
@@ -832,10 +898,12 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   cp.hg = uni(xi[2]);
   cp.k = uni(xi[3]);
 
-  LoadPlan<KIND, D> lp;
-  make_load_plan<KIND, D>(p, lp);
+  WaveLoads<KIND, D> wl;
+  make_wave_loads<KIND, D>(p, st, hl, wl);
   TileOffs<KIND, D> to;
-  make_tile_offs<KIND, D>(p, st, hl, to);
+  make_tile_offs_w<KIND, D>(to);
+  // this wave's region of every ring stage
+  uint8_t* const myring = ring + wv * (32 * G_::RB);
 
   WaveState<KIND, D, RT, HILO> w;
 
@@ -862,14 +930,14 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     q.hg = in ? pos[j].hg : pos[0].hg;
     q.k = in ? pos[j].k : pos[0].k;
     q.rb = in ? pos[j].rb : pos[0].rb;
-    load_pages<KIND, D, SPARSE>(p, table, q, lp, pgs[j]);
+    load_page_w<KIND, D, SPARSE>(p, table, q, wl, pgs[j]);
   }
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j)
-    issue_stage<KIND, D>(p, pos[j], pgs[j], j < nitems, lp, ring + j * stage_bytes);
+    issue_w<KIND, D>(p, pos[j], pgs[j], j < nitems, wl, myring + j * stage_bytes);
   ItemPos ld = pos[kStages - 1];
   PageSet pg;
-  if (kStages - 1 < nitems) load_pages<KIND, D, SPARSE>(p, table, ld, lp, pg);
+  if (kStages - 1 < nitems) load_page_w<KIND, D, SPARSE>(p, table, ld, wl, pg);
 
   // ---- scale constants, after the ring's first loads are on their way:
   // fold normalizer for PER_CHANNEL K [FOLD, Approach], max|k_scale| with 8
@@ -911,13 +979,12 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   }
 
   for (int j = 0; j < nitems; ++j) {
-    // item j has landed for every wave, and every wave is done with item j - 1
+    // this wave's loads of item j have landed (its region is its own: no
+    // barrier), and it is done with item j - 1, whose slot the next loads reuse
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * G_::NL) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
     const int jn = j + kStages - 1;
     const bool live_n = jn < nitems;
-    issue_stage<KIND, D>(p, ld, pg, live_n, lp, ring + (jn % kStages) * stage_bytes);
+    issue_w<KIND, D>(p, ld, pg, live_n, wl, myring + (jn % kStages) * stage_bytes);
     if (live_n) item_next(p, lens, ld);
     const int t0 = (cp.k << p.lts) + 16 * st;
     if constexpr (SPARSE) {
@@ -943,12 +1010,12 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
       const uint32_t sub_any = (any >> (16 * st)) & 0xFFFFu;
       const uint32_t sub_all = (all >> (16 * st)) & 0xFFFFu;
       if (sub_any != 0u)
-        compute_tile<KIND, D, RT, HILO, true>(ring + (j % kStages) * stage_bytes, to, t0, cp.L,
+        compute_tile<KIND, D, RT, HILO, true>(myring + (j % kStages) * stage_bytes, to, t0, cp.L,
                                               sub_all == 0xFFFFu, c2, w, rm, any, 16 * st);
     } else if (t0 < run_len(p, cp.L, cp.rb)) {
       // full: the block's first row (step first_step) sees all 16 tokens
       compute_tile<KIND, D, RT, HILO>(
-          ring + (j % kStages) * stage_bytes, to, t0, cp.L,
+          myring + (j % kStages) * stage_bytes, to, t0, cp.L,
           t0 + 16 <= cp.L - (p.causal ? p.next_n - 1 - first_step(p, cp.rb) : 0), c2, w);
     }
     // end of a (sequence, head group) run inside this range: write the partial
@@ -976,7 +1043,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
         start_run<KIND, D, RT, HILO>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
     }
     // pages of the item the next iteration issues
-    if (jn + 1 < nitems) load_pages<KIND, D, SPARSE>(p, table, ld, lp, pg);
+    if (jn + 1 < nitems) load_page_w<KIND, D, SPARSE>(p, table, ld, wl, pg);
     if constexpr (SPARSE) {
 #pragma unroll
       for (int k = 0; k < kSparseRows; ++k) mc[k] = mn[k];
