@@ -532,10 +532,13 @@ __device__ __forceinline__ void tile_softmax(const f4 s, uint32_t okbits, float 
   // larger max; a row that has seen nothing holds zeros
   alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - m_new) * c2);
   rescale |= m_old != m_new && m_old != -INFINITY;
+  // exponent s * c2 - m * c2 as one fma (a row that saw only masked tokens
+  // keeps m = -inf; its p are selected to 0)
+  const float mc = m_new == -INFINITY ? 0.f : m_new * c2;
   float pf[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    pf[e] = __builtin_amdgcn_exp2f((s[e] - m_new) * c2);
+    pf[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mc));
     if constexpr (MASK) pf[e] = okv[e] ? pf[e] : 0.f;
   }
   const h2 p01 = {(_Float16)pf[0], (_Float16)pf[1]};
@@ -595,7 +598,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
       vraw[e][0] = *reinterpret_cast<const uint32_t*>(slot + to.v[e][0]);
     }
   }
-  if (!full) {
+  if (__builtin_expect(!full, 0)) {
     // tokens past the end (or selected by no row): zero their V codes by
     // select, so no 0 * NaN can reach O [NULLPAD, Fix]
 #pragma unroll
