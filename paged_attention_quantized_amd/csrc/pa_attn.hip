@@ -13,15 +13,19 @@
 // [RELOC, Summary].
 //
 // Memory path. A workgroup streams its items through a ring of kStages stages
-// in LDS. A stage holds the K rows, then the V rows, of the item's TS tokens x
-// HPU heads, fetched with global_load_lds_dwordx4 (HBM -> LDS, no registers):
-// the 16-byte loads of a wave cover whole rows, so a page is read as a few long
-// contiguous runs. kStages - 1 stages are in flight while one is computed; each
-// step waits with an explicit vmcnt and a bare s_barrier, and every step issues
-// the same number of loads (past the end: dummy in-bounds loads into the free
-// slot) so the count stays exact. Blocks are looked up with scalar loads only,
-// so no vector load waits behind the ring. Within a row, 16-byte pieces are
-// stored XOR-swizzled by the token index to spread LDS banks. Tokens past the
+// in LDS. A stage holds the item's TS tokens x HPU heads of K and V, fetched
+// with global_load_lds_dwordx4 (HBM -> LDS, no registers), and is cut into one
+// region per wave: each wave loads the K rows, then the V rows, of exactly the
+// 16 tokens and the head it computes, so it waits for its own loads only (an
+// explicit vmcnt) and the ring needs no barrier between waves. kStages - 1
+// stages are in flight while one is computed, and every step issues the same
+// number of loads (past the end: dummy in-bounds loads into the free slot) so
+// the count stays exact. A wave's 16 tokens lie in one page: one block-table
+// lookup per item, a scalar load issued one step ahead, so no vector load
+// waits behind the ring. Within a row, 16-byte pieces are stored XOR-swizzled
+// by the row index to spread LDS banks. (The prefill kernel below shares one
+// decoded copy of each stage between its waves and keeps a workgroup-wide
+// layout with barriers.) Tokens past the
 // sequence end are read only inside real pages; pages past the end are never
 // read (their lanes re-read the stage's first page), which keeps the null
 // block 0 unread [NULLPAD, Root cause].
@@ -30,8 +34,9 @@
 // the 16-token sub-tile st = w / HPU of every stage:
 //   1. K codes from LDS -> fp16 (exact for E4M3/INT8/INT4), S^T = K Q'^T with
 //      v_mfma_f32_16x16x32_f16 (tokens x query rows); a PER_CHANNEL K scale is
-//      folded into Q' = q * k_scale / max|k_scale| as fp16 hi + lo parts and
-//      max|k_scale| goes into the score scale [FOLD, Approach],
+//      folded into Q' = q * k_scale / max|k_scale| as fp16 hi + lo parts
+//      (both in one operand's 16 columns when a KV head has at most 8 query
+//      rows) and max|k_scale| goes into the score scale [FOLD, Approach],
 //   2. online softmax in base 2 on raw scores; tokens past the end or past a
 //      row's causal limit are selected to p = 0 (never multiplied),
 //   3. V codes from LDS -> fp16, rows of invalid tokens zeroed by select

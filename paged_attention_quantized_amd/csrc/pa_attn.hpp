@@ -198,8 +198,10 @@ __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, const
                : "memory");
 }
 
-// Per-thread constants of the ring loads. Load l of wave wv covers stage pieces
-// [(wv*NL + l)*64, +64): whole rows of tpi = 1024 / (hpu*RB) consecutive
+// Workgroup-wide stage loads (the prefill kernel, whose waves all read the
+// whole stage after a barrier; the ring kernel uses the per-wave regions of
+// make_wave_loads instead). Per-thread constants: load l of wave wv covers
+// stage pieces [(wv*NL + l)*64, +64): whole rows of tpi = 1024 / (hpu*RB) consecutive
 // tokens of one plane (tpi divides ts and bs, so the 1 KiB a load covers never
 // crosses a page). A wave's NL loads are consecutive pieces: with nw >= 2 they
 // lie in one plane and span 32 / hpu tokens, so they touch at most two pages
@@ -279,7 +281,7 @@ __device__ __forceinline__ void load_pages(const AttnParams& p, const int32_t* _
   pg.phys1 = (uint32_t)table_row[min(blk0 + lp.pi1, last_blk)];
 }
 
-// Issue the ring loads of one item into `slot`. Every thread issues exactly NL
+// Issue the workgroup-wide stage loads of one item into `slot`. Every thread issues exactly NL
 // loads whether the item is live or not. Stage layout: K plane then V plane,
 // each [TS tokens][HPU heads][CPR pieces]; piece j of row (tau, hl) is stored
 // at position j ^ (tau & (CPR - 1)). Each load's address is a scalar page base
