@@ -5,7 +5,7 @@
 // ordered by (sequence, head group, logical position) and the persistent grid
 // (one workgroup per compute unit) gives each workgroup a contiguous item
 // range of equal cost: every item costs one slot and every (sequence, head
-// group) run start kRunCost more (the q reload and partial store there drain
+// group) run start run_cost more (the q reload and partial store there drain
 // the load pipeline), and workgroup w takes the items in slots
 // [w*Q, (w+1)*Q), Q = ceil(slots / workgroups). Every workgroup therefore gets
 // about the same streaming time whatever the mix of context lengths, and all
@@ -78,8 +78,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
   const int hg = hk >> p.lhpu, hl = hk & (p.hpu - 1);
   const int idx = blockIdx.y * 256 + threadIdx.x;
   // the ring kernel's split: item k of run (b, rb, hg) sits at cost slot
-  // first_slot(b) + (slots of row blocks before rb) + hg * (nst + kRunCost) +
-  // kRunCost + k, and workgroup w owns slots [w * qc, (w + 1) * qc)
+  // first_slot(b) + (slots of row blocks before rb) + hg * (nst + run_cost) +
+  // run_cost + k, and workgroup w owns slots [w * qc, (w + 1) * qc)
   const int qc = max(1, (p.ws_seq[p.B] + p.nwg - 1) / p.nwg);
   const int L = p.context_lens[b];
   const int r = 4 * idx / D, d = 4 * idx % D;
@@ -91,12 +91,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
   for (int x0 = 0; x0 < rb; x0 += 64) {
     const int x = x0 + (int)(threadIdx.x & 63);
     const int n = x < rb ? run_stages(p, L, x) : 0;
-    before += lane_val(wave_incl_scan(n > 0 ? p.hgroups * (n + kRunCost) : 0), 63);
+    before += lane_val(wave_incl_scan(n > 0 ? p.hgroups * (n + p.run_cost) : 0), 63);
   }
   int slot0 = p.ws_seq[b] + uni(before);
   if (4 * idx >= p.R * D) return;  // after the wave-wide sums, which need every lane
   const int nst = run_stages(p, L, rb);
-  slot0 += hg * (nst + kRunCost) + kRunCost;
+  slot0 += hg * (nst + p.run_cost) + p.run_cost;
   const int i = r / p.G, h = hk * p.G + r % p.G;
   const int nsub = p.wgmerge ? 1 : p.nsub;
   float m = -INFINITY, l = 0.f;
@@ -290,6 +290,7 @@ struct Shape {
   size_t sp_entries_bytes, sp_masks_bytes, sp_vlen_bytes;
   int pages_max, entries_per_seq;
   int wgmerge;
+  int run_cost;                          // cost-line slots of a run start
   int64_t parts;
   size_t ml_bytes, o_bytes, seq_bytes;
 };
@@ -424,6 +425,17 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   const int xch_per_head = sh->RT * (a->head_dim / 16) * 1024 + sh->RT * 512;
   sh->wgmerge = (sh->nsub > 1 && xch_per_head <= kXchBytes) ? 1 : 0;
   if (sh->prefill) sh->wgmerge = 1;  // one partial per group: the waves own disjoint rows
+  // Cost of a run start in items, for the cost line: the first Q' loads wait
+  // for every ring load in flight, the ring refills, the partial is written,
+  // and with sub-tiles merged in the workgroup the LDS exchange runs. Measured
+  // from per-workgroup finish times against the runs each range touches: ~2
+  // items with one row tile, ~9 with two, and with the exchange one item
+  // plus about half an item per merged (head, extra sub-tile). The sparse
+  // route and the prefill layout keep 2.
+  sh->run_cost = 2;
+  if (sparse_topk < 0 && !sh->prefill)
+    sh->run_cost = 2 + (sh->RT == 2 ? 7 : 0) +
+                   (sh->wgmerge ? 1 + (sh->hpu * (sh->nsub - 1) + 1) / 2 : 0);
   // partial slots: one per (run, workgroup) pair a run can span, at most
   // runs + workgroups of them, each with one partial per head (and per
   // sub-tile when sub-tiles are not merged in the workgroup)
@@ -479,6 +491,7 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   p.lts = ilog2(sh.ts);
   p.lhpu = ilog2(sh.hpu);
   p.wgmerge = sh.wgmerge;
+  p.run_cost = sh.run_cost;
   p.k_scale_mode = a->k_scale_mode;
   p.v_scale_mode = a->v_scale_mode;
   p.causal = a->causal ? 1 : 0;

@@ -15,7 +15,6 @@ constexpr int kMaxWaves = 8;           // wavefronts per workgroup
 constexpr int kXchBytes = 32 * 1024;   // LDS exchange buffer (ring + exchange = 160 KiB)
 constexpr int kMaxNextN = 4096;        // query steps per sequence
 constexpr int kMaxRows = 8192;         // query rows per KV head (next_n * q heads per KV head)
-constexpr int kRunCost = 2;            // work split: items a run start costs (q reload, partial)
 
 // Q' formats of the ring kernel. Per-tensor scales: Q' is q in fp16 (kQPlain).
 // Per-channel K scales: Q' = q * k_scale / max|k_scale| in fp32, split into an
@@ -50,6 +49,7 @@ struct AttnParams {
   int nwg;                         // workgroups of the persistent grid
   int lbs, lts, lhpu;              // log2 of bs, ts, hpu (all powers of two)
   int wgmerge;                     // sub-tile states merged in the workgroup: one partial per head
+  int run_cost;                    // work split: items a run start costs (drain, q reload, partial)
   int k_scale_mode, v_scale_mode, causal;
   float softmax_scale;
   // selection-driven sparse mode: union plan of each sequence (entry k =
@@ -101,26 +101,26 @@ __device__ __forceinline__ int locate_slot(const AttnParams& p, int L, int rel, 
   int before = 0, n = run_stages(p, L, 0);
   rb = 0;
   while (rb + 1 < p.nrb) {
-    const int c = n > 0 ? p.hgroups * (n + kRunCost) : 0;
+    const int c = n > 0 ? p.hgroups * (n + p.run_cost) : 0;
     if (rel < c) break;
     rel -= c;
     before += p.hgroups * n;
     ++rb;
     n = run_stages(p, L, rb);
   }
-  hg = rel / (n + kRunCost);
-  k = max(rel % (n + kRunCost) - kRunCost, 0);
+  hg = rel / (n + p.run_cost);
+  k = max(rel % (n + p.run_cost) - p.run_cost, 0);
   return before + hg * n + k;
 }
 
 // A sequence's cost-line slots and items over all its row blocks: each run
-// with items takes kRunCost slots and then one per item, per head group.
+// with items takes run_cost slots and then one per item, per head group.
 __device__ __forceinline__ void seq_cost(const AttnParams& p, int L, int& cost, int& items) {
   cost = 0;
   items = 0;
   for (int rb = 0; rb < p.nrb; ++rb) {
     const int n = run_stages(p, L, rb);
-    cost += n > 0 ? p.hgroups * (n + kRunCost) : 0;
+    cost += n > 0 ? p.hgroups * (n + p.run_cost) : 0;
     items += p.hgroups * n;
   }
 }
@@ -885,7 +885,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
       (!HILO && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
 
   // ---- this workgroup's item range. Items are placed on a cost line where
-  // each (sequence, row block, head group) run first takes kRunCost empty slots (the
+  // each (sequence, row block, head group) run first takes run_cost empty slots (the
   // pipeline drain at a run start) and then one slot per item; workgroup w
   // takes the items whose slots fall in [w*Qc, (w+1)*Qc). One wave scans the
   // sequence lengths; workgroup 0 also publishes every sequence's first slot
