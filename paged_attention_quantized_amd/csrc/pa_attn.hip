@@ -428,14 +428,15 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   // Cost of a run start in items, for the cost line: the first Q' loads wait
   // for every ring load in flight, the ring refills, the partial is written,
   // and with sub-tiles merged in the workgroup the LDS exchange runs. Measured
-  // from per-workgroup finish times against the runs each range touches: ~2
-  // items with one row tile, ~9 with two, and with the exchange one item
-  // plus about half an item per merged (head, extra sub-tile). The sparse
-  // route and the prefill layout keep 2.
+  // from per-workgroup finish times against the runs each range touches, then
+  // tuned by timing: 2 items with one row tile and no exchange, 12 with two
+  // row tiles, and with the exchange 4 items plus about half an item per
+  // merged (head, extra sub-tile). The sparse route and the prefill layout
+  // keep 2 (no measurable change between 2 and 8 for the sparse route).
   sh->run_cost = 2;
   if (sparse_topk < 0 && !sh->prefill)
-    sh->run_cost = 2 + (sh->RT == 2 ? 7 : 0) +
-                   (sh->wgmerge ? 1 + (sh->hpu * (sh->nsub - 1) + 1) / 2 : 0);
+    sh->run_cost = 2 + (sh->RT == 2 ? 10 : 0) +
+                   (sh->wgmerge ? 4 + (sh->hpu * (sh->nsub - 1) + 1) / 2 : 0);
   // partial slots: one per (run, workgroup) pair a run can span, at most
   // runs + workgroups of them, each with one partial per head (and per
   // sub-tile when sub-tiles are not merged in the workgroup)
