@@ -401,6 +401,13 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
     ts = kPfTokens;
   } else {
     while (hpu > 1 && hpu * rb > 1024) hpu /= 2;
+    // Two row tiles: a head's partial is 32 rows x D fp32, and every run
+    // splits into about one partial per workgroup it crosses. At most 4 heads
+    // per item doubles the runs (head groups) and halves the workgroups each
+    // crosses, so the partials the ring writes and the merge reads halve; the
+    // ring itself takes the same time (measured on the FP8 verify workload:
+    // merge 13.6 -> ~7 us).
+    if (sh->RT == 2 && hpu > 4) hpu = 4;
     ts = kStageMax / 2 / (hpu * rb);
     if (ts > 64) ts = 64;
     if (ts > 16 * kMaxWaves / hpu) ts = 16 * kMaxWaves / hpu;
