@@ -23,7 +23,7 @@ from tests.gpu_util import DevAttn, compare_attn, dev, oracle_attn, run_attn, sa
 
 pytestmark = pytest.mark.gpu
 
-N_DENSE = 24
+N_DENSE = 64
 N_SPARSE = 8
 
 

@@ -170,8 +170,11 @@ def attn_case(name, seed, *, B, next_n, Hq, Hkv, D, bs, lens, kv_kind, scale_mod
         kx = rng.standard_normal(shape_real, dtype=np.float32)
         vx = rng.standard_normal(shape_real, dtype=np.float32)
         vmask = valid[:, :, None, None]
-        k_scale = np.array([np.abs(np.where(vmask, kx, 0)).max() / np.float32(448)], np.float32)
-        v_scale = np.array([np.abs(np.where(vmask, vx, 0)).max() / np.float32(448)], np.float32)
+        # a cache with no real page (every length 0) takes scale 1
+        kmax = np.abs(np.where(vmask, kx, 0)).max(initial=0.0)
+        vmax = np.abs(np.where(vmask, vx, 0)).max(initial=0.0)
+        k_scale = np.array([kmax / np.float32(448) if kmax > 0 else 1.0], np.float32)
+        v_scale = np.array([vmax / np.float32(448) if vmax > 0 else 1.0], np.float32)
         kc = e4m3_codes_torch(kx / k_scale[0])
         vc = e4m3_codes_torch(vx / v_scale[0])
     else:
