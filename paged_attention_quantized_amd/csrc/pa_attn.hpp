@@ -880,10 +880,6 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     p.nrb = 1;
     p.rpb = p.R;
   }
-  // the per-tensor K scale is read first, so its latency overlaps the scan
-  const float ks_tensor =
-      (!HILO && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
-
   // ---- this workgroup's item range. Items are placed on a cost line where
   // each (sequence, row block, head group) run first takes run_cost empty slots (the
   // pipeline drain at a run start) and then one slot per item; workgroup w
@@ -891,6 +887,10 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   // sequence lengths; workgroup 0 also publishes every sequence's first slot
   // and the total for the merge kernel ----
   if (wv == 0) range_scan(p, lens, xi);
+  // the per-tensor K scale: its pointer is a scalar load of its own, so it is
+  // read after the scan's length load has gone out
+  const float ks_tensor =
+      (!HILO && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
   __syncthreads();
   // workgroup-uniform (read back from LDS, so say so to the compiler)
   const int nitems = uni(xi[0]);
