@@ -28,11 +28,13 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 KV_F16, KV_BF16, KV_E4M3, KV_INT8, KV_INT4 = 0, 1, 2, 3, 4
 SCALE_NONE, SCALE_PER_TENSOR, SCALE_PER_CHANNEL = 0, 1, 2
 
-CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared",
+          "-fPIC"]
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle with gcc (ISO C11, no FP contraction)."""
+    """Compile the oracle with gcc (ISO C11, no FP contraction, OpenMP over
+    independent units)."""
     subprocess.run(["gcc", *CFLAGS, src, "-o", out, "-lm"], check=True)
     return out
 
@@ -77,16 +79,20 @@ def _bind(lib):
     lib.orc_ue8m0_to_f32.restype = f32
     lib.orc_dequantize.argtypes = [i32, P, i64, P, i32, i64, P]
     lib.orc_dequantize.restype = None
-    lib.orc_paged_attn.argtypes = [P, P, P, P, i32, P, i32, P, i32, P, P,
-                                   i32, i32, i32, i32, i32, i32, i64, i32, f32, i32]
+    lib.orc_set_threads.argtypes = [i32]
+    lib.orc_set_threads.restype = None
+    lib.orc_threads.argtypes = []
+    lib.orc_threads.restype = i32
+    lib.orc_paged_attn.argtypes = [P, P, i32, P, P, i32, P, i32, P, i32, P, P,
+                                   i32, i32, i32, i32, i32, i32, i64, i32, f32, i32, P, P]
     lib.orc_paged_attn.restype = i32
-    lib.orc_paged_attn_sparse.argtypes = [P, P, P, P, i32, P, i32, P, i32, P, P, P, i32,
-                                          i32, i32, i32, i32, i32, i32, i64, i32, f32]
+    lib.orc_paged_attn_sparse.argtypes = [P, P, i32, P, P, i32, P, i32, P, i32, P, P, P, i32,
+                                          i32, i32, i32, i32, i32, i32, i64, i32, f32, P, P]
     lib.orc_paged_attn_sparse.restype = i32
     lib.orc_sparse_plan.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32]
     lib.orc_sparse_plan.restype = i32
     lib.orc_mqa_logits.argtypes = [P, i64, P, P, P, P, P, P,
-                                   i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
+                                   i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.orc_f32_to_bf16_array.argtypes = [P, P, i64]
     lib.orc_f32_to_bf16_array.restype = None
     lib.orc_f32_to_e2m1.argtypes = [f32]
@@ -152,16 +158,47 @@ def dequantize(kind, codes, n, scale=None, mode=SCALE_NONE, channels=1, lib=None
 # the three operations
 # ---------------------------------------------------------------------------
 
+def set_threads(n, lib=None):
+    """Threads of the oracle's parallel loops (n <= 0: one per processor)."""
+    (lib or load()).orc_set_threads(int(n))
+
+
+def threads(lib=None):
+    return (lib or load()).orc_threads()
+
+
+def _q16(q):
+    """fp16 / bf16 query bits and whether they are bf16 (a torch bfloat16
+    tensor, or uint16 bits marked by the caller)."""
+    try:
+        import torch
+        if isinstance(q, torch.Tensor):
+            bf = q.dtype == torch.bfloat16
+            return q.contiguous().view(torch.int16).numpy().view(np.uint16), bf
+    except ImportError:  # pragma: no cover
+        pass
+    return _bits16(q), False
+
+
 def paged_attn(q, k_cache, v_cache, kv_kind, block_table, context_lens, *,
                k_scale=None, k_scale_mode=SCALE_NONE, v_scale=None, v_scale_mode=SCALE_NONE,
-               num_kv_heads, head_dim, block_size, softmax_scale, causal=True, lib=None):
+               num_kv_heads, head_dim, block_size, softmax_scale, causal=True, q_is_bf16=None,
+               conditioning=False, lib=None):
     """Reference paged attention (see orc_paged_attn in oracle.c).
 
-    q: [B, next_n, Hq, D] fp16 (or its uint16 bits); caches: uint8/fp16 arrays of shape
-    [num_blocks, block_size, Hkv, D_bytes]. Returns float64 [B, next_n, Hq, D].
+    q: [B, next_n, Hq, D] fp16 (numpy float16 or uint16 bits), or bf16 (a torch
+    bfloat16 tensor, or uint16 bits with q_is_bf16=True); caches: uint8/fp16
+    arrays of shape [num_blocks, block_size, Hkv, D_bytes]. Returns float64
+    [B, next_n, Hq, D]; with conditioning=True also (cond float64 [B, next_n,
+    Hq, 3]: top-2 score gap, fp32 score-error bound, tokens in the relevant
+    set; vrange float64 [B, next_n, Hq, 3, D]: min and max of V over that set,
+    and sum_t p_t |V_t - out| / l per channel, the output's first-order
+    sensitivity to score errors).
     """
     lib = lib or load()
-    q16 = _bits16(q)
+    q16, bf = _q16(q)
+    if q_is_bf16 is not None:
+        bf = bool(q_is_bf16)
     B, next_n, Hq, D = q16.shape
     assert D == head_dim
     kc = np.ascontiguousarray(k_cache).view(np.uint8)
@@ -172,27 +209,36 @@ def paged_attn(q, k_cache, v_cache, kv_kind, block_table, context_lens, *,
     ks = _c(k_scale if k_scale is not None else np.ones(1, np.float32), np.float32)
     vs = _c(v_scale if v_scale is not None else np.ones(1, np.float32), np.float32)
     out = np.empty((B, next_n, Hq, D), np.float64)
-    rc = lib.orc_paged_attn(_ptr(out), _ptr(q16), _ptr(kc), _ptr(vc), kv_kind,
+    cond = np.empty((B, next_n, Hq, 4), np.float64) if conditioning else None
+    vr = np.empty((B, next_n, Hq, 3, D), np.float64) if conditioning else None
+    rc = lib.orc_paged_attn(_ptr(out), _ptr(q16), int(bf), _ptr(kc), _ptr(vc), kv_kind,
                             _ptr(ks), k_scale_mode, _ptr(vs), v_scale_mode, _ptr(bt), _ptr(cl),
                             B, next_n, Hq, num_kv_heads, D, block_size, num_blocks,
-                            bt.shape[1], float(softmax_scale), int(causal))
+                            bt.shape[1], float(softmax_scale), int(causal), _ptr(cond), _ptr(vr))
     if rc != 0:
         raise ValueError(f"orc_paged_attn failed with code {rc}")
+    if conditioning:
+        return out, cond[..., :3], vr
     return out
 
 
 def paged_attn_sparse(q, k_cache, v_cache, kv_kind, block_table, context_lens, sel, *,
                       k_scale=None, k_scale_mode=SCALE_NONE, v_scale=None,
                       v_scale_mode=SCALE_NONE, num_kv_heads, head_dim, block_size,
-                      softmax_scale, causal=None, lib=None):
+                      softmax_scale, causal=None, q_is_bf16=None, conditioning=False,
+                      lib=None):
     """Reference selection-driven sparse paged attention (see orc_paged_attn_sparse).
 
     sel: int32 [B, next_n, topk] logical token ids (entries outside [0, L_b)
-    select nothing). Returns float64 [B, next_n, Hq, D]. `causal` is accepted
-    for keyword compatibility with paged_attn and ignored.
+    select nothing). Returns float64 [B, next_n, Hq, D] (with
+    conditioning=True also cond and vrange as for paged_attn, over each row's
+    selected tokens). `causal` is accepted for keyword compatibility with
+    paged_attn and ignored.
     """
     lib = lib or load()
-    q16 = _bits16(q)
+    q16, bf = _q16(q)
+    if q_is_bf16 is not None:
+        bf = bool(q_is_bf16)
     B, next_n, Hq, D = q16.shape
     assert D == head_dim
     sl = _c(sel, np.int32)
@@ -204,13 +250,17 @@ def paged_attn_sparse(q, k_cache, v_cache, kv_kind, block_table, context_lens, s
     ks = _c(k_scale if k_scale is not None else np.ones(1, np.float32), np.float32)
     vs = _c(v_scale if v_scale is not None else np.ones(1, np.float32), np.float32)
     out = np.empty((B, next_n, Hq, D), np.float64)
-    rc = lib.orc_paged_attn_sparse(_ptr(out), _ptr(q16), _ptr(kc), _ptr(vc), kv_kind,
+    cond = np.empty((B, next_n, Hq, 4), np.float64) if conditioning else None
+    vr = np.empty((B, next_n, Hq, 3, D), np.float64) if conditioning else None
+    rc = lib.orc_paged_attn_sparse(_ptr(out), _ptr(q16), int(bf), _ptr(kc), _ptr(vc), kv_kind,
                                    _ptr(ks), k_scale_mode, _ptr(vs), v_scale_mode, _ptr(bt),
                                    _ptr(cl), _ptr(sl), sl.shape[2], B, next_n, Hq, num_kv_heads,
                                    D, block_size, k_cache.shape[0], bt.shape[1],
-                                   float(softmax_scale))
+                                   float(softmax_scale), _ptr(cond), _ptr(vr))
     if rc != 0:
         raise ValueError(f"orc_paged_attn_sparse failed with code {rc}")
+    if conditioning:
+        return out, cond[..., :3], vr
     return out
 
 
@@ -236,14 +286,16 @@ def sparse_plan(sel, block_table, context_lens, block_size, cap=None, lib=None):
 
 def mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_context_len, *,
                sf_vec_size=32, out_rows=None, out_row_stride=None, sf_interleaved=False,
-               relu=False, out_format="f32", lib=None):
+               relu=False, out_format="f32", epi_format="f32", lib=None):
     """Reference MXFP4 paged MQA logits (see orc_mqa_logits in oracle.c).
 
     q: uint8 [B, next_n, H, D/2]; sf_q: int32 [B, next_n, H]; kv_fused: uint8
     [num_blocks, bs, 1, D/2 + D/sf_vec] with the scale tail in token order or,
     with sf_interleaved, in the interleaved slot order; weights: fp32
     [B*next_n, H]. relu puts max(., +0) between each head's dot product and its
-    weight. Returns [B*next_n, max_context_len] (or [out_rows, out_row_stride])
+    weight. epi_format "f16" / "bf16" runs the weighted head chain in that type
+    (see epi_step in oracle.c). Returns [B*next_n, max_context_len] (or
+    [out_rows, out_row_stride])
     as fp32, or as fp16 / bf16 (uint16 bits) rounded to nearest even from the
     fp32 values for out_format "f16" / "bf16".
     """
@@ -262,7 +314,8 @@ def mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_contex
     out = np.full((rows, stride), np.nan, np.float32)
     rc = lib.orc_mqa_logits(_ptr(out), stride, _ptr(q), _ptr(sfq), _ptr(kv), _ptr(w), _ptr(cl),
                             _ptr(bt), B, next_n, H, D, bs, bt.shape[1], max_context_len,
-                            sf_vec_size, int(bool(sf_interleaved)), int(bool(relu)))
+                            sf_vec_size, int(bool(sf_interleaved)), int(bool(relu)),
+                            {"f32": 0, "f16": 1, "bf16": 2}[epi_format])
     if rc != 0:
         raise ValueError(f"orc_mqa_logits failed with code {rc}")
     if out_format == "f32":

@@ -29,6 +29,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_KV_F16 0
 #define ORC_KV_BF16 1
@@ -274,8 +277,161 @@ void orc_dequantize(int kind, const uint8_t* codes, int64_t n, const float* scal
 }
 
 /* ------------------------------------------------------------------ */
+/* Threads                                                             */
+/* ------------------------------------------------------------------ */
+
+/* The attention and logits loops run their independent units (a sequence and
+ * KV head, or a logits row) on OpenMP threads; every sum inside a unit keeps
+ * its stated order, so the result does not depend on the thread count.
+ * n > 0 sets the thread count, n <= 0 restores one thread per processor. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+#else
+  (void)n;
+#endif
+}
+
+int orc_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ */
 /* Paged attention                                                     */
 /* ------------------------------------------------------------------ */
+
+/* Query value: fp16 or bf16 bits. */
+static float q_value(const uint16_t* q, int q_is_bf16, int64_t idx) {
+  return q_is_bf16 ? orc_bf16_to_f32(q[idx]) : orc_f16_to_f32(q[idx]);
+}
+
+/* Dequantized K and V rows of tokens t < L of sequence b for KV head hk (only
+ * tokens with want[t] != 0 when want is given): kd[t * D + d], vd[t * D + d].
+ * csum[t] = sum over d of |K code|. A token mapped outside the real blocks
+ * (block 0 is the null block) is a harness error: returns -1. */
+static int gather_rows(float* kd, float* vd, double* csum, const unsigned char* want,
+                       const uint8_t* k_cache, const uint8_t* v_cache, int kind,
+                       const float* k_scale, int k_mode, const float* v_scale, int v_mode,
+                       const int32_t* table_row, int L, int hk, int bs, int Hkv, int D,
+                       int64_t num_blocks) {
+  for (int t = 0; t < L; ++t) {
+    if (want && !want[t]) continue;
+    int64_t blk = table_row[t / bs];
+    if (blk <= 0 || blk >= num_blocks) return -1;
+    double c = 0.0;
+    for (int d = 0; d < D; ++d) {
+      float kc = cache_code(k_cache, kind, blk, t % bs, hk, d, bs, Hkv, D);
+      kd[(int64_t)t * D + d] = kc * scale_of(k_scale, k_mode, hk, d, D); /* = deq() */
+      vd[(int64_t)t * D + d] = deq(v_cache, kind, v_scale, v_mode, blk, t % bs, hk, d, bs, Hkv, D);
+      c += fabs((double)kc);
+    }
+    csum[t] = c;
+  }
+  return 0;
+}
+
+/*
+ * One query row over its visible tokens (vis[t] != 0, t < L): scores
+ * s_t = softmax_scale * sum over d ascending of q[d] * K_t[d] (double), then
+ * softmax and the weighted sum of V, both over t ascending; the row is +0
+ * when no token is visible.
+ *
+ * Conditioning (cond != NULL): cond[0] = s_top1 - s_top2 (the fp64 gap
+ * between the two largest scores, +inf with fewer than two tokens), cond[1] =
+ * eps, a bound on the error of one score computed with fp32 accumulation:
+ * eps = max over t of softmax_scale * ((D + 8) * 2^-24 * sum_d |q[d] K_t[d]|
+ * + fold * 2^-25 * kmax * csum[t]), where the second term (folded per-channel
+ * K scales, kmax = max|k_scale|) bounds a 2^-25 absolute error per element of
+ * a q * k_scale / kmax split into two fp16 parts. cond[2] = the number of
+ * tokens with s_t >= s_top1 - 8 eps - 32, the tokens whose softmax weight can
+ * exceed e^-32 of the largest under such errors; vlo[d] / vhi[d] = min / max
+ * of V_t[d] over them; vsens[d] = sum_t p_t |V_t[d] - out[d]| / l, the
+ * first-order change of out[d] per unit of score error common to no token
+ * (|d out / d s| summed over t).
+ */
+static void attend_row(double* orow, const float* qf, const float* kd, const float* vd,
+                       const double* csum, const unsigned char* vis, int L, int D,
+                       float softmax_scale, double* s, double* ab, double* cond, double* vlo,
+                       double* vhi, double* vsens, double fold_kmax) {
+  for (int d = 0; d < D; ++d) orow[d] = 0.0;
+  double m = -INFINITY;
+  int n = 0;
+  for (int t = 0; t < L; ++t) {
+    if (!vis[t]) continue;
+    double acc = 0.0, aabs = 0.0;
+    for (int d = 0; d < D; ++d) {
+      double x = (double)qf[d] * (double)kd[(int64_t)t * D + d];
+      acc += x;
+      aabs += fabs(x);
+    }
+    s[t] = (double)softmax_scale * acc;
+    ab[t] = (double)softmax_scale * ((D + 8) * ldexp(1.0, -24) * aabs +
+                                     ldexp(1.0, -25) * fold_kmax * csum[t]);
+    if (s[t] > m) m = s[t];
+    ++n;
+  }
+  if (cond) {
+    double second = -INFINITY, eps = 0.0;
+    int top = 0;
+    for (int t = 0; t < L; ++t) {
+      if (!vis[t]) continue;
+      if (ab[t] > eps) eps = ab[t];
+      if (s[t] == m && !top) {
+        top = 1;
+        continue;
+      }
+      if (s[t] > second) second = s[t];
+    }
+    cond[0] = n >= 2 ? m - second : INFINITY;
+    cond[1] = eps;
+    cond[2] = 0.0;
+    for (int d = 0; d < D; ++d) {
+      vlo[d] = INFINITY;
+      vhi[d] = -INFINITY;
+    }
+    for (int t = 0; t < L; ++t) {
+      if (!vis[t] || s[t] < m - 8.0 * eps - 32.0) continue;
+      cond[2] += 1.0;
+      for (int d = 0; d < D; ++d) {
+        double v = vd[(int64_t)t * D + d];
+        if (v < vlo[d]) vlo[d] = v;
+        if (v > vhi[d]) vhi[d] = v;
+      }
+    }
+  }
+  if (vsens)
+    for (int d = 0; d < D; ++d) vsens[d] = 0.0;
+  if (n == 0) return;
+  double l = 0.0;
+  for (int t = 0; t < L; ++t) {
+    if (!vis[t]) continue;
+    s[t] = exp(s[t] - m);
+    l += s[t];
+  }
+  for (int t = 0; t < L; ++t) {
+    if (!vis[t]) continue;
+    for (int d = 0; d < D; ++d) orow[d] += s[t] * (double)vd[(int64_t)t * D + d];
+  }
+  for (int d = 0; d < D; ++d) orow[d] /= l;
+  if (vsens) {
+    for (int t = 0; t < L; ++t) {
+      if (!vis[t]) continue;
+      for (int d = 0; d < D; ++d) vsens[d] += s[t] * fabs((double)vd[(int64_t)t * D + d] - orow[d]);
+    }
+    for (int d = 0; d < D; ++d) vsens[d] /= l;
+  }
+}
+
+static float max_abs(const float* x, int64_t n) {
+  float m = 0.0f;
+  for (int64_t i = 0; i < n; ++i)
+    if (fabsf(x[i]) > m) m = fabsf(x[i]);
+  return m;
+}
 
 /*
  * out[b, i, h, :] = softmax(softmax_scale * q[b,i,h,:] . K_t) @ V_t over the
@@ -284,72 +440,74 @@ void orc_dequantize(int kind, const uint8_t* codes, int64_t n, const float* scal
  *
  * Readings where the pages are silent:
  *  - q and out are [B, next_n, Hq, D]; query head h reads KV head
- *    h / (Hq / Hkv) (contiguous groups).
+ *    h / (Hq / Hkv) (contiguous groups). q is fp16, or bf16 with q_is_bf16.
  *  - Query row i sits at absolute position L_b - next_n + i; with causal set
  *    it sees tokens t <= that position, otherwise all t < L_b.
  *  - No visible token: the output row is +0.
- *  - Tokens that are not visible are never read, so the null block (physical
- *    block 0 [P1, Root cause]) and tail slots cannot influence the result. A
- *    visible token mapped to block 0 is a harness error (returns -1).
+ *  - Tokens past L_b are never read, so the null block (physical block 0
+ *    [P1, Root cause]) and tail slots cannot influence the result. A token
+ *    t < L_b mapped to block 0 is a harness error (returns -1).
  *
  * Scores, softmax and the weighted sum are accumulated in double; `out` is
- * the double result (the caller rounds to its output dtype).
+ * the double result (the caller rounds to its output dtype). cond / vrange
+ * (NULL to skip): per output row (b, i, h) the conditioning of attend_row,
+ * cond[row * 4 + {0, 1, 2}], vrange[(row * 3 + {0, 1, 2}) * D + d] = vlo, vhi,
+ * vsens.
  */
-int orc_paged_attn(double* out, const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
-                   int kv_kind, const float* k_scale, int k_scale_mode, const float* v_scale,
-                   int v_scale_mode, const int32_t* block_table, const int32_t* context_lens, int B,
-                   int next_n, int Hq, int Hkv, int D, int bs, int64_t num_blocks, int max_blocks,
-                   float softmax_scale, int causal) {
+int orc_paged_attn(double* out, const uint16_t* q, int q_is_bf16, const uint8_t* k_cache,
+                   const uint8_t* v_cache, int kv_kind, const float* k_scale, int k_scale_mode,
+                   const float* v_scale, int v_scale_mode, const int32_t* block_table,
+                   const int32_t* context_lens, int B, int next_n, int Hq, int Hkv, int D, int bs,
+                   int64_t num_blocks, int max_blocks, float softmax_scale, int causal,
+                   double* cond, double* vrange) {
   int group = Hq / Hkv;
   int max_len = max_blocks * bs;
-  double* s = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+  double fold_kmax = k_scale_mode == ORC_SCALE_PER_CHANNEL
+                         ? (double)max_abs(k_scale, (int64_t)Hkv * D) : 0.0;
   int rc = 0;
-  for (int b = 0; b < B; ++b) {
+  for (int b = 0; b < B; ++b)
+    if (context_lens[b] > max_len) return -2;
+#pragma omp parallel for schedule(dynamic)
+  for (int u = 0; u < B * Hkv; ++u) {
+    int b = u / Hkv, hk = u % Hkv;
     int L = context_lens[b];
-    for (int i = 0; i < next_n; ++i) {
+    int n = L > 0 ? L : 1;
+    float* kd = (float*)malloc(sizeof(float) * (size_t)n * D);
+    float* vd = (float*)malloc(sizeof(float) * (size_t)n * D);
+    double* csum = (double*)malloc(sizeof(double) * (size_t)n);
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double* ab = (double*)malloc(sizeof(double) * (size_t)n);
+    unsigned char* vis = (unsigned char*)malloc((size_t)n);
+    float* qf = (float*)malloc(sizeof(float) * (size_t)D);
+    int bad = gather_rows(kd, vd, csum, NULL, k_cache, v_cache, kv_kind, k_scale, k_scale_mode,
+                          v_scale, v_scale_mode, block_table + (int64_t)b * max_blocks, L, hk, bs,
+                          Hkv, D, num_blocks);
+    if (bad) {
+#pragma omp atomic write
+      rc = -1;
+    }
+    for (int i = 0; i < next_n && !bad; ++i) {
       int pos = L - next_n + i;
       int nvis = L;
       if (causal && pos + 1 < nvis) nvis = pos + 1;
-      if (nvis < 0) nvis = 0;
-      if (nvis > max_len) { rc = -2; goto done; }
-      for (int h = 0; h < Hq; ++h) {
-        int hk = h / group;
-        const uint16_t* qrow = q + (((int64_t)b * next_n + i) * Hq + h) * D;
-        double* orow = out + (((int64_t)b * next_n + i) * Hq + h) * D;
-        for (int d = 0; d < D; ++d) orow[d] = 0.0;
-        if (nvis == 0) continue;
-        double m = -INFINITY;
-        for (int t = 0; t < nvis; ++t) {
-          int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
-          int slot = t % bs;
-          if (blk <= 0 || blk >= num_blocks) { rc = -1; goto done; }
-          double acc = 0.0;
-          for (int d = 0; d < D; ++d) {
-            float kv = deq(k_cache, kv_kind, k_scale, k_scale_mode, blk, slot, hk, d, bs, Hkv, D);
-            acc += (double)orc_f16_to_f32(qrow[d]) * (double)kv;
-          }
-          s[t] = (double)softmax_scale * acc;
-          if (s[t] > m) m = s[t];
-        }
-        double l = 0.0;
-        for (int t = 0; t < nvis; ++t) {
-          s[t] = exp(s[t] - m);
-          l += s[t];
-        }
-        for (int t = 0; t < nvis; ++t) {
-          int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
-          int slot = t % bs;
-          for (int d = 0; d < D; ++d) {
-            float vv = deq(v_cache, kv_kind, v_scale, v_scale_mode, blk, slot, hk, d, bs, Hkv, D);
-            orow[d] += s[t] * (double)vv;
-          }
-        }
-        for (int d = 0; d < D; ++d) orow[d] /= l;
+      for (int t = 0; t < L; ++t) vis[t] = t < nvis;
+      for (int h = hk * group; h < (hk + 1) * group; ++h) {
+        int64_t row = ((int64_t)b * next_n + i) * Hq + h;
+        for (int d = 0; d < D; ++d) qf[d] = q_value(q, q_is_bf16, row * D + d);
+        attend_row(out + row * D, qf, kd, vd, csum, vis, L, D, softmax_scale, s, ab,
+                   cond ? cond + row * 4 : NULL, vrange ? vrange + row * 3 * D : NULL,
+                   vrange ? vrange + row * 3 * D + D : NULL,
+                   vrange ? vrange + row * 3 * D + 2 * D : NULL, fold_kmax);
       }
     }
+    free(kd);
+    free(vd);
+    free(csum);
+    free(s);
+    free(ab);
+    free(vis);
+    free(qf);
   }
-done:
-  free(s);
   return rc;
 }
 
@@ -374,66 +532,66 @@ static void mark_selection(unsigned char* mark, const int32_t* sel_row, int topk
  * token ids of a query row]. All heads of a row share its selection. An empty
  * selection gives +0. No causal limit is applied: the selection alone decides
  * what a row sees. Tokens outside every selection are never read, so tail
- * slots and the null block cannot reach the output [P1, Fix].
+ * slots and the null block cannot reach the output [P1, Fix]. cond / vrange
+ * as for orc_paged_attn, over each row's selected tokens.
  */
-int orc_paged_attn_sparse(double* out, const uint16_t* q, const uint8_t* k_cache,
+int orc_paged_attn_sparse(double* out, const uint16_t* q, int q_is_bf16, const uint8_t* k_cache,
                           const uint8_t* v_cache, int kv_kind, const float* k_scale,
                           int k_scale_mode, const float* v_scale, int v_scale_mode,
                           const int32_t* block_table, const int32_t* context_lens,
                           const int32_t* sel, int topk, int B, int next_n, int Hq, int Hkv, int D,
-                          int bs, int64_t num_blocks, int max_blocks, float softmax_scale) {
+                          int bs, int64_t num_blocks, int max_blocks, float softmax_scale,
+                          double* cond, double* vrange) {
   int group = Hq / Hkv;
   int max_len = max_blocks * bs;
-  double* s = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
-  unsigned char* mark = (unsigned char*)malloc((size_t)(max_len > 0 ? max_len : 1));
+  double fold_kmax = k_scale_mode == ORC_SCALE_PER_CHANNEL
+                         ? (double)max_abs(k_scale, (int64_t)Hkv * D) : 0.0;
   int rc = 0;
-  for (int b = 0; b < B; ++b) {
+  for (int b = 0; b < B; ++b)
+    if (context_lens[b] > max_len) return -2;
+#pragma omp parallel for schedule(dynamic)
+  for (int u = 0; u < B * Hkv; ++u) {
+    int b = u / Hkv, hk = u % Hkv;
     int L = context_lens[b];
-    if (L > max_len) { rc = -2; goto done; }
+    int n = L > 0 ? L : 1;
+    float* kd = (float*)malloc(sizeof(float) * (size_t)n * D);
+    float* vd = (float*)malloc(sizeof(float) * (size_t)n * D);
+    double* csum = (double*)malloc(sizeof(double) * (size_t)n);
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double* ab = (double*)malloc(sizeof(double) * (size_t)n);
+    unsigned char* mark = (unsigned char*)malloc((size_t)n * (next_n > 0 ? next_n : 1));
+    unsigned char* any = (unsigned char*)calloc((size_t)n, 1);
+    float* qf = (float*)malloc(sizeof(float) * (size_t)D);
     for (int i = 0; i < next_n; ++i) {
-      mark_selection(mark, sel + ((int64_t)b * next_n + i) * topk, topk, L);
-      for (int h = 0; h < Hq; ++h) {
-        int hk = h / group;
-        const uint16_t* qrow = q + (((int64_t)b * next_n + i) * Hq + h) * D;
-        double* orow = out + (((int64_t)b * next_n + i) * Hq + h) * D;
-        for (int d = 0; d < D; ++d) orow[d] = 0.0;
-        double m = -INFINITY;
-        int n = 0;
-        for (int t = 0; t < L; ++t) {
-          if (!mark[t]) continue;
-          int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
-          if (blk <= 0 || blk >= num_blocks) { rc = -1; goto done; }
-          double acc = 0.0;
-          for (int d = 0; d < D; ++d) {
-            float kv = deq(k_cache, kv_kind, k_scale, k_scale_mode, blk, t % bs, hk, d, bs, Hkv, D);
-            acc += (double)orc_f16_to_f32(qrow[d]) * (double)kv;
-          }
-          s[t] = (double)softmax_scale * acc;
-          if (s[t] > m) m = s[t];
-          ++n;
-        }
-        if (n == 0) continue;
-        double l = 0.0;
-        for (int t = 0; t < L; ++t) {
-          if (!mark[t]) continue;
-          s[t] = exp(s[t] - m);
-          l += s[t];
-        }
-        for (int t = 0; t < L; ++t) {
-          if (!mark[t]) continue;
-          int64_t blk = block_table[(int64_t)b * max_blocks + t / bs];
-          for (int d = 0; d < D; ++d) {
-            float vv = deq(v_cache, kv_kind, v_scale, v_scale_mode, blk, t % bs, hk, d, bs, Hkv, D);
-            orow[d] += s[t] * (double)vv;
-          }
-        }
-        for (int d = 0; d < D; ++d) orow[d] /= l;
+      mark_selection(mark + (size_t)i * n, sel + ((int64_t)b * next_n + i) * topk, topk, L);
+      for (int t = 0; t < L; ++t) any[t] |= mark[(size_t)i * n + t];
+    }
+    int bad = gather_rows(kd, vd, csum, any, k_cache, v_cache, kv_kind, k_scale, k_scale_mode,
+                          v_scale, v_scale_mode, block_table + (int64_t)b * max_blocks, L, hk, bs,
+                          Hkv, D, num_blocks);
+    if (bad) {
+#pragma omp atomic write
+      rc = -1;
+    }
+    for (int i = 0; i < next_n && !bad; ++i) {
+      for (int h = hk * group; h < (hk + 1) * group; ++h) {
+        int64_t row = ((int64_t)b * next_n + i) * Hq + h;
+        for (int d = 0; d < D; ++d) qf[d] = q_value(q, q_is_bf16, row * D + d);
+        attend_row(out + row * D, qf, kd, vd, csum, mark + (size_t)i * n, L, D, softmax_scale,
+                   s, ab, cond ? cond + row * 4 : NULL, vrange ? vrange + row * 3 * D : NULL,
+                   vrange ? vrange + row * 3 * D + D : NULL,
+                   vrange ? vrange + row * 3 * D + 2 * D : NULL, fold_kmax);
       }
     }
+    free(kd);
+    free(vd);
+    free(csum);
+    free(s);
+    free(ab);
+    free(mark);
+    free(any);
+    free(qf);
   }
-done:
-  free(s);
-  free(mark);
   return rc;
 }
 
@@ -505,9 +663,26 @@ static int sf_slot_of_token(int t, int bs, int spi, int interleaved) {
   return -1;
 }
 
+/* Value x rounded to the epilogue type: fp32 (0), fp16 (1) or bf16 (2), both
+ * round to nearest even. */
+static float epi_round(float x, int epi_format) {
+  if (epi_format == 1) return orc_f16_to_f32(orc_f64_to_f16((double)x));
+  if (epi_format == 2) return orc_bf16_to_f32(orc_f32_to_bf16(x));
+  return x;
+}
+
+/* One step of the weighted head chain [P5, epi_dtype]. fp32: fmaf(w, s, acc).
+ * Reading for the fp16 / bf16 epilogues (the page names them without their
+ * arithmetic): the weight and the head's dot product are rounded to the
+ * epilogue type, the step is the fp32 fmaf of those and the running value, and
+ * its result is rounded to the epilogue type again. */
+static float epi_step(float w, float s, float acc, int epi_format) {
+  return epi_round(fmaf(epi_round(w, epi_format), epi_round(s, epi_format), acc), epi_format);
+}
+
 /*
  * out[b*next_n + i, t] = sum over heads h (ascending, fp32 fmaf chain from +0)
- *   of weights[b*next_n + i, h] * A(S_h), with
+ *   of weights[b*next_n + i, h] * A(S_h) (each step as epi_step), with
  *   S_h = sum over d (ascending, fp32) of deq(q[b,i,h,d]) * deq(k_t[d]),
  * for t < context_lens[b]; -inf for context_lens[b] <= t < max_context_len.
  * A is the identity, or with relu != 0 the rectifier (S_h > 0 ? S_h : +0).
@@ -527,13 +702,16 @@ int orc_mqa_logits(float* out, int64_t out_row_stride, const uint8_t* q, const i
                    const uint8_t* kv_fused, const float* weights, const int32_t* context_lens,
                    const int32_t* block_table, int B, int next_n, int H, int D, int bs,
                    int max_blocks, int max_context_len, int sf_vec, int sf_interleaved,
-                   int relu) {
+                   int relu, int epi_format) {
   int row_bytes = D / 2 + D / sf_vec;
   int spi = D / sf_vec;
   if (sf_interleaved && bs % spi != 0) return -3;
+  for (int b = 0; b < B; ++b)
+    if (context_lens[b] > max_context_len || context_lens[b] > max_blocks * bs) return -2;
+  /* rows are independent: one per OpenMP work unit */
+#pragma omp parallel for schedule(dynamic)
   for (int b = 0; b < B; ++b) {
     int L = context_lens[b];
-    if (L > max_context_len || L > max_blocks * bs) return -2;
     for (int i = 0; i < next_n; ++i) {
       int64_t r = (int64_t)b * next_n + i;
       float* orow = out + r * out_row_stride;
@@ -559,7 +737,7 @@ int orc_mqa_logits(float* out, int64_t out_row_stride, const uint8_t* q, const i
             sh += qv * kv;
           }
           if (relu) sh = sh > 0.0f ? sh : 0.0f;
-          acc = fmaf(weights[r * H + h], sh, acc);
+          acc = epi_step(weights[r * H + h], sh, acc, epi_format);
         }
         orow[t] = acc;
       }

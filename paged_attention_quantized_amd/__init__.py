@@ -164,10 +164,40 @@ def _mode(scale, mode):
 # paged attention
 # ---------------------------------------------------------------------------
 
+def _need(t, name, dtypes, ndim=None, optional=False):
+    """Reject a tensor the C ABI would misread: wrong dtype, rank or layout."""
+    if t is None:
+        if optional:
+            return
+        raise PaError(1, f"{name} is required")
+    if t.dtype not in dtypes:
+        raise PaError(1, f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise PaError(1, f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise PaError(1, f"{name} must be contiguous")
+
+
+def _q_dtype(q):
+    import torch
+    return {torch.float16: DT_F16, torch.bfloat16: DT_BF16}[q.dtype]
+
+
 def _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len, kv_kind,
                k_scale, v_scale, k_scale_mode, v_scale_mode, softmax_scale, causal):
+    import torch
+    _need(q, "q", (torch.float16, torch.bfloat16), 4)
+    _need(out, "out", (q.dtype,), 4, optional=True)
+    if out is not None and out.shape != q.shape:
+        raise PaError(1, f"out shape {tuple(out.shape)} != q shape {tuple(q.shape)}")
+    _need(k_cache, "k_cache", (torch.uint8, torch.float16, torch.bfloat16), 4)
+    _need(v_cache, "v_cache", (k_cache.dtype,), 4, optional=v_cache is None)
+    _need(block_table, "block_table", (torch.int32,), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1, optional=True)
+    _need(k_scale, "k_scale", (torch.float32,), optional=True)
+    _need(v_scale, "v_scale", (torch.float32,), optional=True)
     B, next_n, Hq, D = q.shape
-    return AttnArgs(out=_ptr(out), q=_ptr(q), q_dtype=DT_F16, k_cache=_ptr(k_cache),
+    return AttnArgs(out=_ptr(out), q=_ptr(q), q_dtype=_q_dtype(q), k_cache=_ptr(k_cache),
                     v_cache=_ptr(v_cache), kv_kind=kv_kind, k_scale=_ptr(k_scale),
                     k_scale_mode=_mode(k_scale, k_scale_mode), v_scale=_ptr(v_scale),
                     v_scale_mode=_mode(v_scale, v_scale_mode), block_table=_ptr(block_table),
@@ -206,9 +236,9 @@ def prepare_paged_attn_fwd(out, q, k_cache, v_cache, block_table, context_lens,
 def paged_attn_fwd(out, q, k_cache, v_cache, block_table, context_lens, max_context_len, *,
                    kv_kind, k_scale=None, v_scale=None, k_scale_mode=None, v_scale_mode=None,
                    softmax_scale=0.0, causal=True, workspace=None, stream=None):
-    """out[B, next_n, Hq, D] fp16 <- paged attention (see paged_attn_fwd in include/pa.h).
+    """out[B, next_n, Hq, D] <- paged attention (see paged_attn_fwd in include/pa.h).
 
-    q fp16 [B, next_n, Hq, D]; k_cache/v_cache uint8 [num_blocks, bs, Hkv, row_bytes];
+    q fp16 or bf16 [B, next_n, Hq, D], out of q's dtype; k_cache/v_cache uint8 [num_blocks, bs, Hkv, row_bytes];
     block_table int32 [B, max_blocks]; context_lens int32 [B]; scales fp32 [1] or [Hkv, D].
     The workspace (uint8 tensor) is allocated here when not given.
     """
@@ -287,7 +317,7 @@ def prepare_paged_attn_sparse(out, q, k_cache, v_cache, block_table, context_len
 def paged_attn_sparse(out, q, k_cache, v_cache, block_table, context_lens, max_context_len, sel,
                       *, kv_kind, k_scale=None, v_scale=None, k_scale_mode=None,
                       v_scale_mode=None, softmax_scale=0.0, workspace=None, stream=None):
-    """out[B, next_n, Hq, D] fp16 <- attention of each query row over the tokens
+    """out[B, next_n, Hq, D] (q's dtype) <- attention of each query row over the tokens
     it selected (sel int32 [B, next_n, topk] logical token ids; see
     paged_attn_sparse in include/pa.h). Other arguments as for paged_attn_fwd."""
     prepare_paged_attn_sparse(out, q, k_cache, v_cache, block_table, context_lens,
@@ -407,11 +437,20 @@ def paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_
 
 def kv_insert(k_cache, v_cache, k, v, slot_mapping, *, kv_kind, k_scale=None, v_scale=None,
               k_scale_mode=None, v_scale_mode=None, stream=None):
-    """Quantize rows k, v [T, Hkv, D] fp16 into the paged caches at slot_mapping (int64)."""
+    """Quantize rows k, v [T, Hkv, D] (fp16 or bf16) into the paged caches at
+    slot_mapping (int64)."""
+    import torch
+    _need(k, "k", (torch.float16, torch.bfloat16), 3)
+    _need(v, "v", (k.dtype,), 3)
+    _need(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    _need(k_cache, "k_cache", (torch.uint8, torch.float16, torch.bfloat16), 4)
+    _need(v_cache, "v_cache", (k_cache.dtype,), 4)
+    _need(k_scale, "k_scale", (torch.float32,), optional=True)
+    _need(v_scale, "v_scale", (torch.float32,), optional=True)
     T, Hkv, D = k.shape
     a = InsertArgs(k_cache=_ptr(k_cache), v_cache=_ptr(v_cache), kv_kind=kv_kind, k=_ptr(k),
-                   v=_ptr(v), in_dtype=DT_F16, slot_mapping=_ptr(slot_mapping), num_tokens=T,
-                   num_slots=slot_mapping.shape[0], num_kv_heads=Hkv, head_dim=D,
+                   v=_ptr(v), in_dtype=_q_dtype(k), slot_mapping=_ptr(slot_mapping),
+                   num_tokens=T, num_slots=slot_mapping.shape[0], num_kv_heads=Hkv, head_dim=D,
                    block_size=k_cache.shape[1], num_blocks=k_cache.shape[0],
                    k_scale=_ptr(k_scale), k_scale_mode=_mode(k_scale, k_scale_mode),
                    v_scale=_ptr(v_scale), v_scale_mode=_mode(v_scale, v_scale_mode))

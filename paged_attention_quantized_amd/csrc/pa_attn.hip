@@ -140,9 +140,23 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
     const float* vs = p.v_scale + hk * D + d;
     val *= f4{vs[0], vs[1], vs[2], vs[3]};
   }
-  _Float16* dst = p.out + (((size_t)b * p.next_n + i) * p.Hq + h) * D + d;
-  *reinterpret_cast<h4*>(dst) =
-      h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
+  const size_t at = (((size_t)b * p.next_n + i) * p.Hq + h) * D + d;
+  if (p.out_bf16) {
+    // round to nearest even on the fp32 bits (no NaN can reach here: a NaN
+    // keeps a quiet payload)
+    uint16_t hb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = __float_as_uint(val[e]);
+      hb[e] = val[e] != val[e] ? (uint16_t)((u >> 16) | 0x40u)
+                               : (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    }
+    *reinterpret_cast<u2*>(static_cast<uint16_t*>(p.out) + at) =
+        u2{hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16)};
+  } else {
+    *reinterpret_cast<h4*>(static_cast<_Float16*>(p.out) + at) =
+        h4{(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
+  }
 }
 
 // Planner probe: the page entries each sequence's tokens are read through, in
@@ -319,12 +333,12 @@ int device_cus() {
   return n;
 }
 
-PrefillFn pick_prefill_fn(int kind, int D, bool hilo) {
+PrefillFn pick_prefill_fn(int kind, int D, bool fold) {
   switch (kind) {
-    case PA_KV_F16: return pick_prefill_f16(D, hilo);
-    case PA_KV_E4M3: return pick_prefill_e4m3(D, hilo);
-    case PA_KV_INT8: return pick_prefill_int8(D, hilo);
-    case PA_KV_INT4: return pick_prefill_int4(D, hilo);
+    case PA_KV_F16: return pick_prefill_f16(D, fold);
+    case PA_KV_E4M3: return pick_prefill_e4m3(D, fold);
+    case PA_KV_INT8: return pick_prefill_int8(D, fold);
+    case PA_KV_INT4: return pick_prefill_int4(D, fold);
   }
   return nullptr;
 }
@@ -338,7 +352,8 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
     return fail(PA_ERR_INVALID_ARG, "paged_attn: num_q_heads %% num_kv_heads != 0");
   if (!valid_kind(a->kv_kind) || !valid_mode(a->k_scale_mode) || !valid_mode(a->v_scale_mode))
     return fail(PA_ERR_INVALID_ARG, "paged_attn: unknown kv_kind or scale mode");
-  if (a->q_dtype != PA_DT_F16) return fail(PA_ERR_UNSUPPORTED, "paged_attn: q_dtype must be F16");
+  if (a->q_dtype != PA_DT_F16 && a->q_dtype != PA_DT_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "paged_attn: q_dtype must be F16 or BF16");
   if (a->kv_kind == PA_KV_BF16) return fail(PA_ERR_UNSUPPORTED, "paged_attn: BF16 KV unsupported");
   if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
     return fail(PA_ERR_UNSUPPORTED, "paged_attn: head_dim must be 64, 128 or 256");
@@ -384,10 +399,6 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   int ts;
   if (sparse_topk >= 0) {
     // selection-driven mode: an item is one page of the union plan
-    if (a->kv_kind != PA_KV_F16 && a->kv_kind != PA_KV_E4M3)
-      return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: KV kind must be F16 or E4M3");
-    if (a->k_scale_mode == PA_SCALE_PER_CHANNEL || a->v_scale_mode == PA_SCALE_PER_CHANNEL)
-      return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: per-channel scales unsupported");
     if (a->next_n > kSparseRows || R > 32)
       return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: next_n <= 4 and next_n * G <= 32");
     if ((int64_t)a->max_blocks_per_seq > 32 * kPlanWords)
@@ -468,8 +479,10 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
 
 AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   AttnParams p;
-  p.out = (_Float16*)a->out;
-  p.q = (const _Float16*)a->q;
+  p.out = a->out;
+  p.q = (const uint16_t*)a->q;
+  p.q_bf16 = a->q_dtype == PA_DT_BF16;
+  p.out_bf16 = a->q_dtype == PA_DT_BF16;
   p.k_cache = (const uint8_t*)a->k_cache;
   p.v_cache = (const uint8_t*)a->v_cache;
   p.k_scale = a->k_scale;
@@ -507,14 +520,23 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
   return p;
 }
 
-RingFn pick_ring(int kind, int D, int nw, int RT, int hilo, int mode) {
+RingFn pick_ring(int kind, int D, int nw, int RT, int qf, int mode) {
   switch (kind) {
-    case PA_KV_F16: return pick_ring_f16(D, nw, RT, hilo, mode);
-    case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, hilo, mode);
-    case PA_KV_INT8: return pick_ring_int8(D, nw, RT, hilo, mode);
-    case PA_KV_INT4: return pick_ring_int4(D, nw, RT, hilo, mode);
+    case PA_KV_F16: return pick_ring_f16(D, nw, RT, qf, mode);
+    case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, qf, mode);
+    case PA_KV_INT8: return pick_ring_int8(D, nw, RT, qf, mode);
+    case PA_KV_INT4: return pick_ring_int4(D, nw, RT, qf, mode);
   }
   return nullptr;
+}
+
+// Q' format of the ring kernel: with at most 8 query rows per KV head the rows
+// are mirrored in the operand's upper 8 columns (and P packed the same way);
+// PER_CHANNEL K scales fold into hi + lo parts of Q'.
+int q_format(const pa_attn_args* a, const Shape& sh) {
+  const bool fold = a->k_scale_mode == PA_SCALE_PER_CHANNEL;
+  const bool pack = sh.nrb == 1 && sh.RT == 1 && sh.rpb <= 8;
+  return fold ? (pack ? kQPacked : kQSplit) : (pack ? kQDup : kQPlain);
 }
 
 // Enqueue the ring kernel and the merge for checked arguments.
@@ -527,10 +549,7 @@ pa_status launch_attn(const pa_attn_args* a, const Shape& sh, void* workspace, h
     launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * kPfWaves), s, p, a->block_table,
                  a->context_lens);
   } else {
-    // per-channel K scales: Q' hi/lo parts packed into one operand when a KV
-    // head has at most 8 query rows
-    const int qf = !hilo ? kQPlain : (sh.nrb == 1 && sh.RT == 1 && sh.R <= 8) ? kQPacked : kQSplit;
-    RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, qf,
+    RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, q_format(a, sh),
                           sh.nrb > 1 ? kModeRows : kModeDense);
     if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn: no kernel for this kind/shape");
     launch_timed(fn, dim3((unsigned)sh.nwg), dim3(64 * sh.nw), s, p, a->block_table,
@@ -626,7 +645,7 @@ extern "C" pa_status paged_attn_sparse(const pa_attn_args* a, const int32_t* sel
                 workspace_bytes);
   if (a->batch == 0) return PA_OK;
   if (topk > 0 && !sel) return fail(PA_ERR_INVALID_ARG, "paged_attn_sparse: sel is NULL");
-  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, kQPlain, kModeSparse);
+  RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, q_format(a, sh), kModeSparse);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: no kernel for this kind/shape");
   char* base = (char*)workspace + sh.ml_bytes + sh.o_bytes + sh.seq_bytes;
   int32_t* entries = (int32_t*)base;

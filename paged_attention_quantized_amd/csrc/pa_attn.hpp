@@ -16,21 +16,43 @@ constexpr int kXchBytes = 32 * 1024;   // LDS exchange buffer (ring + exchange =
 constexpr int kMaxNextN = 4096;        // query steps per sequence
 constexpr int kMaxRows = 8192;         // query rows per KV head (next_n * q heads per KV head)
 
-// Q' formats of the ring kernel. Per-tensor scales: Q' is q in fp16 (kQPlain).
+// Q' formats of the ring kernel. Per-tensor scales: Q' is q in fp16.
 // Per-channel K scales: Q' = q * k_scale / max|k_scale| in fp32, split into an
 // fp16 high part and an fp16 remainder, so the folded scale keeps ~22 bits.
-// kQSplit: the parts are two B operands, each summed by its own MFMA.
-// kQPacked (at most 8 query rows per KV head): one B operand carries the high
-// parts of rows 0-7 in columns 0-7 and the remainders in columns 8-15; a
-// rotation by 8 lanes inside each 16-lane row adds the two halves, so one MFMA
-// per k-step does the work of two and the remainder needs no registers.
-constexpr int kQPlain = 0, kQSplit = 1, kQPacked = 2;
+//   kQPlain:  one B operand, query row 16 rt + n in column n.
+//   kQSplit:  the fold's parts as two B operands, each summed by its own MFMA.
+//   kQPacked: (at most 8 query rows per KV head) one B operand carries the
+//             high parts of rows 0-7 in columns 0-7 and the remainders in
+//             columns 8-15; a rotation by 8 lanes inside each 16-lane row adds
+//             the two halves, so one MFMA per k-step does the work of two.
+//   kQDup:    (at most 8 rows, per-tensor scales) rows 0-7 in columns 0-7 and
+//             again in columns 8-15.
+// In the two packed forms (kQPacked, kQDup) lanes n and n + 8 of a 16-lane row
+// hold the same scores, and the softmax weights of the P V product travel as
+// an fp16 high part (columns 0-7) and an fp16 remainder (columns 8-15) of one
+// k = 16 operand; the halves of O and of the row sums are added when a
+// partial is written. In the other forms every lane carries both parts of its
+// four tokens in one k = 32 operand (high parts in slots 0-3, remainders in
+// 4-7) against the V codes repeated in both halves. Either way p keeps ~22
+// bits in the products, not fp16's 11.
+constexpr int kQPlain = 0, kQSplit = 1, kQPacked = 2, kQDup = 3;
+// per-channel fold (hi + lo Q' parts)
+__host__ __device__ constexpr bool qf_fold(int qf) { return qf == kQSplit || qf == kQPacked; }
+// query rows in columns 0-7, mirrored in 8-15 (P packed into one k = 16 operand)
+__host__ __device__ constexpr bool qf_pack(int qf) { return qf == kQPacked || qf == kQDup; }
+
+// The softmax weights are computed as p * 2^kPScale (the exponent offset is
+// one subtraction): the largest weight is 2^14 rather than 1, so the fp16
+// remainder of small weights stays out of fp16's subnormal range. O and the
+// row sums carry the same factor, which cancels in O / l.
+constexpr float kPScale = 14.0f;
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 struct AttnParams {
-  _Float16* out;
-  const _Float16* q;
+  void* out;           // fp16 or bf16 (out_bf16)
+  const uint16_t* q;   // fp16 or bf16 bits (q_bf16)
+  int q_bf16, out_bf16;
   const uint8_t* k_cache;
   const uint8_t* v_cache;
   const float* k_scale;
@@ -188,13 +210,16 @@ struct Geo {
 // inline asm so that the compiler does not treat the asynchronous LDS write as
 // something every later LDS read has to wait for (it would wait for the whole
 // ring); the ring's own vmcnt + barrier protocol orders writes and reads. The
-// asm sets M0 itself; nothing else in these kernels uses M0.
+// asm sets M0 itself; nothing else in these kernels uses M0. An LDS DMA that
+// reads M0 right after a scalar write of M0 needs one wait state on gfx950
+// (the compiler puts an s_nop between the pair when it emits them itself), so
+// the asm carries it too.
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, const uint8_t* lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   // the base is uniform by construction; saying so keeps it in SGPRs
   const uint64_t sb = uni64((uint64_t)(uintptr_t)sbase);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff),
-               "s"(sb)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v),
+               "v"(voff), "s"(sb)
                : "memory");
 }
 
@@ -396,46 +421,69 @@ __device__ __forceinline__ void issue_w(const AttnParams& p, const ItemPos& it, 
 }
 
 // Softmax state and Q' operands of one wave.
-template <int KIND, int D, int RT, int HILO>
+template <int KIND, int D, int RT, int QF>
 struct WaveState {
   h8 qa[RT][Geo<KIND, D>::KS];
-  h8 qb[RT][HILO == kQSplit ? Geo<KIND, D>::KS : 1];
+  h8 qb[RT][QF == kQSplit ? Geo<KIND, D>::KS : 1];
   f4 o[RT][Geo<KIND, D>::DV];
   float m_run[RT];
   f4 l_acc[RT];  // row sums of P, accumulated by the matrix cores (all 4 lanes of a row equal)
   int lim[RT];  // query row 16*rt+n sees tokens t <= lim
 };
 
+// Eight channels of a q row as fp32: fp16 values, or bf16 bits widened (a
+// bf16 value is the upper half of an fp32).
+__device__ __forceinline__ void load_q8(const uint16_t* src, bool bf16, bool valid, float* x) {
+  u4 raw = {0u, 0u, 0u, 0u};
+  if (valid) raw = *reinterpret_cast<const u4*>(src);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (bf16) {
+      x[2 * k] = __uint_as_float(raw[k] << 16);
+      x[2 * k + 1] = __uint_as_float(raw[k] & 0xFFFF0000u);
+    } else {
+      const h2 v = as_h2(raw[k]);
+      x[2 * k] = (float)v[0];
+      x[2 * k + 1] = (float)v[1];
+    }
+  }
+}
+
+// Row of the run's block that lane column n of row tile rt holds.
+template <int QF>
+__device__ __forceinline__ int lane_row(int rt, int n) {
+  return qf_pack(QF) ? (n & 7) : 16 * rt + n;
+}
+
 // Load Q' of (sequence b, row block rb, KV head hk) and reset the softmax
-// state. Local row 16 rt + n is query row rb * rpb + 16 rt + n.
-template <int KIND, int D, int RT, int HILO>
+// state. Local row lane_row(rt, n) is query row rb * rpb + that row.
+template <int KIND, int D, int RT, int QF>
 __device__ __forceinline__ void start_run(const AttnParams& p, int b, int rb, int hk, int L,
                                           float inv_m, float sgn,
-                                          WaveState<KIND, D, RT, HILO>& w) {
+                                          WaveState<KIND, D, RT, QF>& w) {
   using G_ = Geo<KIND, D>;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    // kQPacked: column n holds row n & 7 (its high part for n < 8)
-    const int rl = HILO == kQPacked ? (n & 7) : 16 * rt + n, r = rb * p.rpb + rl;
+    const int rl = lane_row<QF>(rt, n), r = rb * p.rpb + rl;
     const bool rv = rl < p.rpb && r < p.R;
     const int i = r / p.G, hg = r % p.G;
-    const _Float16* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
+    const uint16_t* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
 #pragma unroll
     for (int ks = 0; ks < G_::KS; ++ks) {
       const int j = ks / G_::KPC, u = ks % G_::KPC;
       const int d0 = (g + 4 * j) * G_::EPC + 8 * u;
-      h8 v = {};
-      if (rv) v = *reinterpret_cast<const h8*>(qrow + d0);
+      float xv[8];
+      load_q8(qrow + d0, p.q_bf16, rv, xv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = d0 + run_elem<KIND>(e);
-        const float x = (float)v[run_elem<KIND>(e)];
-        if constexpr (HILO) {
+        const float x = xv[run_elem<KIND>(e)];
+        if constexpr (qf_fold(QF)) {
           const float xf = x * (p.k_scale[hk * D + d] * inv_m) * sgn;
           const _Float16 hi = (_Float16)xf;
           const _Float16 lo = (_Float16)(xf - (float)hi);
-          if constexpr (HILO == kQPacked) {
+          if constexpr (QF == kQPacked) {
             w.qa[rt][ks][e] = n < 8 ? hi : lo;
           } else {
             w.qa[rt][ks][e] = hi;
@@ -509,12 +557,19 @@ __device__ __forceinline__ void pair_tokens(uint32_t xa, uint32_t xb, uint32_t& 
   }
 }
 
+// The two fp16 parts of a softmax weight: hi = fp16(x), lo = fp16(x - hi)
+// (x - hi is exact in fp32).
+__device__ __forceinline__ _Float16 p_lo(float x, _Float16 hi) { return (_Float16)(x - (float)hi); }
+
 // Softmax step of one row tile: new running max, rescale factor, P as the B
-// operand of the PV product. MASK = false when every query row sees all 16
-// tokens (none past the end or past a row's causal limit): no selects then.
-template <bool MASK>
+// operand of the P V product (PACK: the k = 16 form, lanes n < 8 the high
+// parts and n >= 8 the remainders, in pb[0..3]; otherwise the k = 32 form,
+// high parts in pb[0..3] and remainders in pb[4..7]). MASK = false when every
+// query row sees all 16 tokens (none past the end or past a row's causal
+// limit): no selects then.
+template <bool MASK, bool PACK>
 __device__ __forceinline__ void tile_softmax(const f4 s, uint32_t okbits, float c2, float& m_run,
-                                             float& alpha, bool& rescale, h4& pb) {
+                                             float& alpha, bool& rescale, h8& pb) {
   bool okv[4];
   float mx;
   if constexpr (MASK) {
@@ -534,18 +589,30 @@ __device__ __forceinline__ void tile_softmax(const f4 s, uint32_t okbits, float 
   // larger max; a row that has seen nothing holds zeros
   alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - m_new) * c2);
   rescale |= m_old != m_new && m_old != -INFINITY;
-  // exponent s * c2 - m * c2 as one fma (a row that saw only masked tokens
-  // keeps m = -inf; its p are selected to 0)
-  const float mc = m_new == -INFINITY ? 0.f : m_new * c2;
+  // exponent s * c2 - (m * c2 - kPScale) as one fma (a row that saw only
+  // masked tokens keeps m = -inf; its p are selected to 0)
+  const float mc = m_new == -INFINITY ? 0.f : m_new * c2 - kPScale;
   float pf[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     pf[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mc));
     if constexpr (MASK) pf[e] = okv[e] ? pf[e] : 0.f;
   }
-  const h2 p01 = {(_Float16)pf[0], (_Float16)pf[1]};
-  const h2 p23 = {(_Float16)pf[2], (_Float16)pf[3]};
-  pb = h4{p01[0], p01[1], p23[0], p23[1]};
+  if constexpr (PACK) {
+    const bool hi_lane = (threadIdx.x & 15) < 8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 hi = (_Float16)pf[e];
+      pb[e] = hi_lane ? hi : p_lo(pf[e], hi);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 hi = (_Float16)pf[e];
+      pb[e] = hi;
+      pb[4 + e] = p_lo(pf[e], hi);
+    }
+  }
   m_run = m_new;
 }
 
@@ -555,17 +622,19 @@ __device__ __forceinline__ void tile_softmax(const f4 s, uint32_t okbits, float 
 // sub-tile is valid for the lane's row when bit tin + 4g + e of rmask[rt] is
 // set (tin = the sub-tile's first token in its page), and its V codes are
 // kept when that bit is set in umask (some row selected it).
-template <int KIND, int D, int RT, int HILO, bool SPARSE = false>
+template <int KIND, int D, int RT, int QF, bool SPARSE = false>
 __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs<KIND, D>& to,
                                              int t0, int L, bool full, float c2,
-                                             WaveState<KIND, D, RT, HILO>& w,
+                                             WaveState<KIND, D, RT, QF>& w,
                                              const uint32_t* rmask = nullptr, uint32_t umask = 0,
                                              int tin = 0) {
   using G_ = Geo<KIND, D>;
   constexpr int KS = G_::KS, NJ = G_::NJ, KPC = G_::KPC, EPC = G_::EPC, DV = G_::DV;
   constexpr int VDW = G_::VDW, VB = G_::VB;
   constexpr int P = Kv<KIND>::kPairsPerDword;
+  constexpr bool PACK = qf_pack(QF);
   static_assert(VDW * 2 * P == DV, "V channels per lane");
+  static_assert(!PACK || RT == 1, "packed rows fill one row tile");
   const int lane = threadIdx.x & 63, g = lane >> 4;
 
   // ---- K operand: lane (n, g) holds token n, pieces g + 4j ----
@@ -622,10 +691,10 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qa[rt][ks], acc, 0, 0, 0);
-      if constexpr (HILO == kQSplit)
+      if constexpr (QF == kQSplit)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qb[rt][ks], acc, 0, 0, 0);
     }
-    if constexpr (HILO == kQPacked) {
+    if constexpr (QF == kQPacked) {
       // column n + high part of its row, from column (n + 8) mod 16 (row_ror:8);
       // both halves of the row end up with the same sum
 #pragma unroll
@@ -637,13 +706,13 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
   }
 
   // ---- online softmax (query row = lane column n) ----
-  h4 pb[RT];
+  h8 pb[RT];
   bool rescale = false;
   float alpha[RT];
   if (full) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
-      tile_softmax<false>(sacc[rt], 0xFu, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+      tile_softmax<false, PACK>(sacc[rt], 0xFu, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
   } else {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -657,7 +726,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
           okbits |= (uint32_t)(t < L && t <= w.lim[rt]) << e;
         }
       }
-      tile_softmax<true>(sacc[rt], okbits, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
+      tile_softmax<true, PACK>(sacc[rt], okbits, c2, w.m_run[rt], alpha[rt], rescale, pb[rt]);
     }
   }
   if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
@@ -670,7 +739,8 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
   }
 
   // ---- O^T += V^T P^T: the A operand of channel q is (tokens 4g .. 4g+3) of
-  // that channel, built straight from decodes of token-paired codes ----
+  // that channel, built straight from decodes of token-paired codes (and
+  // repeated for the remainder slots of the k = 32 form) ----
 #pragma unroll
   for (int k = 0; k < VDW; ++k) {
     // dword k of the lane's run: channels [2Pk, 2Pk + 2P), decoded and used at once
@@ -683,25 +753,38 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
 #pragma unroll
     for (int i = 0; i < 2 * P; ++i) {
       const h2 a = pr[i < P ? 0 : 1][i % P], b = pr[i < P ? 2 : 3][i % P];
-      const h4 vop = {a[0], a[1], b[0], b[1]};
       const int q = 2 * P * k + i;
+      if constexpr (PACK) {
+        const h4 vop = {a[0], a[1], b[0], b[1]};
+        const h4 pb4 = {pb[0][0], pb[0][1], pb[0][2], pb[0][3]};
+        w.o[0][q] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pb4, w.o[0][q], 0, 0, 0);
+      } else {
+        const h8 vop = {a[0], a[1], b[0], b[1], a[0], a[1], b[0], b[1]};
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pb[rt], w.o[rt][q], 0, 0, 0);
+        for (int rt = 0; rt < RT; ++rt)
+          w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pb[rt], w.o[rt][q], 0, 0, 0);
+      }
     }
   }
   // row sums of P on the matrix cores: every lane gets its row's sum
-  const h4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  if constexpr (PACK) {
+    const h4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+    const h4 pb4 = {pb[0][0], pb[0][1], pb[0][2], pb[0][3]};
+    w.l_acc[0] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb4, w.l_acc[0], 0, 0, 0);
+  } else {
+    const h8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                     (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-    w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb[rt], w.l_acc[rt], 0, 0, 0);
+    for (int rt = 0; rt < RT; ++rt)
+      w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rt], w.l_acc[rt], 0, 0, 0);
+  }
 }
 
 // Exchange of a wave's softmax state through LDS, in the MFMA register layout
 // (lane-major), so the receiving wave of the same head combines element-wise:
 // o as [rt][q][lane] f4, then m and l as [rt][lane] floats.
-template <int KIND, int D, int RT, int HILO>
-__device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, HILO>& w, float* xbuf) {
+template <int KIND, int D, int RT, int QF>
+__device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, QF>& w, float* xbuf) {
   constexpr int DV = Geo<KIND, D>::DV;
   const int lane = threadIdx.x & 63;
   f4* xo = reinterpret_cast<f4*>(xbuf);
@@ -715,8 +798,8 @@ __device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, HILO>& w, f
 }
 
 // Combine the state in xbuf into w (w first, then xbuf: a fixed order).
-template <int KIND, int D, int RT, int HILO>
-__device__ __forceinline__ void xch_merge(WaveState<KIND, D, RT, HILO>& w, const float* xbuf,
+template <int KIND, int D, int RT, int QF>
+__device__ __forceinline__ void xch_merge(WaveState<KIND, D, RT, QF>& w, const float* xbuf,
                                           float c2) {
   constexpr int DV = Geo<KIND, D>::DV;
   const int lane = threadIdx.x & 63;
@@ -755,18 +838,34 @@ __device__ __forceinline__ size_t part_index(const AttnParams& p, int r, int w, 
   return ((size_t)(r + w) * p.hpu + hl) * (p.wgmerge ? 1 : p.nsub) + st;
 }
 
-template <int KIND, int D, int RT, int HILO>
+// Adds column (n + 8) mod 16 of a packed state to column n (row_ror:8): the
+// remainder half of P's products joins the high half.
+__device__ __forceinline__ float add_ror8(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF,
+                                                        false));
+}
+
+// Write the wave's state as a partial. A packed state's halves are added
+// first, in place (the state is reset by the next start_run).
+template <int KIND, int D, int RT, int QF>
 __device__ __forceinline__ void write_partial(const AttnParams& p, size_t u, float c2,
-                                              const WaveState<KIND, D, RT, HILO>& w,
-                                              int row0 = 0) {
+                                              WaveState<KIND, D, RT, QF>& w, int row0 = 0) {
   constexpr int DV = Geo<KIND, D>::DV;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const float l = w.l_acc[rt][0];
-    const int r = row0 + 16 * rt + n;  // row of the run's block
-    if (r < p.rpb) {
-      if (g == 0) p.ws_ml[u * p.rpb + r] = f4{w.m_run[rt], l, c2, 0.f};
+    if constexpr (qf_pack(QF)) {
+      // lanes n < 8 hold the products of P's high parts, n + 8 the remainders
+      w.l_acc[rt][0] = add_ror8(w.l_acc[rt][0]);
+#pragma unroll
+      for (int q = 0; q < DV; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w.o[rt][q][e] = add_ror8(w.o[rt][q][e]);
+    }
+    // row of the run's block; packed states write from lanes n < 8 only
+    const int r = row0 + 16 * rt + n;
+    if (r < p.rpb && (!qf_pack(QF) || n < 8)) {
+      if (g == 0) p.ws_ml[u * p.rpb + r] = f4{w.m_run[rt], w.l_acc[rt][0], c2, 0.f};
       float* orow = p.ws_o + (u * p.rpb + r) * D;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -863,7 +962,7 @@ enum RingMode { kModeDense = 0, kModeSparse = 1, kModeRows = 2 };
 // MODE kModeSparse: table holds the union plan entries ({physical, logical}
 // per page), lens the per-sequence entry count times block_size, masks the row
 // masks. kModeRows: query rows come in p.nrb blocks of p.rpb rows.
-template <int KIND, int D, int RT, int HILO, int NWB, int MODE>
+template <int KIND, int D, int RT, int QF, int NWB, int MODE>
 __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
     const uint32_t* __restrict__ masks) {
@@ -890,7 +989,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   // the per-tensor K scale: its pointer is a scalar load of its own, so it is
   // read after the scan's length load has gone out
   const float ks_tensor =
-      (!HILO && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
+      (!qf_fold(QF) && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
   __syncthreads();
   // workgroup-uniform (read back from LDS, so say so to the compiler)
   const int nitems = uni(xi[0]);
@@ -910,7 +1009,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   // this wave's region of every ring stage
   uint8_t* const myring = ring + wv * (32 * G_::RB);
 
-  WaveState<KIND, D, RT, HILO> w;
+  WaveState<KIND, D, RT, QF> w;
 
   // ---- ring prologue: kStages - 1 items in flight; the block-table loads of
   // all of them (and of the next one) are issued before any is waited for ----
@@ -948,7 +1047,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   // fold normalizer for PER_CHANNEL K [FOLD, Approach], max|k_scale| with 8
   // loads in flight per lane ----
   float qk, inv_m = 0.f;
-  if constexpr (HILO) {
+  if constexpr (qf_fold(QF)) {
     float mx = 0.f;
     const int nks = p.Hkv * D;
     for (int i0 = 0; i0 < nks; i0 += 512) {
@@ -973,7 +1072,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
   // Q' of the first run: its loads follow the ring's first stages, so the
   // ring does not wait for them (the conversion waits for both; the first
   // compute needs the first stage anyway)
-  start_run<KIND, D, RT, HILO>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
+  start_run<KIND, D, RT, QF>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
   // SPARSE: row masks of the item being computed (mc) and of the next (mn),
   // loaded one iteration ahead; mp is the position of mn
   uint32_t mc[kSparseRows] = {0u, 0u, 0u, 0u}, mn[kSparseRows] = {0u, 0u, 0u, 0u};
@@ -997,7 +1096,7 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
       uint32_t rm[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int r = 16 * rt + (lane & 15);
+        const int r = lane_row<QF>(rt, lane & 15);
         const int i = r / p.G;
         uint32_t m = 0u;
 #pragma unroll
@@ -1015,11 +1114,11 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
       const uint32_t sub_any = (any >> (16 * st)) & 0xFFFFu;
       const uint32_t sub_all = (all >> (16 * st)) & 0xFFFFu;
       if (sub_any != 0u)
-        compute_tile<KIND, D, RT, HILO, true>(myring + (j % kStages) * stage_bytes, to, t0, cp.L,
+        compute_tile<KIND, D, RT, QF, true>(myring + (j % kStages) * stage_bytes, to, t0, cp.L,
                                               sub_all == 0xFFFFu, c2, w, rm, any, 16 * st);
     } else if (t0 < run_len(p, cp.L, cp.rb)) {
       // full: the block's first row (step first_step) sees all 16 tokens
-      compute_tile<KIND, D, RT, HILO>(
+      compute_tile<KIND, D, RT, QF>(
           myring + (j % kStages) * stage_bytes, to, t0, cp.L,
           t0 + 16 <= cp.L - (p.causal ? p.next_n - 1 - first_step(p, cp.rb) : 0), c2, w);
     }
@@ -1032,20 +1131,20 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
         // fold sub-tiles 1 .. nsub-1 of each head into sub-tile 0, in order
         for (int h = 0; h < p.hpu; ++h)
           for (int s2 = 1; s2 < p.nsub; ++s2) {
-            if (hl == h && st == s2) xch_put<KIND, D, RT, HILO>(w, xbuf);
+            if (hl == h && st == s2) xch_put<KIND, D, RT, QF>(w, xbuf);
             lds_barrier();
-            if (hl == h && st == 0) xch_merge<KIND, D, RT, HILO>(w, xbuf, c2);
+            if (hl == h && st == 0) xch_merge<KIND, D, RT, QF>(w, xbuf, c2);
             lds_barrier();
           }
         if (st == 0)
-          write_partial<KIND, D, RT, HILO>(p, part_index(p, run, blockIdx.x, hl, 0),
+          write_partial<KIND, D, RT, QF>(p, part_index(p, run, blockIdx.x, hl, 0),
                                            c2, w);
       } else {
-        write_partial<KIND, D, RT, HILO>(p, part_index(p, run, blockIdx.x, hl, st),
+        write_partial<KIND, D, RT, QF>(p, part_index(p, run, blockIdx.x, hl, st),
                                          c2, w);
       }
       if (j + 1 < nitems)
-        start_run<KIND, D, RT, HILO>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
+        start_run<KIND, D, RT, QF>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
     }
     // pages of the item the next iteration issues
     if (jn + 1 < nitems) load_page_w<KIND, D, SPARSE>(p, table, ld, wl, pg);
@@ -1148,10 +1247,10 @@ __device__ __forceinline__ void pf_decode(const uint8_t* slot, uint8_t* kdec, ui
 // Q of rows [row0, row0 + 32) of sequence b for KV head hk, in natural channel
 // order (k-step ks, lane group g: channels 32 ks + 8 g .. + 7), folded with a
 // PER_CHANNEL K scale as in start_run; resets the softmax state.
-template <int KIND, int D, bool HILO>
+template <int KIND, int D, int QF>
 __device__ __forceinline__ void pf_start_run(const AttnParams& p, int b, int row0, int hk, int L,
                                              float inv_m, float sgn,
-                                             WaveState<KIND, D, 2, HILO>& w) {
+                                             WaveState<KIND, D, 2, QF>& w) {
   using G_ = Geo<KIND, D>;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -1159,16 +1258,16 @@ __device__ __forceinline__ void pf_start_run(const AttnParams& p, int b, int row
     const int r = row0 + 16 * rt + n;
     const bool rv = r < p.R;
     const int i = r / p.G, hg = r % p.G;
-    const _Float16* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
+    const uint16_t* qrow = p.q + (((size_t)b * p.next_n + i) * p.Hq + hk * p.G + hg) * D;
 #pragma unroll
     for (int ks = 0; ks < G_::KS; ++ks) {
       const int d0 = 32 * ks + 8 * g;
-      h8 v = {};
-      if (rv) v = *reinterpret_cast<const h8*>(qrow + d0);
+      float xv[8];
+      load_q8(qrow + d0, p.q_bf16, rv, xv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (float)v[e];
-        if constexpr (HILO) {
+        const float x = xv[e];
+        if constexpr (qf_fold(QF)) {
           const float xf = x * (p.k_scale[hk * D + d0 + e] * inv_m) * sgn;
           const _Float16 hi = (_Float16)xf;
           w.qa[rt][ks][e] = hi;
@@ -1187,11 +1286,14 @@ __device__ __forceinline__ void pf_start_run(const AttnParams& p, int b, int row
 }
 
 // Softmax step over a pair of 16-token tiles (sa: tokens 4g + e, sb: tokens
-// 16 + 4g + e of the pair): P of the pair as one k = 32 operand, token order
-// {4g .. 4g + 3, 16 + 4g .. 16 + 4g + 3} in lane group g.
+// 16 + 4g + e of the pair): P of the pair as two k = 32 operands, the fp16
+// high parts (ph) and the fp16 remainders (pl), token order
+// {4g .. 4g + 3, 16 + 4g .. 16 + 4g + 3} in lane group g. The weights carry the
+// factor 2^kPScale, as in tile_softmax.
 template <bool MASK>
 __device__ __forceinline__ void pair_softmax(const f4 sa, const f4 sb, uint32_t okbits, float c2,
-                                             float& m_run, float& alpha, bool& rescale, h8& pb) {
+                                             float& m_run, float& alpha, bool& rescale, h8& ph,
+                                             h8& pl) {
   float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
   float mx = -INFINITY;
 #pragma unroll
@@ -1204,23 +1306,26 @@ __device__ __forceinline__ void pair_softmax(const f4 sa, const f4 sb, uint32_t 
   const float m_new = fmaxf(m_old, mx);
   alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - m_new) * c2);
   rescale |= m_old != m_new && m_old != -INFINITY;
+  const float mc = m_new == -INFINITY ? 0.f : m_new * c2 - kPScale;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float pf = __builtin_amdgcn_exp2f((s[e] - m_new) * c2);
+    float pf = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mc));
     if constexpr (MASK) pf = (okbits >> e) & 1u ? pf : 0.f;
-    pb[e] = (_Float16)pf;
+    const _Float16 hi = (_Float16)pf;
+    ph[e] = hi;
+    pl[e] = p_lo(pf, hi);
   }
   m_run = m_new;
 }
 
 // A pair of 16-token sub-tiles (stage tokens 32 u .. 32 u + 31, sequence
 // tokens t0 ..) for the wave's 32 rows from the decoded stage; P V and the row
-// sums run as k = 32 products over the pair. full: every row sees all 32
-// tokens.
-template <int KIND, int D, bool HILO>
+// sums run as k = 32 products over the pair, once with P's high parts and once
+// with its remainders. full: every row sees all 32 tokens.
+template <int KIND, int D, int QF>
 __device__ __forceinline__ void pf_pair(const uint8_t* kdec, const uint8_t* vdec, int u, int t0,
                                         int L, bool full, float c2,
-                                        WaveState<KIND, D, 2, HILO>& w) {
+                                        WaveState<KIND, D, 2, QF>& w) {
   using G_ = Geo<KIND, D>;
   using F_ = PfGeo<KIND, D>;
   constexpr int KS = G_::KS, DV = G_::DV;
@@ -1240,20 +1345,20 @@ __device__ __forceinline__ void pf_pair(const uint8_t* kdec, const uint8_t* vdec
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qa[rt][ks], acc, 0, 0, 0);
-        if constexpr (HILO)
+        if constexpr (qf_fold(QF))
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[ks], w.qb[rt][ks], acc, 0, 0, 0);
       }
       sacc[h][rt] = acc;
     }
   }
-  h8 pb[2];
+  h8 ph[2], pl[2];
   bool rescale = false;
   float alpha[2];
   if (full) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
       pair_softmax<false>(sacc[0][rt], sacc[1][rt], 0xFFu, c2, w.m_run[rt], alpha[rt], rescale,
-                          pb[rt]);
+                          ph[rt], pl[rt]);
   } else {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -1264,7 +1369,7 @@ __device__ __forceinline__ void pf_pair(const uint8_t* kdec, const uint8_t* vdec
         okbits |= (uint32_t)(t < L && t <= w.lim[rt]) << e;
       }
       pair_softmax<true>(sacc[0][rt], sacc[1][rt], okbits, c2, w.m_run[rt], alpha[rt], rescale,
-                         pb[rt]);
+                         ph[rt], pl[rt]);
     }
   }
   if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
@@ -1293,17 +1398,21 @@ __device__ __forceinline__ void pf_pair(const uint8_t* kdec, const uint8_t* vdec
       }
     }
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-      w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rt], w.o[rt][q], 0, 0, 0);
+    for (int rt = 0; rt < 2; ++rt) {
+      w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph[rt], w.o[rt][q], 0, 0, 0);
+      w.o[rt][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl[rt], w.o[rt][q], 0, 0, 0);
+    }
   }
   const h8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
                    (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-    w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[rt], w.l_acc[rt], 0, 0, 0);
+  for (int rt = 0; rt < 2; ++rt) {
+    w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, ph[rt], w.l_acc[rt], 0, 0, 0);
+    w.l_acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pl[rt], w.l_acc[rt], 0, 0, 0);
+  }
 }
 
-template <int KIND, int D, bool HILO>
+template <int KIND, int D, int QF>
 __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
     AttnParams p, const int32_t* __restrict__ table, const int32_t* __restrict__ lens) {
   using G_ = Geo<KIND, D>;
@@ -1315,7 +1424,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
   uint8_t* vdec = kdec + F_::KDEC;
   int* xi = reinterpret_cast<int*>(kdec);  // the scan result, read before any decode
   const int lane = threadIdx.x & 63, wv = uni(threadIdx.x >> 6);
-  const float ks_tensor = (!HILO && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
+  const float ks_tensor = (!qf_fold(QF) && p.k_scale_mode == PA_SCALE_PER_TENSOR) ? p.k_scale[0] : 1.0f;
   if (wv == 0) range_scan(p, lens, xi);
   __syncthreads();
   const int nitems = uni(xi[0]);
@@ -1334,7 +1443,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
 
   // rows of this wave inside its run's group, and the steps they span
   auto row0_of = [&](int rb) { return rb * p.rpb + 32 * wv; };
-  WaveState<KIND, D, 2, HILO> w;
+  WaveState<KIND, D, 2, QF> w;
 
   // ---- prologue: items 0 and 1 in flight, the pages of item 2 looked up ----
   ItemPos pos[kPfStages];
@@ -1359,7 +1468,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
 
   // scale constants and the first run's Q', behind the ring's first loads
   float qk, inv_m = 0.f;
-  if constexpr (HILO) {
+  if constexpr (qf_fold(QF)) {
     float mx = 0.f;
     const int nks = p.Hkv * D;
     for (int i0 = 0; i0 < nks; i0 += 512) {
@@ -1380,7 +1489,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
   }
   const float sgn = qk < 0.f ? -1.f : 1.f;
   const float c2 = fabsf(qk) * kLog2e;
-  pf_start_run<KIND, D, HILO>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
+  pf_start_run<KIND, D, QF>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
 
   for (int j = 0; j < nitems; ++j) {
     // item j has landed for every wave, and every wave is done with the
@@ -1404,7 +1513,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
       for (int u = 0; u < kPfTokens / 32; ++u) {
         const int t0 = tbase + 32 * u;
         if (t0 >= vis) break;
-        pf_pair<KIND, D, HILO>(kdec, vdec, u, t0, cp.L, t0 + 32 <= flim, c2, w);
+        pf_pair<KIND, D, QF>(kdec, vdec, u, t0, cp.L, t0 + 32 <= flim, c2, w);
       }
     }
     // end of a run inside this range: write the wave's rows of its partial
@@ -1413,10 +1522,10 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
     if (j + 1 == nitems || cp.b != b || cp.hg != hg || cp.rb != rb) {
       const int run = (b * p.nrb + rb) * p.hgroups + hg;
       if (row0_of(rb) < p.R)
-        write_partial<KIND, D, 2, HILO>(p, part_index(p, run, blockIdx.x, 0, 0), c2, w,
+        write_partial<KIND, D, 2, QF>(p, part_index(p, run, blockIdx.x, 0, 0), c2, w,
                                         32 * wv);
       if (j + 1 < nitems)
-        pf_start_run<KIND, D, HILO>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
+        pf_start_run<KIND, D, QF>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
     }
     if (jn + 1 < nitems) load_pages<KIND, D>(p, table, ld, lp, pg);
   }
@@ -1426,85 +1535,84 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
 typedef void (*PrefillFn)(AttnParams, const int32_t*, const int32_t*);
 
 template <int KIND, int D>
-PrefillFn pick_prefill_d(bool hilo) {
+PrefillFn pick_prefill_d(bool fold) {
   if constexpr (!PfGeo<KIND, D>::OK) {
     return nullptr;
   } else {
-    if (hilo) {
-      if constexpr (KIND == PA_KV_F16) return nullptr;
-      else return attn_prefill_kernel<KIND, D, true>;
+    if (fold) {
+      if constexpr (KIND == PA_KV_F16 || KIND == PA_KV_BF16) return nullptr;
+      else return attn_prefill_kernel<KIND, D, kQSplit>;
     }
-    return attn_prefill_kernel<KIND, D, false>;
+    return attn_prefill_kernel<KIND, D, kQPlain>;
   }
 }
 
 template <int KIND>
-PrefillFn pick_prefill(int D, bool hilo) {
+PrefillFn pick_prefill(int D, bool fold) {
   if constexpr (KIND != PA_KV_INT4)
-    if (D == 64) return pick_prefill_d<KIND, 64>(hilo);
-  if (D == 128) return pick_prefill_d<KIND, 128>(hilo);
+    if (D == 64) return pick_prefill_d<KIND, 64>(fold);
+  if (D == 128) return pick_prefill_d<KIND, 128>(fold);
   return nullptr;
 }
 
 typedef void (*RingFn)(AttnParams, const int32_t*, const int32_t*, const uint32_t*);
 
+// The ring kernel of one Q' format (kQPlain / kQSplit / kQPacked / kQDup) and
+// row-tile count. The folded formats exist for scaled kinds only, the packed
+// ones for one row tile, and the row-block mode has two row tiles.
+template <int KIND, int D, int NWB, int MODE>
+RingFn pick_qf(int RT, int qf) {
+  constexpr bool kFold = KIND != PA_KV_F16 && KIND != PA_KV_BF16;
+  if constexpr (MODE != kModeRows) {
+    if (RT == 1) {
+      if (qf == kQPlain) return attn_ring_kernel<KIND, D, 1, kQPlain, NWB, MODE>;
+      if (qf == kQDup) return attn_ring_kernel<KIND, D, 1, kQDup, NWB, MODE>;
+      if constexpr (kFold) {
+        if (qf == kQSplit) return attn_ring_kernel<KIND, D, 1, kQSplit, NWB, MODE>;
+        if (qf == kQPacked) return attn_ring_kernel<KIND, D, 1, kQPacked, NWB, MODE>;
+      }
+      return nullptr;
+    }
+  }
+  if (RT == 2) {
+    if (qf == kQPlain) return attn_ring_kernel<KIND, D, 2, kQPlain, NWB, MODE>;
+    if constexpr (kFold)
+      if (qf == kQSplit) return attn_ring_kernel<KIND, D, 2, kQSplit, NWB, MODE>;
+  }
+  return nullptr;
+}
+
 // NWB: the launch bound in waves (4 or 8); a 4-wave workgroup gets twice the
 // registers per wave. Row tiles RT are 1 or 2 (16 or 32 rows): more rows come
-// in row blocks of 32 (kModeRows). The sparse mode exists for FP16 and
-// per-tensor E4M3 caches, up to 32 query rows per KV head.
+// in row blocks of 32 (kModeRows).
 template <int KIND, int D, int NWB>
-RingFn pick_rt(int RT, int hilo, int mode) {
-  if (RT != 1 && RT != 2) return nullptr;
-  if (mode == kModeSparse) {
-    if constexpr (KIND == PA_KV_F16 || KIND == PA_KV_E4M3) {
-      if (hilo) return nullptr;
-      if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, kModeSparse>;
-      return attn_ring_kernel<KIND, D, 2, false, NWB, kModeSparse>;
-    }
-    return nullptr;
-  }
-  if (mode == kModeRows) {
-    if (RT != 2 || hilo == kQPacked) return nullptr;
-    if (hilo) {
-      if constexpr (KIND == PA_KV_F16) return nullptr;
-      else return attn_ring_kernel<KIND, D, 2, kQSplit, NWB, kModeRows>;
-    }
-    return attn_ring_kernel<KIND, D, 2, false, NWB, kModeRows>;
-  }
-  if (hilo) {
-    if constexpr (KIND == PA_KV_F16) return nullptr;
-    else {
-      if (hilo == kQPacked)
-        return RT == 1 ? attn_ring_kernel<KIND, D, 1, kQPacked, NWB, kModeDense> : nullptr;
-      if (RT == 1) return attn_ring_kernel<KIND, D, 1, kQSplit, NWB, kModeDense>;
-      return attn_ring_kernel<KIND, D, 2, kQSplit, NWB, kModeDense>;
-    }
-  }
-  if (RT == 1) return attn_ring_kernel<KIND, D, 1, false, NWB, kModeDense>;
-  return attn_ring_kernel<KIND, D, 2, false, NWB, kModeDense>;
+RingFn pick_rt(int RT, int qf, int mode) {
+  if (mode == kModeSparse) return pick_qf<KIND, D, NWB, kModeSparse>(RT, qf);
+  if (mode == kModeRows) return pick_qf<KIND, D, NWB, kModeRows>(RT, qf);
+  return pick_qf<KIND, D, NWB, kModeDense>(RT, qf);
 }
 
 template <int KIND, int D>
-RingFn pick_nw(int nw, int RT, int hilo, int mode) {
-  return nw <= 4 ? pick_rt<KIND, D, 4>(RT, hilo, mode) : pick_rt<KIND, D, 8>(RT, hilo, mode);
+RingFn pick_nw(int nw, int RT, int qf, int mode) {
+  return nw <= 4 ? pick_rt<KIND, D, 4>(RT, qf, mode) : pick_rt<KIND, D, 8>(RT, qf, mode);
 }
 
 template <int KIND>
-RingFn pick_d(int D, int nw, int RT, int hilo, int mode) {
+RingFn pick_d(int D, int nw, int RT, int qf, int mode) {
   if constexpr (KIND != PA_KV_INT4)
-    if (D == 64) return pick_nw<KIND, 64>(nw, RT, hilo, mode);
-  if (D == 128) return pick_nw<KIND, 128>(nw, RT, hilo, mode);
-  return pick_nw<KIND, 256>(nw, RT, hilo, mode);
+    if (D == 64) return pick_nw<KIND, 64>(nw, RT, qf, mode);
+  if (D == 128) return pick_nw<KIND, 128>(nw, RT, qf, mode);
+  return pick_nw<KIND, 256>(nw, RT, qf, mode);
 }
 
 // Ring kernel of one KV kind (each defined in its own translation unit).
-RingFn pick_ring_f16(int D, int nw, int RT, int hilo, int mode);
-RingFn pick_ring_e4m3(int D, int nw, int RT, int hilo, int mode);
-RingFn pick_ring_int8(int D, int nw, int RT, int hilo, int mode);
-RingFn pick_ring_int4(int D, int nw, int RT, int hilo, int mode);
-PrefillFn pick_prefill_f16(int D, bool hilo);
-PrefillFn pick_prefill_e4m3(int D, bool hilo);
-PrefillFn pick_prefill_int8(int D, bool hilo);
-PrefillFn pick_prefill_int4(int D, bool hilo);
+RingFn pick_ring_f16(int D, int nw, int RT, int qf, int mode);
+RingFn pick_ring_e4m3(int D, int nw, int RT, int qf, int mode);
+RingFn pick_ring_int8(int D, int nw, int RT, int qf, int mode);
+RingFn pick_ring_int4(int D, int nw, int RT, int qf, int mode);
+PrefillFn pick_prefill_f16(int D, bool fold);
+PrefillFn pick_prefill_e4m3(int D, bool fold);
+PrefillFn pick_prefill_int8(int D, bool fold);
+PrefillFn pick_prefill_int4(int D, bool fold);
 
 }  // namespace pa

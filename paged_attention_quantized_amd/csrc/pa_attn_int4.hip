@@ -3,10 +3,10 @@
 
 namespace pa {
 
-RingFn pick_ring_int4(int D, int nw, int RT, int hilo, int mode) {
-  return pick_d<PA_KV_INT4>(D, nw, RT, hilo, mode);
+RingFn pick_ring_int4(int D, int nw, int RT, int qf, int mode) {
+  return pick_d<PA_KV_INT4>(D, nw, RT, qf, mode);
 }
 
-PrefillFn pick_prefill_int4(int D, bool hilo) { return pick_prefill<PA_KV_INT4>(D, hilo); }
+PrefillFn pick_prefill_int4(int D, bool fold) { return pick_prefill<PA_KV_INT4>(D, fold); }
 
 }  // namespace pa

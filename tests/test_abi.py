@@ -62,7 +62,7 @@ def test_workspace_size_positive_and_shape_only():
 
 @pytest.mark.parametrize("field,value,status", [
     ("batch", -1, 1), ("num_kv_heads", 3, 1), ("head_dim", 100, 2), ("block_size", 8, 2),
-    ("q_dtype", 1, 2), ("kv_kind", 9, 1), ("k_scale_mode", 7, 1), ("next_n", 0, 1),
+    ("q_dtype", 2, 2), ("q_dtype", 7, 2), ("kv_kind", 9, 1), ("k_scale_mode", 7, 1), ("next_n", 0, 1),
     ("softmax_scale", -1.0, 1), ("max_blocks_per_seq", 100, 3), ("out", None, 1),
     ("k_scale", None, 1),
 ])

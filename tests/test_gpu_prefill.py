@@ -16,7 +16,8 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.gpu_util import DevAttn, compare_attn, oracle_attn, run_attn, say
+from tests.gpu_util import (DevAttn, compare_attn, compare_attn_conditioned, log_parity,
+                            oracle_attn, run_attn, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,17 +115,18 @@ def test_step_slices_match_full_oracle():
 
 
 def test_full_fp8_prefill(pa):
-    """The benchmark's workload in its launch configuration: the first 2 and
-    last 2 query steps of sampled sequences against the oracle, every output
-    finite, and a relocation of all pages bit-identical."""
+    """The benchmark's workload in its launch configuration: every query row
+    of every sequence against the oracle, and a relocation of all pages
+    bit-identical."""
     case = W.fp8_prefill()
     say(f"full {case.name}: B={case.batch} next_n={case.next_n} "
         f"tokens={int(case.context_lens.sum())}")
     got = run_attn(pa, case)
     assert not np.isnan(got.astype(np.float32)).any()
-    sub = case.sub_batch([1, 6])
-    r1 = compare_attn(got[[1, 6], :2], oracle_attn(first_steps(sub, 2)), case.name + " first")
-    r2 = compare_attn(got[[1, 6], -2:], oracle_attn(last_steps(sub, 2)), case.name + " last")
-    say(f"{case.name}: sampled max err/tol = {max(r1, r2):.3f}")
+    say("full prefill: oracle")
+    ref, cond, vr = oracle_attn(case, conditioning=True)
+    st = compare_attn_conditioned(got, ref, cond, vr, case.name)
+    say(f"{case.name}: {st}")
+    log_parity({"test": "full", "case": case.name, **st})
     other = run_attn(pa, W.relocate(case, 41))
     assert np.array_equal(other.view(np.uint16), got.view(np.uint16))

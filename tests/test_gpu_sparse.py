@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import DevAttn, compare_attn, dev, say
+from tests.gpu_util import (DevAttn, compare_attn, compare_attn_conditioned, dev, log_parity,
+                            say)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +40,19 @@ def small_cases():
     c = W.attn_case("sp_f16_nosel_scale", 2105, B=2, next_n=3, Hq=4, Hkv=4, D=128, bs=16,
                     lens=[64, 200], kv_kind=W.KV_F16, scale_mode=W.SCALE_NONE)
     out.append(W.with_selection(c, 2205, 5, window=2))
+    # integer kinds with per-channel K and V scales (the fold of the dense path)
+    c = W.attn_case("sp_int8_perchan", 2106, B=3, next_n=2, Hq=16, Hkv=2, D=256, bs=32,
+                    lens=[800, 97, 3], kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_CHANNEL,
+                    q_dist=(-100.0, 100.0), zero_k_channel_frac=0.1,
+                    v_scale_range=(1e-2, 65504.0 / 127))
+    out.append(W.with_selection(c, 2206, 80, window=20))
+    c = W.attn_case("sp_int4_perchan", 2108, B=2, next_n=4, Hq=8, Hkv=1, D=128, bs=16,
+                    lens=[600, 45], kv_kind=W.KV_INT4, scale_mode=W.SCALE_PER_CHANNEL,
+                    q_dist=(-100.0, 100.0), zero_k_channel_frac=0.1)
+    out.append(W.with_selection(c, 2208, 70, window=10))
+    c = W.attn_case("sp_int4_pt_rt2", 2109, B=2, next_n=4, Hq=32, Hkv=4, D=256, bs=32,
+                    lens=[333, 64], kv_kind=W.KV_INT4, scale_mode=W.SCALE_PER_TENSOR)
+    out.append(W.with_selection(c, 2209, 50, window=12))
     return out
 
 
@@ -69,17 +83,19 @@ def empty_rows(case, sel):
     return e
 
 
-@pytest.mark.parametrize("idx", range(5))
+@pytest.mark.parametrize("idx", range(8))
 def test_sparse_small_parity(pa, idx):
     case, sel = small_cases()[idx]
     say(f"sparse parity {case.name} B={case.batch} next_n={case.next_n} "
         f"lens={list(case.context_lens)} topk={sel.shape[2]}")
     got = run_sparse(pa, case, sel)
-    ref = oracle_sparse(case, sel)
-    r = compare_attn(got, ref, case.name)
+    ref, cond, vr = oracle.paged_attn_sparse(case.q, case.k_cache, case.v_cache, case.kv_kind,
+                                             case.block_table, case.context_lens, sel,
+                                             conditioning=True, **case.oracle_kwargs())
+    st = compare_attn_conditioned(got, ref, cond, vr, case.name)
     e = empty_rows(case, sel)
     assert np.all(got[e].view(np.uint16) == 0)  # +0 bits
-    say(f"{case.name}: max err/tol = {r:.3f}, empty rows {int(e.sum())}")
+    say(f"{case.name}: {st}, empty rows {int(e.sum())}")
 
 
 def test_sparse_plan_probe(pa):
@@ -102,7 +118,7 @@ def test_sparse_plan_probe(pa):
         assert np.array_equal(m, rm)
 
 
-@pytest.mark.parametrize("idx", [0, 3])
+@pytest.mark.parametrize("idx", [0, 3, 5, 6])
 def test_sparse_relocation_and_selection_order_bit_identical(pa, idx):
     case, sel = small_cases()[idx]
     say(f"sparse relocation {case.name}")
@@ -164,13 +180,14 @@ def test_sparse_args_errors(pa):
     case, sel = small_cases()[0]
     d = DevAttn(case)
     out = torch.empty(case.q.shape, dtype=torch.float16, device="cuda")
-    i8 = W.attn_case("sp_i8", 2107, B=1, next_n=1, Hq=4, Hkv=1, D=128, bs=16, lens=[20],
+    # more than 4 query steps per sequence: no sparse kernel
+    i8 = W.attn_case("sp_i8", 2107, B=1, next_n=5, Hq=4, Hkv=1, D=128, bs=16, lens=[20],
                      kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_TENSOR)
     di = DevAttn(i8)
     with pytest.raises(pa.PaError, match="UNSUPPORTED"):
         pa.paged_attn_sparse(torch.empty(i8.q.shape, dtype=torch.float16, device="cuda"), di.q,
                              di.k, di.v, di.bt, di.cl, i8.max_context_len,
-                             dev(np.zeros((1, 1, 4), np.int32)), kv_kind=i8.kv_kind,
+                             dev(np.zeros((1, 5, 4), np.int32)), kv_kind=i8.kv_kind,
                              k_scale=di.ks, v_scale=di.vs)
     with pytest.raises(pa.PaError, match="WORKSPACE"):
         pa.paged_attn_sparse(out, d.q, d.k, d.v, d.bt, d.cl, case.max_context_len, dev(sel),
@@ -179,17 +196,19 @@ def test_sparse_args_errors(pa):
 
 
 def test_full_fp8_sparse_verify(pa):
-    """The benchmark's workload in its launch configuration; sampled sequences
+    """The benchmark's workload in its launch configuration; every sequence
     against the oracle, then a relocation of all pages (bit-identical)."""
     case, sel = W.fp8_sparse_verify()
     say(f"full {case.name}: B={case.batch} tokens={int(case.context_lens.sum())} "
         f"topk={sel.shape[2]}")
     got = run_sparse(pa, case, sel)
     assert not np.isnan(got.astype(np.float32)).any()
-    sample = [2, 9]
-    ref = oracle_sparse(case.sub_batch(sample), np.ascontiguousarray(sel[sample]))
-    r = compare_attn(got[sample], ref, case.name)
-    say(f"{case.name}: sampled max err/tol = {r:.3f}")
+    ref, cond, vr = oracle.paged_attn_sparse(case.q, case.k_cache, case.v_cache, case.kv_kind,
+                                             case.block_table, case.context_lens, sel,
+                                             conditioning=True, **case.oracle_kwargs())
+    st = compare_attn_conditioned(got, ref, cond, vr, case.name)
+    say(f"{case.name}: {st}")
+    log_parity({"test": "full", "case": case.name, **st})
     other = run_sparse(pa, W.relocate(case, 21), sel)
     assert np.array_equal(other.view(np.uint16), got.view(np.uint16))
 

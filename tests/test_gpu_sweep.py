@@ -5,13 +5,15 @@ prefill paths.
 Each case draws the KV kind and scale mode, head_dim, block size, KV heads,
 query heads per KV head, query steps (up to prefill-sized row counts, so the
 ring kernel's dense, row-block and the prefill layouts are all exercised),
-the causal flag and ragged lengths including empty sequences. Values are
-those of roughly unit-normal data: INT scales (per tensor or per channel) as
-if max|x| / 127 (or / 7) with |x| <= 5. The extreme per-channel distribution
-(scales up to 1e3, q up to 100) has its own full-size tests. Tolerance as in
-the other attention tests:
-|gpu - oracle| <= max(2e-3, 1 fp16 ulp of the oracle value); rows that see no
-token are +0.
+the causal flag, fp16 or bf16 queries and ragged lengths including empty
+sequences. Values span the input generator's full ranges: per-tensor INT
+scales uniform in [0.01, 2], per-channel K and V scales log-uniform in
+[1e-2, 1e3] (INT8 V up to 65504/127) with q uniform in [-100, 100] and 10% of
+K channels zero. Tolerance: |gpu - oracle| <= max(2e-3, 1 ulp of the output
+type at the oracle value); rows whose fp64 top-2 score gap is below 8x the
+fp32 score-error bound are classified ill-conditioned and checked for lying
+within the V range of the tokens that can carry weight (the counts are
+printed and, with $PA_PARITY_LOG set, logged). Rows that see no token are +0.
 """
 import numpy as np
 import pytest
@@ -19,12 +21,13 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import DevAttn, compare_attn, dev, oracle_attn, run_attn, say
+from tests.gpu_util import (DevAttn, compare_attn, compare_attn_conditioned, dev, log_parity,
+                            oracle_attn, run_attn, say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
-N_DENSE = 64
-N_SPARSE = 8
+N_DENSE = 72
+N_SPARSE = 12
 
 
 def dense_case(i):
@@ -48,49 +51,67 @@ def dense_case(i):
         mode = W.SCALE_PER_TENSOR
     else:
         mode = [W.SCALE_PER_TENSOR, W.SCALE_PER_CHANNEL][i % 2]
-    lim = 127 if kind == W.KV_INT8 else 7
-    rng_scale = (2.0 / lim, 5.0 / lim)
-    kw = dict(pt_scale_range=rng_scale)
+    kw = {}
     if mode == W.SCALE_PER_CHANNEL:
-        kw = dict(zero_k_channel_frac=0.1, k_scale_range=rng_scale, v_scale_range=rng_scale)
+        # the generator's per-channel distribution: K and V scales log-uniform in
+        # [1e-2, 1e3] (INT8 V up to 65504/127 so V stays finite in fp16), q in
+        # [-100, 100], 10% of K channels zero
+        kw = dict(zero_k_channel_frac=0.1, q_dist=(-100.0, 100.0),
+                  v_scale_range=(1e-2, 65504.0 / 127) if kind == W.KV_INT8 else (1e-2, 1e3))
     return W.attn_case(f"sweep{i}_k{kind}_d{D}_bs{bs}_h{Hkv}x{G}_n{next_n}", 6000 + i, B=B,
                        next_n=next_n, Hq=Hkv * G, Hkv=Hkv, D=D, bs=bs, lens=lens, kv_kind=kind,
                        scale_mode=mode, causal=bool(i % 4 != 3),
                        max_context_len=max(1, max(lens)), **kw)
 
 
+def bf16_query(i):
+    return i % 5 == 1
+
+
 @pytest.mark.parametrize("i", range(N_DENSE))
 def test_dense_sweep(pa, i):
     case = dense_case(i)
-    say(f"sweep {case.name} lens={list(case.context_lens)} causal={case.causal}")
-    got = run_attn(pa, case)
-    ref = oracle_attn(case)
-    r = compare_attn(got, ref, case.name)
-    say(f"{case.name}: max err/tol = {r:.3f}")
+    bf = bf16_query(i)
+    say(f"sweep {case.name} lens={list(case.context_lens)} causal={case.causal} bf16={bf}")
+    d = DevAttn(case, bf16=bf)
+    got = to_f64(d.run(pa))
+    ref, cond, vr = oracle_attn(case, conditioning=True, q=d.q.cpu() if bf else None)
+    st = compare_attn_conditioned(got, ref, cond, vr, case.name, "bf16" if bf else "f16")
+    say(f"{case.name}: {st}")
+    log_parity({"test": "dense_sweep", "case": case.name, "bf16": bf, **st})
 
 
 def sparse_case(i):
     rng = np.random.default_rng(7000 + i)
-    kind = [W.KV_F16, W.KV_E4M3][i % 2]
-    D = int(rng.choice([64, 128, 256]))
+    kind = [W.KV_F16, W.KV_E4M3, W.KV_INT8, W.KV_INT4][i % 4]
+    D = int(rng.choice([128, 256] if kind == W.KV_INT4 else [64, 128, 256]))
     bs = int(rng.choice([16, 32]))
     Hkv = int(rng.choice([1, 2, 4]))
     next_n = int(rng.integers(1, 5))
     G = int(rng.choice([g for g in (1, 2, 4, 8) if g * next_n <= 32]))
     B = int(rng.integers(1, 5))
     lens = [int(x) for x in rng.integers(0, 900, B)]
-    case = W.attn_case(f"ssweep{i}_k{kind}_d{D}_bs{bs}_h{Hkv}x{G}_n{next_n}", 8000 + i, B=B,
-                       next_n=next_n, Hq=Hkv * G, Hkv=Hkv, D=D, bs=bs, lens=lens, kv_kind=kind,
-                       scale_mode=W.SCALE_NONE if kind == W.KV_F16 else W.SCALE_PER_TENSOR,
-                       max_context_len=max(1, max(lens)))
+    if kind == W.KV_F16:
+        mode = W.SCALE_NONE
+    elif kind == W.KV_E4M3:
+        mode = W.SCALE_PER_TENSOR
+    else:
+        mode = [W.SCALE_PER_TENSOR, W.SCALE_PER_CHANNEL][(i // 4) % 2]
+    kw = {}
+    if mode == W.SCALE_PER_CHANNEL:
+        kw = dict(zero_k_channel_frac=0.1, q_dist=(-100.0, 100.0),
+                  v_scale_range=(1e-2, 65504.0 / 127) if kind == W.KV_INT8 else (1e-2, 1e3))
+    case = W.attn_case(f"ssweep{i}_k{kind}_s{mode}_d{D}_bs{bs}_h{Hkv}x{G}_n{next_n}", 8000 + i,
+                       B=B, next_n=next_n, Hq=Hkv * G, Hkv=Hkv, D=D, bs=bs, lens=lens,
+                       kv_kind=kind, scale_mode=mode, max_context_len=max(1, max(lens)), **kw)
     return W.with_selection(case, 9000 + i, int(rng.integers(1, 120)),
                             window=int(rng.integers(1, 40)))
 
 
-def run_sparse(pa, case, sel, workspace=None, out=None):
-    d = DevAttn(case)
+def run_sparse(pa, case, sel, workspace=None, out=None, bf16=False):
+    d = DevAttn(case, bf16=bf16)
     if out is None:
-        out = torch.full(case.q.shape, float("nan"), dtype=torch.float16, device="cuda")
+        out = torch.full(case.q.shape, float("nan"), dtype=d.q.dtype, device="cuda")
     pa.paged_attn_sparse(out, d.q, d.k, d.v, d.bt, d.cl, case.max_context_len, dev(sel),
                          kv_kind=case.kv_kind, k_scale=d.ks, v_scale=d.vs,
                          k_scale_mode=case.k_scale_mode, v_scale_mode=case.v_scale_mode,
@@ -102,13 +123,17 @@ def run_sparse(pa, case, sel, workspace=None, out=None):
 @pytest.mark.parametrize("i", range(N_SPARSE))
 def test_sparse_sweep(pa, i):
     case, sel = sparse_case(i)
-    say(f"sparse sweep {case.name} lens={list(case.context_lens)} topk={sel.shape[2]}")
-    got = run_sparse(pa, case, sel).cpu().numpy()
-    ref = oracle.paged_attn_sparse(case.q, case.k_cache, case.v_cache, case.kv_kind,
-                                   case.block_table, case.context_lens, sel,
-                                   **case.oracle_kwargs())
-    r = compare_attn(got, ref, case.name)
-    say(f"{case.name}: max err/tol = {r:.3f}")
+    bf = bf16_query(i)
+    say(f"sparse sweep {case.name} lens={list(case.context_lens)} topk={sel.shape[2]} bf16={bf}")
+    out = run_sparse(pa, case, sel, bf16=bf)
+    got = to_f64(out)
+    q = DevAttn(case, bf16=True).q.cpu() if bf else case.q
+    ref, cond, vr = oracle.paged_attn_sparse(q, case.k_cache, case.v_cache, case.kv_kind,
+                                             case.block_table, case.context_lens, sel,
+                                             conditioning=True, **case.oracle_kwargs())
+    st = compare_attn_conditioned(got, ref, cond, vr, case.name, "bf16" if bf else "f16")
+    say(f"{case.name}: {st}")
+    log_parity({"test": "sparse_sweep", "case": case.name, "bf16": bf, **st})
 
 
 def replay_check(eager, out, g, again):

@@ -132,8 +132,109 @@ def pin_poison_insensitive(lib):
         assert np.array_equal(got.view(np.uint64), base.view(np.uint64)), case.name
 
 
+def pin_bf16_q(lib):
+    """bf16 queries: the oracle reads their bits as bf16 (brute force on the
+    same values through torch's bfloat16 cast)."""
+    import dataclasses
+
+    import torch
+    for case in tiny_cases()[1:4]:
+        qb = torch.from_numpy(case.q.astype(np.float32) * 3.0).to(torch.bfloat16)
+        got = oracle.paged_attn(qb, case.k_cache, case.v_cache, case.kv_kind, case.block_table,
+                                case.context_lens, lib=lib, **case.oracle_kwargs())
+        ref = brute.attention_sdpa(dataclasses.replace(case, q=qb.float().numpy()))
+        scale = max(1.0, float(np.abs(ref).max()))
+        np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-9 * scale, err_msg=case.name)
+
+
+def pin_thread_count_invariant(lib):
+    """The parallel loops split independent units: 1 or 5 threads give the
+    same bits."""
+    case = tiny_cases()[2]
+    oracle.set_threads(1, lib)
+    one = run_oracle(case, lib)
+    oracle.set_threads(5, lib)
+    five = run_oracle(case, lib)
+    oracle.set_threads(0, lib)
+    assert np.array_equal(one.view(np.uint64), five.view(np.uint64))
+
+
+def brute_conditioning(case):
+    """fp64 scores from library-decoded K, their top-2 gap, the fp32
+    score-error bound (the formula stated in orc_paged_attn's header) and the
+    V range over the relevant tokens, per output row."""
+    D = case.head_dim
+    K = brute.dequant_cache(case.k_cache, case.kv_kind, D, case.k_scale, case.k_scale_mode)
+    C = brute.decode_cache(case.k_cache, case.kv_kind, D)
+    V = brute.dequant_cache(case.v_cache, case.kv_kind, D, case.v_scale, case.v_scale_mode)
+    fold = case.k_scale_mode == W.SCALE_PER_CHANNEL
+    kmax = float(np.abs(case.k_scale).max()) if fold else 0.0
+    B, N, Hq, _ = case.q.shape
+    G = Hq // case.num_kv_heads
+    out = {}
+    for b in range(B):
+        L = int(case.context_lens[b])
+        kb = brute.gather(K, case.block_table[b], L, case.block_size).astype(np.float64)
+        cb = brute.gather(C, case.block_table[b], L, case.block_size).astype(np.float64)
+        vb = brute.gather(V, case.block_table[b], L, case.block_size).astype(np.float64)
+        for i in range(N):
+            nvis = min(L, L - N + i + 1) if case.causal else L
+            for h in range(Hq):
+                hk = h // G
+                if nvis <= 0:
+                    continue
+                q = case.q[b, i, h].astype(np.float64)
+                prod = q[None, :] * kb[:nvis, hk]
+                s = case.softmax_scale * prod.sum(1)
+                eps = case.softmax_scale * ((D + 8) * 2.0 ** -24 * np.abs(prod).sum(1) +
+                                            2.0 ** -25 * kmax * np.abs(cb[:nvis, hk]).sum(1))
+                srt = np.sort(s)
+                gap = srt[-1] - srt[-2] if nvis >= 2 else np.inf
+                e = eps.max()
+                rel = s >= srt[-1] - 8 * e - 32
+                p = np.exp(s - srt[-1])
+                o = (p[:, None] * vb[:nvis, hk]).sum(0) / p.sum()
+                sens = (p[:, None] * np.abs(vb[:nvis, hk] - o[None, :])).sum(0) / p.sum()
+                out[(b, i, h)] = (gap, e, rel.sum(), vb[:nvis, hk][rel].min(0),
+                                  vb[:nvis, hk][rel].max(0), sens)
+    return out
+
+
+def pin_conditioning(lib):
+    """The conditioning outputs: gap, bound and sensitivity to rounding, the
+    relevant-set size and V range exactly; a planted exact tie gives gap 0."""
+    cases = tiny_cases()[1:5]
+    tie = W.attn_case("tie", 41, B=1, next_n=1, Hq=2, Hkv=1, D=16, bs=4, lens=[9],
+                      kv_kind=W.KV_INT8, scale_mode=W.SCALE_PER_TENSOR)
+    tie.k_cache[tie.block_table[0, 1], 1] = tie.k_cache[tie.block_table[0, 0], 2]  # K_5 = K_2
+    tie.q[0, 0, 0] = 0
+    tie.q[0, 0, 0, 0] = np.float16(1.0)
+    tie.k_cache[:, :, :, 0] = 0
+    tie.k_cache[tie.block_table[0, 0], 2, 0, 0] = 100
+    tie.k_cache[tie.block_table[0, 1], 1, 0, 0] = 100  # tokens 2 and 5 tie at the top
+    for case in cases + [tie]:
+        _, cond, vr = oracle.paged_attn(case.q, case.k_cache, case.v_cache, case.kv_kind,
+                                        case.block_table, case.context_lens, lib=lib,
+                                        conditioning=True, **case.oracle_kwargs())
+        for (b, i, h), (gap, e, n, lo, hi, sens) in brute_conditioning(case).items():
+            c = cond[b, i, h]
+            if np.isinf(gap):
+                assert np.isinf(c[0])
+            else:
+                np.testing.assert_allclose(c[0], gap, rtol=1e-9, atol=1e-9 * (1 + abs(e)))
+            np.testing.assert_allclose(c[1], e, rtol=1e-9)
+            assert c[2] == n, (case.name, b, i, h)
+            assert np.array_equal(vr[b, i, h, 0], lo) and np.array_equal(vr[b, i, h, 1], hi)
+            np.testing.assert_allclose(vr[b, i, h, 2], sens, rtol=1e-9,
+                                       atol=1e-12 * (1 + np.abs(hi).max()))
+    _, cond, _ = oracle.paged_attn(tie.q, tie.k_cache, tie.v_cache, tie.kv_kind, tie.block_table,
+                                   tie.context_lens, lib=lib, conditioning=True,
+                                   **tie.oracle_kwargs())
+    assert cond[0, 0, 0, 0] == 0.0
+
+
 ALL_PINS = [pin_brute_force, pin_relocation_and_unpaged, pin_worked_case, pin_single_token,
-            pin_poison_insensitive]
+            pin_poison_insensitive, pin_bf16_q, pin_thread_count_invariant, pin_conditioning]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)

@@ -158,8 +158,45 @@ def pin_output_formats(lib):
     assert (bf16[0, int(case.context_lens[0]):case.max_context_len] == 0xFF80).all()  # -inf
 
 
+def epi_chain_numpy(S, w, epi):
+    """The reduced-precision head chain written with numpy and torch casts: the
+    weight and the dot rounded to the epilogue type (torch's round to nearest
+    even), an fp32 fused multiply-add (exact product and sum in float64, one
+    rounding to float32, which equals fmaf for float32 operands), then the
+    running value rounded to the epilogue type."""
+    import torch
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[epi]
+    rnd = lambda x: torch.from_numpy(np.asarray(x, np.float32)).to(dt).float().numpy()
+    acc = np.zeros(S.shape[0], np.float32)
+    ws, ss = rnd(w), rnd(S.astype(np.float32))
+    for h in range(S.shape[1]):
+        fma = (ws[h].astype(np.float64) * ss[:, h].astype(np.float64) +
+               acc.astype(np.float64)).astype(np.float32)
+        acc = rnd(fma)
+    return acc
+
+
+def pin_epilogue_types(lib):
+    """fp16 / bf16 epilogues (the reading stated at epi_step in oracle.c)
+    against the numpy/torch chain on the exact dots, bit for bit; and they are
+    not the fp32 result (the pin has teeth)."""
+    case = small_logits(seed=14)
+    S = brute.logits_exact(case)
+    f32 = run(case, lib)
+    for epi in ("f16", "bf16"):
+        got = run(case, lib, epi_format=epi)
+        for b in range(case.batch):
+            L = int(case.context_lens[b])
+            for i in range(case.next_n):
+                r = b * case.next_n + i
+                ref = epi_chain_numpy(S[b][i], case.weights[r], epi)
+                assert np.array_equal(got[r, :L].view(np.uint32), ref.view(np.uint32)), epi
+                assert np.all(got[r, L:case.max_context_len] == -np.inf)
+        assert not np.array_equal(got.view(np.uint32), f32.view(np.uint32))
+
+
 ALL_PINS = [pin_one_hot_weights_exact, pin_weighted_sum_bound, pin_tail_and_rows, pin_relocation,
-            pin_interleaved_sf_tail, pin_relu, pin_output_formats]
+            pin_interleaved_sf_tail, pin_relu, pin_output_formats, pin_epilogue_types]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)

@@ -43,7 +43,8 @@ PINS = ([pin_codec_e4m3, pin_codec_round] + test_oracle_attn.ALL_PINS +
         test_oracle_sparse.ALL_PINS)
 
 MUTATIONS = {
-    "gqa_head_map": ("int hk = h / group;", "int hk = h % Hkv;", 0),
+    "gqa_head_map": ("for (int h = hk * group; h < (hk + 1) * group; ++h) {\n        int64_t row",
+                     "for (int h = hk; h < Hq; h += Hkv) {\n        int64_t row", 0),
     "causal_off_by_one": ("if (causal && pos + 1 < nvis) nvis = pos + 1;",
                           "if (causal && pos < nvis) nvis = pos;"),
     "softmax_sign": ("s[t] = exp(s[t] - m);", "s[t] = exp(m - s[t]);", 0),
@@ -58,14 +59,19 @@ MUTATIONS = {
                      "- a);\n    if (d < bestd || (d == bestd)) {"),
     "int4_nibble_order": ("int nib = (d % 2 == 0) ? (byte & 15) : (byte >> 4);\n    return",
                           "int nib = (d % 2 == 0) ? (byte >> 4) : (byte & 15);\n    return"),
-    "v_slot_index": ("int slot = t % bs;\n          for (int d = 0; d < D; ++d) {\n"
-                     "            float vv",
-                     "int slot = (t + 1) % bs;\n          for (int d = 0; d < D; ++d) {\n"
-                     "            float vv"),
+    "v_slot_index": ("deq(v_cache, kind, v_scale, v_mode, blk, t % bs, hk,",
+                     "deq(v_cache, kind, v_scale, v_mode, blk, (t + 1) % bs, hk,"),
     "f16_exponent": ("v = ldexp(1024.0 + f, e - 25);", "v = ldexp(1024.0 + f, e - 24);"),
     "int_round_away": ("float r = nearbyintf(y);", "float r = roundf(y);"),
-    "logits_weight_row": ("acc = fmaf(weights[r * H + h], sh, acc);",
-                          "acc = fmaf(weights[h], sh, acc);"),
+    "logits_weight_row": ("acc = epi_step(weights[r * H + h], sh, acc, epi_format);",
+                          "acc = epi_step(weights[h], sh, acc, epi_format);"),
+    "logits_epi_unrounded_sum": ("return epi_round(fmaf(epi_round(w, epi_format), "
+                                 "epi_round(s, epi_format), acc), epi_format);",
+                                 "return fmaf(epi_round(w, epi_format), "
+                                 "epi_round(s, epi_format), acc);"),
+    "logits_epi_f16_as_bf16": ("if (epi_format == 1) return orc_f16_to_f32(orc_f64_to_f16(",
+                               "if (epi_format == 1) return orc_bf16_to_f32(orc_f32_to_bf16(("
+                               "float)"),
     "logits_sf_offset": ("const uint8_t* ksf = base + (int64_t)bs * (D / 2) +\n",
                          "const uint8_t* ksf = base +\n"),
     "logits_sf_interleave_swapped": ("if ((k % spi) * (bs / spi) + k / spi == t) return k;",
@@ -85,8 +91,15 @@ MUTATIONS = {
     "sparse_range_unchecked": ("if (sel_row[j] >= 0 && sel_row[j] < L) mark[sel_row[j]] = 1;",
                                "if (sel_row[j] >= 0 && sel_row[j] < L - 1) mark[sel_row[j]] = 1;"),
     "sparse_plan_mask_bit": ("rowmask[i] |= 1u << j;", "rowmask[i] |= 1u << (j ^ 1);"),
-    "sparse_score_scale": ("          s[t] = (double)softmax_scale * acc;\n          if (s[t] > m) m = s[t];\n          ++n;",
-                           "          s[t] = acc;\n          if (s[t] > m) m = s[t];\n          ++n;"),
+    "sparse_row_selection": ("mark + (size_t)i * n, L, D, softmax_scale,",
+                             "mark, L, D, softmax_scale,"),
+    "cond_gap_uses_first": ("if (s[t] > second) second = s[t];",
+                            "if (s[t] > second && second == -INFINITY) second = s[t];"),
+    "cond_eps_drops_length": ("(D + 8) * ldexp(1.0, -24) * aabs", "8 * ldexp(1.0, -24) * aabs"),
+    "cond_range_misses_ties": ("if (!vis[t] || s[t] < m - 8.0 * eps - 32.0) continue;",
+                               "if (!vis[t] || s[t] < m) continue;"),
+    "cond_sens_signed": ("vsens[d] += s[t] * fabs((double)vd[(int64_t)t * D + d] - orow[d]);",
+                         "vsens[d] += s[t] * ((double)vd[(int64_t)t * D + d] - orow[d]);"),
     "mx_sf_token_order": ("(int64_t)sf_slot_of_token(pos, bs, spi, sf_interleaved) * spi;",
                           "(int64_t)pos * spi;"),
 }
