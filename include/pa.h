@@ -147,6 +147,24 @@ pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace, size_t workspac
                          void* stream);
 
 /*
+ * paged_attn_fwd_noalloc -- paged_attn_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, kernels and result, with the
+ * workspace taken from a scratch array the library holds in device memory
+ * (paged_attn_noalloc_scratch_bytes() bytes per GPU, 32 MiB, kept until the
+ * process ends) instead of a caller's buffer. Nothing is allocated or freed
+ * by the call. Calls needing more workspace than the array holds (see
+ * paged_attn_workspace_size) return PA_ERR_WORKSPACE and enqueue nothing.
+ * The array is shared by every call on that GPU and keeps the last call's
+ * contents (the kernels write every byte they read, so nothing needs
+ * clearing); calls that overlap in time on one GPU -- on different streams
+ * or from different threads -- race on it. The first call on a device
+ * resolves the array's device address (hipGetSymbolAddress, no allocation).
+ */
+pa_status paged_attn_fwd_noalloc(const pa_attn_args* a, void* stream);
+size_t paged_attn_noalloc_scratch_bytes(void);
+
+/*
  * Test probe of the planner: writes the page-entry list the attention kernel
  * walks. Work units are (b, split); entries of unit (b, s) are
  * entries[((b * nsplit + s) * entries_per_unit + e) * 3 + {0,1,2}] =

@@ -11,7 +11,8 @@ import ctypes
 import os
 
 __all__ = [
-    "load", "paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_mqa_logits",
+    "load", "paged_attn_fwd", "paged_attn_workspace_size", "paged_attn_fwd_noalloc",
+    "pa_plan", "paged_mqa_logits",
     "paged_mqa_logits_workspace_size", "kv_insert", "pa_dequantize", "pa_set_profile_events",
     "prepare_paged_attn_fwd", "prepare_paged_mqa_logits", "Prepared", "PaError",
     "kv_insert_mxfp4", "prepare_kv_insert_mxfp4",
@@ -74,7 +75,8 @@ class PaError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "pa_plan", "paged_attn_sparse",
+EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "paged_attn_fwd_noalloc",
+           "paged_attn_noalloc_scratch_bytes", "pa_plan", "paged_attn_sparse",
            "paged_attn_sparse_workspace_size", "pa_sparse_plan", "paged_mqa_logits",
            "paged_mqa_logits_workspace_size", "kv_insert", "kv_insert_mxfp4", "pa_dequantize",
            "pa_last_error", "pa_set_profile_events"]
@@ -93,6 +95,10 @@ def load(path: str | None = None):
     lib.paged_attn_fwd.restype = _i32
     lib.paged_attn_workspace_size.argtypes = [ctypes.POINTER(AttnArgs)]
     lib.paged_attn_workspace_size.restype = ctypes.c_size_t
+    lib.paged_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+    lib.paged_attn_fwd_noalloc.restype = _i32
+    lib.paged_attn_noalloc_scratch_bytes.argtypes = []
+    lib.paged_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.pa_plan.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i64, _vp, _vp]
     lib.pa_plan.restype = _i32
     lib.paged_attn_sparse.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i32, _vp, ctypes.c_size_t,
@@ -247,6 +253,19 @@ def paged_attn_fwd(out, q, k_cache, v_cache, block_table, context_lens, max_cont
                            k_scale_mode=k_scale_mode, v_scale_mode=v_scale_mode,
                            softmax_scale=softmax_scale, causal=causal, workspace=workspace,
                            stream=stream)()
+    return out
+
+
+def paged_attn_fwd_noalloc(out, q, k_cache, v_cache, block_table, context_lens,
+                           max_context_len, *, kv_kind, k_scale=None, v_scale=None,
+                           k_scale_mode=None, v_scale_mode=None, softmax_scale=0.0, causal=True,
+                           stream=None):
+    """paged_attn_fwd without a workspace: the library's own scratch array in
+    device memory serves instead, and the call allocates nothing (see
+    paged_attn_fwd_noalloc in include/pa.h). Arguments as for paged_attn_fwd."""
+    a = _attn_args(out, q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                   kv_kind, k_scale, v_scale, k_scale_mode, v_scale_mode, softmax_scale, causal)
+    _check(load().paged_attn_fwd_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 
 

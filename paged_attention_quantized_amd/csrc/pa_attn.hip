@@ -588,6 +588,68 @@ extern "C" pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace,
   return launch_attn(a, sh, workspace, (hipStream_t)stream);
 }
 
+// ---------------------------------------------------------------------------
+// paged_attn_fwd_noalloc: the same kernels with their workspace in a
+// file-scope device array, for callers that cannot allocate
+// ---------------------------------------------------------------------------
+
+namespace pa {
+namespace {
+
+constexpr size_t kScratchBytes = 32u << 20;  // per GPU, held until the process ends
+
+// The workspace of paged_attn_fwd_noalloc. In host code this name is a host-side
+// stand-in, not the device address: only the address from hipGetSymbolAddress
+// (kept per device in g_scratch) is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device, resolved once per
+// device (hipGetSymbolAddress allocates nothing); NULL with an error message
+// if it cannot be resolved.
+void* scratch_ptr(pa_status* st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *st = fail(PA_ERR_HIP, "paged_attn_fwd_noalloc: no current HIP device");
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      *st = fail(PA_ERR_HIP, "paged_attn_fwd_noalloc: hipGetSymbolAddress: %s",
+                 hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *st = PA_OK;
+  return p;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" size_t paged_attn_noalloc_scratch_bytes(void) { return pa::kScratchBytes; }
+
+extern "C" pa_status paged_attn_fwd_noalloc(const pa_attn_args* a, void* stream) {
+  Shape sh;
+  pa_status st = check_args(a, &sh, true);
+  if (st != PA_OK) return st;
+  const size_t ws_need = sh.ml_bytes + sh.o_bytes + sh.seq_bytes;
+  if (ws_need > kScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "paged_attn_fwd_noalloc: this call needs %zu bytes of workspace, more than the "
+                "%zu bytes of the library's scratch array (use paged_attn_fwd)",
+                ws_need, kScratchBytes);
+  void* ws = scratch_ptr(&st);
+  if (st != PA_OK) return st;
+  if (a->batch == 0) return PA_OK;
+  return launch_attn(a, sh, ws, (hipStream_t)stream);
+}
+
 extern "C" pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t max_entries,
                              int32_t* info, void* stream) {
   Shape sh;
