@@ -15,10 +15,20 @@
  *    returns an error. pa_last_error() gives a message for the calling
  *    thread's last non-OK status.
  *  - Host-side checks (shapes, kinds, sizes) always run. Conditions that
- *    depend on device data (context lengths within max_context_len, block
- *    ids within num_blocks) are the caller's preconditions, as on the
+ *    depend on device data (context lengths within [0, max_context_len],
+ *    block ids of visible pages within [0, num_blocks) and, for attention,
+ *    not the null block 0) are the caller's preconditions, as on the
  *    fp4_paged_mqa_logits API page (block_table / max_context_len
- *    parameters): violating them is undefined behaviour.
+ *    parameters): violating them is undefined behaviour -- unless the
+ *    environment variable PA_VALIDATE is set (to anything but "" or "0"):
+ *    then paged_attn_fwd, paged_attn_fwd_noalloc, paged_attn_sparse and
+ *    paged_mqa_logits first run a device check that reads only
+ *    context_lens and the in-range table columns of visible pages, wait for
+ *    it on the stream, and return PA_ERR_PRECONDITION (nothing else
+ *    enqueued) naming the first violating sequence. The check is skipped
+ *    while the stream is being captured into a graph, as the API page's
+ *    validation is (max_context_len parameter). Its flags use 8 bytes of the
+ *    workspace.
  *
  * Sources (titles of the pages these operations come from):
  *  [NULLPAD] "Stop grouped-page4 null-block padding from leaking E4M3 NaN"
@@ -83,7 +93,11 @@ typedef enum {
  * position.
  *
  * Layouts (all row-major, device memory):
- *   q, out       [batch, next_n, num_q_heads, head_dim]  fp16 (q_dtype = PA_DT_F16)
+ *   q, out       [batch, next_n, num_q_heads, head_dim], both of q_dtype: fp16
+ *                (PA_DT_F16) or bf16 (PA_DT_BF16; q is widened to fp32 on load
+ *                and converted to fp16 for the matrix cores -- exact for bf16
+ *                values in fp16's normal range, |q| <= 65504 required -- and
+ *                out is rounded to bf16 to nearest even)
  *   k_cache,
  *   v_cache      [num_blocks, block_size, num_kv_heads, row_bytes], row_bytes =
  *                head_dim * 2 (F16/BF16), head_dim (E4M3/INT8), head_dim / 2 (INT4)
@@ -112,9 +126,11 @@ typedef enum {
  * next_n <= 4096 and next_n * num_q_heads / num_kv_heads <= 8192 query rows
  * per KV head (beyond 32 rows -- long verify, chunked prefill -- the rows are
  * processed in blocks of 32, each block walking only the tokens its last row
- * can see; the workspace grows with the number of blocks), q_dtype F16; KV
- * kinds F16, E4M3,
- * INT8, INT4. Workspace: paged_attn_workspace_size(a) bytes, 256-byte aligned.
+ * can see; the workspace grows with the number of blocks), q_dtype F16 or
+ * BF16; KV kinds F16, BF16, E4M3, INT8, INT4. A BF16 cache is read through
+ * fp16 for the matrix cores: exact for magnitudes in [2^-14, 65504], finite
+ * magnitudes above become 65504, smaller ones keep fp16's subnormal
+ * precision. Workspace: paged_attn_workspace_size(a) bytes, 256-byte aligned.
  */
 typedef struct pa_attn_args {
   void* out;
@@ -165,18 +181,27 @@ pa_status paged_attn_fwd_noalloc(const pa_attn_args* a, void* stream);
 size_t paged_attn_noalloc_scratch_bytes(void);
 
 /*
- * Test probe of the planner: writes the page-entry list the attention kernel
- * walks. Work units are (b, split); entries of unit (b, s) are
- * entries[((b * nsplit + s) * entries_per_unit + e) * 3 + {0,1,2}] =
- * {physical block, logical block, token mask}, in ascending logical order,
- * padded to a multiple of 8 with {0, logical block, 0} null entries
- * (mask 0 = never read). `info` is HOST memory (may be NULL when entries is
- * not) and receives {split_tokens, nsplit, entries_per_unit, 0}. Needs
- * max_entries >= batch * nsplit * entries_per_unit; call with entries = NULL
- * to get info only.
+ * Test probe of the plan [RELOC, Summary: reduce in logical order, split
+ * points that do not follow physical ids]: dumps what paged_attn_fwd's
+ * attention kernel walks for these arguments. The work is a list of items --
+ * (sequence, query row block, KV head group, block of `ts` logical tokens) in
+ * that order -- placed on a cost line and cut into one contiguous range per
+ * workgroup of the persistent grid; the probe runs the kernel's own range
+ * computation in every workgroup and writes, for every item at its global
+ * index g, items[g * 6 + {0..5}] = {workgroup, sequence, row block, head
+ * group, first logical token, physical block of the item's first page}. It
+ * also writes seq_first[b] (b < batch) = the first cost slot of sequence b
+ * and seq_first[batch] = the slot total (what the merge kernel reads), and
+ * *total = the number of items. Pages past a sequence's length are never
+ * items, so the null block 0 never appears for a valid table.
+ * `info` is HOST memory (int32[8], may be NULL when items is not) and
+ * receives {workgroups, item capacity needed, ts, KV heads per item, run-start
+ * cost in slots, row blocks, rows per block, head groups}; call with items =
+ * NULL to get info only. items, seq_first and total are DEVICE memory; items
+ * needs max_items >= the capacity, and entries past *total are not written.
  */
-pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t max_entries, int32_t* info,
-                  void* stream);
+pa_status pa_plan(const pa_attn_args* a, int32_t* items, int64_t max_items, int32_t* seq_first,
+                  int32_t* total, int32_t* info, void* stream);
 
 /*
  * paged_attn_sparse -- selection-driven sparse paged attention, the QSA route
@@ -195,7 +220,8 @@ pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t max_entries, 
  * physical relocation of pages. A row with an empty set outputs +0 and reads
  * no KV byte; KV bytes of unselected tokens are never part of a result (NaN
  * there cannot leak).
- * Supported: KV kinds F16 and E4M3 with per-tensor or no scales, next_n <= 4,
+ * Supported: every KV kind and scale mode of paged_attn_fwd (a PER_CHANNEL K
+ * scale is folded into q the same way), q_dtype F16 or BF16, next_n <= 4,
  * next_n * (num_q_heads / num_kv_heads) <= 32, max_blocks_per_seq <= 16384,
  * plus the shapes paged_attn_fwd supports.
  * Workspace: paged_attn_sparse_workspace_size(a, topk) bytes (0 when the
@@ -237,8 +263,13 @@ typedef enum { PA_LOGITS_F32 = 0, PA_LOGITS_F16 = 1, PA_LOGITS_BF16 = 2 } pa_log
  *   (E2M1 values, one UE8M0 scale per sf_vec_size elements), for
  *   t < context_lens[b]; -inf for context_lens[b] <= t < max_context_len.
  *   A is the identity, or with relu != 0 the rectifier max(., +0) (a variant
- *   the API page does not name). The fp32 value is stored as out_format:
- *   fp32, or fp16 / bf16 rounded to nearest even (-inf stays -inf).
+ *   the API page does not name). With epi_format fp16 / bf16 the head chain
+ *   runs in that type [FP4API, epi_dtype; the page leaves the arithmetic
+ *   open, the reading taken here]: the weight and A(S_h) are rounded to it
+ *   (nearest even), each step is the fp32 fma of those and the running value,
+ *   and the step's result is rounded to it again. The value is stored as
+ *   out_format: fp32, or fp16 / bf16 rounded to nearest even (-inf stays
+ *   -inf).
  * Rows >= batch*next_n and columns >= max_context_len are not written.
  *
  * Layouts:
@@ -254,11 +285,12 @@ typedef enum { PA_LOGITS_F32 = 0, PA_LOGITS_F16 = 1, PA_LOGITS_BF16 = 2 } pa_log
  *   weights   [batch*next_n, num_heads] fp32
  *   block_table [batch, max_blocks_per_seq] int32 with max_blocks_per_seq >=
  *             round_up(max_context_len, 128) / block_size (checked on the host)
- * Supported: head_dim 128, sf_vec_size 32, block_size 64, num_heads a multiple of 16
- * up to 64, next_n 1..4, epi_format PA_LOGITS_F32 (the page names fp16/bf16
- * epilogues without defining their arithmetic; they return PA_ERR_UNSUPPORTED).
- * There is no schedule argument: the grid follows max_context_len and each
- * workgroup reads context_lens itself. Workspace: none (pass NULL, 0).
+ * Supported: head_dim 128, sf_vec_size 32, block_size 64, num_heads 16, 32 or
+ * 64, next_n 1..4, epi_format fp32 / fp16 / bf16. There is no schedule
+ * argument: the grid follows max_context_len and each workgroup reads
+ * context_lens itself, so nothing can go stale [FP4API, schedule_meta].
+ * Workspace: paged_mqa_logits_workspace_size(a) bytes, used only for the
+ * PA_VALIDATE flags; without PA_VALIDATE NULL, 0 is accepted.
  */
 typedef struct pa_logits_args {
   void* out;
@@ -341,13 +373,15 @@ pa_status kv_insert_mxfp4(const pa_mxfp4_insert_args* a, void* stream);
  * and likewise for v. Rows without a slot (i >= num_slots, or slot < 0) are
  * skipped and their destination bytes are left untouched [INSERT, Design: the
  * KV-only mode skips DP-padding rows that have no slot].
+ * Rows whose slot lies at or past num_blocks * block_size are skipped too.
  * Q: E4M3 round-to-nearest-even saturating to +-448; INT8 / INT4 round to
- * nearest even clamped to +-127 / +-7; x / scale is an IEEE fp32 division.
- * F16 caches take fp16 input bits unchanged (scale mode NONE).
+ * nearest even clamped to +-127 / +-7; x / scale is an IEEE fp32 division of
+ * the input value (fp16, or bf16 widened exactly to fp32).
+ * F16 / BF16 caches take input of their own type, bits unchanged (scale mode
+ * NONE).
  *
- * Layouts: k, v [num_tokens, num_kv_heads, head_dim] fp16 (in_dtype PA_DT_F16);
+ * Layouts: k, v [num_tokens, num_kv_heads, head_dim] fp16 or bf16 (in_dtype);
  * slot_mapping [num_slots] int64; caches and scales as for paged_attn_fwd.
- * Precondition: every slot < num_blocks * block_size.
  */
 typedef struct pa_insert_args {
   void* k_cache;
@@ -378,7 +412,9 @@ pa_status kv_insert(const pa_insert_args* a, void* stream);
 /*
  * Test probe of the cache codecs used by paged_attn_fwd: out[i] =
  * fp32(code_i) * scale, scale = scale[0] (PER_TENSOR), scale[i % channels]
- * (PER_CHANNEL) or 1 (NONE). `n` counts elements (INT4: two per byte).
+ * (PER_CHANNEL) or 1 (NONE). `n` counts elements (INT4: two per byte). A BF16
+ * code's value is the fp16 the attention kernels read it as (see
+ * paged_attn_fwd).
  */
 pa_status pa_dequantize(pa_kv_kind kind, const void* codes, int64_t n, const float* scale,
                         pa_scale_mode mode, int64_t channels, float* out, void* stream);

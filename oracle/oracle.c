@@ -787,7 +787,9 @@ static void store_code(uint8_t* cache, int kind, int64_t blk, int off, int hk, i
  * Write rows k[i], v[i] ([T, Hkv, D]) of new tokens into the paged caches at
  * slot_mapping[i] (block = slot / bs, offset = slot % bs). Rows with
  * i >= num_slots or slot < 0 have no slot and are skipped, as the KV-only
- * insert skips padding rows that have no slot [P4, Design]. Codes: E4M3
+ * insert skips padding rows that have no slot [P4, Design]; so are rows whose
+ * slot lies past num_blocks * bs (reading: the pages say nothing of them, and
+ * a write there would leave the cache). Codes: E4M3
  * nearest-even saturating, INT8/INT4 nearest-even clamped to +-127 / +-7,
  * computed from x / scale in fp32. F16/BF16 caches store the input bits
  * unchanged and require the matching input dtype.
@@ -802,7 +804,7 @@ int orc_kv_insert(uint8_t* k_cache, uint8_t* v_cache, int kv_kind, const uint16_
     if (slot < 0) continue;
     int64_t blk = slot / bs;
     int off = (int)(slot % bs);
-    if (blk >= num_blocks) return -1;
+    if (blk >= num_blocks) continue; /* a slot past the cache is not written */
     for (int hk = 0; hk < Hkv; ++hk) {
       for (int d = 0; d < D; ++d) {
         int64_t idx = (i * Hkv + hk) * D + d;

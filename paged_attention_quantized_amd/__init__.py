@@ -99,7 +99,7 @@ def load(path: str | None = None):
     lib.paged_attn_fwd_noalloc.restype = _i32
     lib.paged_attn_noalloc_scratch_bytes.argtypes = []
     lib.paged_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
-    lib.pa_plan.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i64, _vp, _vp]
+    lib.pa_plan.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i64, _vp, _vp, _vp, _vp]
     lib.pa_plan.restype = _i32
     lib.paged_attn_sparse.argtypes = [ctypes.POINTER(AttnArgs), _vp, _i32, _vp, ctypes.c_size_t,
                                       _vp]
@@ -269,9 +269,15 @@ def paged_attn_fwd_noalloc(out, q, k_cache, v_cache, block_table, context_lens,
     return out
 
 
+PLAN_INFO = ("workgroups", "capacity", "tokens_per_item", "heads_per_item", "run_cost",
+             "row_blocks", "rows_per_block", "head_groups")
+
+
 def pa_plan(block_table, context_lens, max_context_len, *, q_shape, k_cache_shape, kv_kind,
-            k_scale_mode=SCALE_NONE, v_scale_mode=SCALE_NONE, stream=None):
-    """Planner probe: returns (entries int32 [B, nsplit, entries_per_unit, 3], info)."""
+            k_scale_mode=SCALE_NONE, v_scale_mode=SCALE_NONE, causal=True, stream=None):
+    """Plan probe (pa_plan in include/pa.h): returns (items int32 [total, 6] of
+    {workgroup, sequence, row block, head group, first logical token, physical
+    block}, seq_first int32 [B + 1], info dict)."""
     import torch
     B, next_n, Hq, D = q_shape
     nb, bs, Hkv, _ = k_cache_shape
@@ -280,15 +286,19 @@ def pa_plan(block_table, context_lens, max_context_len, *, q_shape, k_cache_shap
                  context_lens=_ptr(context_lens), max_context_len=int(max_context_len), batch=B,
                  next_n=next_n, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                  max_blocks_per_seq=block_table.shape[1], num_blocks=nb, softmax_scale=0.0,
-                 causal=1)
+                 causal=int(bool(causal)))
     lib = load()
-    info = (ctypes.c_int32 * 4)()
-    _check(lib.pa_plan(ctypes.byref(a), None, 0, ctypes.cast(info, _vp), None))
-    split, nsplit, epu = info[0], info[1], info[2]
-    entries = torch.empty((B, nsplit, epu, 3), dtype=torch.int32, device=block_table.device)
-    _check(lib.pa_plan(ctypes.byref(a), _ptr(entries), entries.numel() // 3,
-                       ctypes.cast(info, _vp), _stream(stream)))
-    return entries, {"split_tokens": split, "nsplit": nsplit, "entries_per_unit": epu}
+    raw = (ctypes.c_int32 * 8)()
+    _check(lib.pa_plan(ctypes.byref(a), None, 0, None, None, ctypes.cast(raw, _vp), None))
+    info = dict(zip(PLAN_INFO, list(raw)))
+    dev = block_table.device
+    items = torch.full((max(info["capacity"], 1), 6), -1, dtype=torch.int32, device=dev)
+    seq_first = torch.full((B + 1,), -1, dtype=torch.int32, device=dev)
+    total = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib.pa_plan(ctypes.byref(a), _ptr(items), items.shape[0], _ptr(seq_first),
+                       _ptr(total), ctypes.cast(raw, _vp), _stream(stream)))
+    n = int(total.item())
+    return items[:n], seq_first, info
 
 
 # ---------------------------------------------------------------------------

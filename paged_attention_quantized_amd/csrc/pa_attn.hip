@@ -159,22 +159,48 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
   }
 }
 
-// Planner probe: the page entries each sequence's tokens are read through, in
-// the logical order the kernel consumes them, padded to a multiple of 8 with
-// null entries {0, logical block, 0} that are never read [NULLPAD].
-__global__ void plan_dump_kernel(AttnParams p, int entries_per_seq, int pages_max,
-                                 int32_t* entries) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.B * entries_per_seq;
-  if (idx >= total) return;
-  const int e = idx % entries_per_seq;
-  const int b = idx / entries_per_seq;
-  const int L = p.context_lens[b];
-  const PlanEntry x =
-      plan_entry(p.block_table + (size_t)b * p.max_blocks, L, p.bs, 0, pages_max, e);
-  entries[idx * 3 + 0] = x.phys;
-  entries[idx * 3 + 1] = x.lblk;
-  entries[idx * 3 + 2] = (int32_t)x.mask;
+// Plan probe: what the attention kernels walk. Workgroup w of the persistent
+// grid runs the kernels' own range scan and writes each item of its range,
+// in walking order, at its global index: {w, sequence, row block, head group,
+// first logical token, physical block of the item's first page}. Workgroup 0
+// also leaves every sequence's first cost slot (the merge's arithmetic) in
+// p.ws_seq and the item total in *total.
+__global__ __launch_bounds__(64) void plan_probe_kernel(AttnParams p, int32_t* items,
+                                                        int64_t cap, int32_t* total) {
+  __shared__ int xi[8];
+  range_scan(p, p.context_lens, xi);
+  if (blockIdx.x == 0) {
+    // the item total, by the cost-line bookkeeping the kernels use
+    int n_all = 0;
+    for (int base = 0; base < p.B; base += 64) {
+      const int b = base + (int)threadIdx.x;
+      int cost, items;
+      seq_cost(p, b < p.B ? p.context_lens[b] : 0, cost, items);
+      n_all += lane_val(wave_incl_scan(items), 63);
+    }
+    if (threadIdx.x == 0) *total = n_all;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const int n = xi[0], ia = xi[6];
+  ItemPos it;
+  it.b = xi[1];
+  it.hg = xi[2];
+  it.k = xi[3];
+  it.L = xi[4];
+  it.rb = xi[5];
+  it.nst = run_stages(p, it.L, it.rb);
+  for (int j = 0; j < n && ia + j < cap; ++j) {
+    const int t0 = it.k << p.lts;
+    int32_t* e = items + (size_t)(ia + j) * 6;
+    e[0] = blockIdx.x;
+    e[1] = it.b;
+    e[2] = it.rb;
+    e[3] = it.hg;
+    e[4] = t0;
+    e[5] = p.block_table[(size_t)it.b * p.max_blocks + (t0 >> p.lbs)];
+    item_next(p, p.context_lens, it);
+  }
 }
 
 // Grouped union planner of a selection [RELOC, Summary: a physical-page union
@@ -302,7 +328,6 @@ struct Shape {
   int sparse, sp_cap;                    // selection-driven mode: plan entries per sequence
   int prefill;                           // the prefill layout (attn_prefill_kernel)
   size_t sp_entries_bytes, sp_masks_bytes, sp_vlen_bytes;
-  int pages_max, entries_per_seq;
   int wgmerge;
   int run_cost;                          // cost-line slots of a run start
   int64_t parts;
@@ -336,6 +361,7 @@ int device_cus() {
 PrefillFn pick_prefill_fn(int kind, int D, bool fold) {
   switch (kind) {
     case PA_KV_F16: return pick_prefill_f16(D, fold);
+    case PA_KV_BF16: return pick_prefill_bf16(D, fold);
     case PA_KV_E4M3: return pick_prefill_e4m3(D, fold);
     case PA_KV_INT8: return pick_prefill_int8(D, fold);
     case PA_KV_INT4: return pick_prefill_int4(D, fold);
@@ -354,16 +380,15 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
     return fail(PA_ERR_INVALID_ARG, "paged_attn: unknown kv_kind or scale mode");
   if (a->q_dtype != PA_DT_F16 && a->q_dtype != PA_DT_BF16)
     return fail(PA_ERR_UNSUPPORTED, "paged_attn: q_dtype must be F16 or BF16");
-  if (a->kv_kind == PA_KV_BF16) return fail(PA_ERR_UNSUPPORTED, "paged_attn: BF16 KV unsupported");
   if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
     return fail(PA_ERR_UNSUPPORTED, "paged_attn: head_dim must be 64, 128 or 256");
   if (a->block_size != 16 && a->block_size != 32)
     return fail(PA_ERR_UNSUPPORTED, "paged_attn: block_size must be 16 or 32");
   const int rb = a->head_dim * kv_bits(a->kv_kind) / 8;
   if (rb % 64) return fail(PA_ERR_UNSUPPORTED, "paged_attn: head_dim too small for this kv kind");
-  if (a->kv_kind == PA_KV_F16 &&
+  if ((a->kv_kind == PA_KV_F16 || a->kv_kind == PA_KV_BF16) &&
       (a->k_scale_mode != PA_SCALE_NONE || a->v_scale_mode != PA_SCALE_NONE))
-    return fail(PA_ERR_UNSUPPORTED, "paged_attn: F16 KV takes no scales");
+    return fail(PA_ERR_UNSUPPORTED, "paged_attn: F16 / BF16 KV takes no scales");
   if (a->softmax_scale < 0.f || !(a->softmax_scale == a->softmax_scale))
     return fail(PA_ERR_INVALID_ARG, "paged_attn: softmax_scale must be >= 0");
   const int G = a->num_q_heads / a->num_kv_heads;
@@ -435,8 +460,6 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   if (sh->nw == 1 && ts > 2 * a->block_size)
     return fail(PA_ERR_UNSUPPORTED, "paged_attn: item spans more than two pages");
   sh->nwg = device_cus();
-  sh->pages_max = (int)ceil_div(a->max_context_len > 0 ? a->max_context_len : 1, a->block_size);
-  sh->entries_per_seq = (int)round_up(sh->pages_max, 8);
   // Sub-tile states are merged inside the workgroup when one head's state (in
   // the MFMA layout: 16*RT rows x D fp32, plus m and l) fits the LDS exchange
   // buffer.
@@ -462,7 +485,8 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   sh->parts = slots * (sh->wgmerge ? sh->hpu : sh->nw);
   sh->ml_bytes = (size_t)round_up(sh->parts * sh->rpb * 16, 256);
   sh->o_bytes = (size_t)round_up(sh->parts * sh->rpb * a->head_dim * 4, 256);
-  sh->seq_bytes = (size_t)round_up(((int64_t)a->batch + 1) * 4, 256);
+  // sequence first slots, then the PA_VALIDATE flags
+  sh->seq_bytes = (size_t)round_up(((int64_t)a->batch + 1) * 4, 256) + kValidateBytes;
   sh->sparse = sparse_topk >= 0 ? 1 : 0;
   sh->sp_cap = 0;
   sh->sp_entries_bytes = sh->sp_masks_bytes = sh->sp_vlen_bytes = 0;
@@ -523,11 +547,21 @@ AttnParams make_params(const pa_attn_args* a, const Shape& sh, void* ws) {
 RingFn pick_ring(int kind, int D, int nw, int RT, int qf, int mode) {
   switch (kind) {
     case PA_KV_F16: return pick_ring_f16(D, nw, RT, qf, mode);
+    case PA_KV_BF16: return pick_ring_bf16(D, nw, RT, qf, mode);
     case PA_KV_E4M3: return pick_ring_e4m3(D, nw, RT, qf, mode);
     case PA_KV_INT8: return pick_ring_int8(D, nw, RT, qf, mode);
     case PA_KV_INT4: return pick_ring_int4(D, nw, RT, qf, mode);
   }
   return nullptr;
+}
+
+// PA_VALIDATE=1 check of the call's context lengths and visible block ids; the
+// flags live in the last kValidateBytes of the sequence-start region.
+pa_status validate_attn(const char* who, const pa_attn_args* a, const Shape& sh, void* ws,
+                        hipStream_t s) {
+  int* flags = (int*)((char*)ws + sh.ml_bytes + sh.o_bytes + sh.seq_bytes - kValidateBytes);
+  return validate_tables(who, a->block_table, a->context_lens, a->batch, a->max_blocks_per_seq,
+                         a->max_context_len, a->block_size, a->num_blocks, true, flags, s);
 }
 
 // Q' format of the ring kernel: with at most 8 query rows per KV head the rows
@@ -585,6 +619,8 @@ extern "C" pa_status paged_attn_fwd(const pa_attn_args* a, void* workspace,
     return fail(PA_ERR_WORKSPACE, "paged_attn: workspace needs %zu bytes, got %zu", ws_need,
                 workspace_bytes);
   if (a->batch == 0) return PA_OK;
+  st = validate_attn("paged_attn_fwd", a, sh, workspace, (hipStream_t)stream);
+  if (st != PA_OK) return st;
   return launch_attn(a, sh, workspace, (hipStream_t)stream);
 }
 
@@ -647,32 +683,41 @@ extern "C" pa_status paged_attn_fwd_noalloc(const pa_attn_args* a, void* stream)
   void* ws = scratch_ptr(&st);
   if (st != PA_OK) return st;
   if (a->batch == 0) return PA_OK;
+  st = validate_attn("paged_attn_fwd_noalloc", a, sh, ws, (hipStream_t)stream);
+  if (st != PA_OK) return st;
   return launch_attn(a, sh, ws, (hipStream_t)stream);
 }
 
-extern "C" pa_status pa_plan(const pa_attn_args* a, int32_t* entries, int64_t max_entries,
-                             int32_t* info, void* stream) {
+extern "C" pa_status pa_plan(const pa_attn_args* a, int32_t* items, int64_t max_items,
+                             int32_t* seq_first, int32_t* total, int32_t* info, void* stream) {
   Shape sh;
   pa_status st = check_args(a, &sh, false);
   if (st != PA_OK) return st;
-  const int64_t total = (int64_t)a->batch * sh.entries_per_seq;
+  // at most one item per (sequence, row block, head group, stage)
+  const int64_t cap = (int64_t)a->batch * sh.nrb * sh.hgroups *
+                      ceil_div(a->max_context_len > 0 ? a->max_context_len : 1, sh.ts);
   if (info) {
-    info[0] = sh.pages_max * a->block_size;
-    info[1] = 1;
-    info[2] = sh.entries_per_seq;
-    info[3] = sh.ts;
+    info[0] = sh.nwg;
+    info[1] = (int32_t)cap;
+    info[2] = sh.ts;
+    info[3] = sh.hpu;
+    info[4] = sh.run_cost;
+    info[5] = sh.nrb;
+    info[6] = sh.rpb;
+    info[7] = sh.hgroups;
   }
-  if (!entries) {
-    if (!info) return fail(PA_ERR_INVALID_ARG, "pa_plan: entries and info both NULL");
+  if (!items) {
+    if (!info) return fail(PA_ERR_INVALID_ARG, "pa_plan: items and info both NULL");
     return PA_OK;
   }
-  if (max_entries < total) return fail(PA_ERR_WORKSPACE, "pa_plan: needs %lld entries",
-                                       (long long)total);
-  if (!a->block_table || !a->context_lens) return fail(PA_ERR_INVALID_ARG, "pa_plan: null ptr");
+  if (max_items < cap) return fail(PA_ERR_WORKSPACE, "pa_plan: needs %lld items", (long long)cap);
+  if (!a->block_table || !a->context_lens || !seq_first || !total)
+    return fail(PA_ERR_INVALID_ARG, "pa_plan: null pointer");
+  if (a->batch == 0) return PA_OK;
   AttnParams p = make_params(a, sh, nullptr);
-  if (total > 0)
-    hipLaunchKernelGGL(plan_dump_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
-                       (hipStream_t)stream, p, sh.entries_per_seq, sh.pages_max, entries);
+  p.ws_seq = seq_first;
+  hipLaunchKernelGGL(plan_probe_kernel, dim3((unsigned)sh.nwg), dim3(64), 0, (hipStream_t)stream,
+                     p, items, cap, total);
   return launch_status("pa_plan kernel");
 }
 
@@ -707,6 +752,8 @@ extern "C" pa_status paged_attn_sparse(const pa_attn_args* a, const int32_t* sel
                 workspace_bytes);
   if (a->batch == 0) return PA_OK;
   if (topk > 0 && !sel) return fail(PA_ERR_INVALID_ARG, "paged_attn_sparse: sel is NULL");
+  st = validate_attn("paged_attn_sparse", a, sh, workspace, (hipStream_t)stream);
+  if (st != PA_OK) return st;
   RingFn fn = pick_ring(a->kv_kind, a->head_dim, sh.nw, sh.RT, q_format(a, sh), kModeSparse);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "paged_attn_sparse: no kernel for this kind/shape");
   char* base = (char*)workspace + sh.ml_bytes + sh.o_bytes + sh.seq_bytes;

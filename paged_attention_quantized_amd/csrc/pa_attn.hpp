@@ -895,7 +895,7 @@ __device__ __forceinline__ void load_row_masks(const AttnParams& p,
 
 // This workgroup's item range, computed by one wave (see the cost line in
 // the kernel below); lane 0 leaves {count, b, hg, k, L, rb} of the first item
-// in xi[0..5]. Workgroup 0 also publishes every sequence's first slot and the
+// in xi[0..5] and the range's first global item index in xi[6]. Workgroup 0 also publishes every sequence's first slot and the
 // slot total for the merge kernel.
 __device__ __forceinline__ void range_scan(const AttnParams& p, const int32_t* __restrict__ lens,
                                            int* xi) {
@@ -952,6 +952,7 @@ __device__ __forceinline__ void range_scan(const AttnParams& p, const int32_t* _
     xi[3] = fk;
     xi[4] = fL;
     xi[5] = frb;
+    xi[6] = ia;  // global index of the range's first item
   }
 }
 
@@ -1607,10 +1608,12 @@ RingFn pick_d(int D, int nw, int RT, int qf, int mode) {
 
 // Ring kernel of one KV kind (each defined in its own translation unit).
 RingFn pick_ring_f16(int D, int nw, int RT, int qf, int mode);
+RingFn pick_ring_bf16(int D, int nw, int RT, int qf, int mode);
 RingFn pick_ring_e4m3(int D, int nw, int RT, int qf, int mode);
 RingFn pick_ring_int8(int D, int nw, int RT, int qf, int mode);
 RingFn pick_ring_int4(int D, int nw, int RT, int qf, int mode);
 PrefillFn pick_prefill_f16(int D, bool fold);
+PrefillFn pick_prefill_bf16(int D, bool fold);
 PrefillFn pick_prefill_e4m3(int D, bool fold);
 PrefillFn pick_prefill_int8(int D, bool fold);
 PrefillFn pick_prefill_int4(int D, bool fold);

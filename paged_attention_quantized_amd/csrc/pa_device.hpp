@@ -1,6 +1,5 @@
 // pa_device.hpp -- device helpers shared by the gfx950 kernels of libpa:
-// vector types, KV-cache codecs (code -> fp16, exact for every kind), the
-// planner's page-entry function and small wavefront utilities.
+// vector types, KV-cache codecs (code -> fp16) and small wavefront utilities.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,6 +36,22 @@ struct Kv<PA_KV_F16> {
   static constexpr int kPairsPerDword = 1;
   __device__ static void decode(uint32_t w, h2* out) { out[0] = as_h2(w); }
   // element order of the pairs produced from one dword (see decode)
+  __device__ static constexpr int order(int e) { return e; }
+};
+
+// bf16 cache: 2 bytes per element; each value is widened to fp32 (its upper
+// half) and converted to fp16 toward zero. bf16's 8-bit significand fits
+// fp16's 11 bits, so the conversion is exact for magnitudes in fp16's normal
+// range [2^-14, 65504]; smaller ones keep fp16's subnormal precision, larger
+// finite ones become +-65504, and infinities and NaN stay what they are.
+template <>
+struct Kv<PA_KV_BF16> {
+  static constexpr int kBits = 16;
+  static constexpr int kPairsPerDword = 1;
+  __device__ static void decode(uint32_t w, h2* out) {
+    out[0] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                                __uint_as_float(w & 0xFFFF0000u)));
+  }
   __device__ static constexpr int order(int e) { return e; }
 };
 
@@ -115,36 +130,6 @@ template <int KIND>
 __device__ __forceinline__ constexpr int run_elem(int s) {
   constexpr int E = 2 * Kv<KIND>::kPairsPerDword;
   return (s / E) * E + Kv<KIND>::order(s % E);
-}
-
-// ---------------------------------------------------------------------------
-// Planner ([RELOC] logical order; [NULLPAD] padding entries are null block 0
-// with mask 0 and are never dereferenced). The unit (b, split) walks logical
-// blocks split * pages_per_split + e in ascending e. Entries past the sequence
-// or past the split are padding.
-// ---------------------------------------------------------------------------
-
-struct PlanEntry {
-  int32_t phys;
-  int32_t lblk;
-  uint32_t mask;  // bit j: token slot j is a real, in-range token
-};
-
-__device__ __forceinline__ PlanEntry plan_entry(const int32_t* __restrict__ table_row, int L,
-                                                int bs, int first_lblk, int pages_per_split,
-                                                int e) {
-  PlanEntry x;
-  x.lblk = first_lblk + e;
-  int start = x.lblk * bs;
-  if (e < pages_per_split && start < L) {
-    x.phys = table_row[x.lblk];
-    int valid = L - start < bs ? L - start : bs;
-    x.mask = valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u);
-  } else {
-    x.phys = 0;
-    x.mask = 0u;
-  }
-  return x;
 }
 
 // ---------------------------------------------------------------------------

@@ -29,6 +29,17 @@ void launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) 
     hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
+// PA_VALIDATE=1: device check of context_lens against max_context_len and of
+// the block ids of visible pages (range, and the null block 0 when it is
+// reserved), then a sync; PA_ERR_PRECONDITION names the first violating
+// sequence. Skipped (PA_OK) when validation is off or the stream is
+// capturing. `flags` is 8 bytes of device scratch.
+bool validation_requested();
+pa_status validate_tables(const char* who, const int32_t* table, const int32_t* lens, int B,
+                          int max_blocks, int max_ctx, int bs, int64_t num_blocks,
+                          bool null_reserved, int* flags, hipStream_t s);
+constexpr size_t kValidateBytes = 256;  // workspace bytes reserved for the flags
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 

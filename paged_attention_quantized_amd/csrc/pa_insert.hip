@@ -31,14 +31,19 @@ __device__ __forceinline__ int enc_int(float y, float lim) {
 struct InsertParams {
   uint8_t* k_cache;
   uint8_t* v_cache;
-  const _Float16* k;
-  const _Float16* v;
+  const uint16_t* k;  // fp16 or bf16 bits (in_bf16)
+  const uint16_t* v;
   const int64_t* slot_mapping;
   const float* k_scale;
   const float* v_scale;
-  int64_t num_tokens, num_slots;
-  int Hkv, D, bs, k_mode, v_mode;
+  int64_t num_tokens, num_slots, num_blocks;
+  int Hkv, D, bs, k_mode, v_mode, in_bf16;
 };
+
+// Input value: fp16 bits, or bf16 bits (the upper half of an fp32).
+__device__ __forceinline__ float in_val(const uint16_t* x, int d, bool bf16) {
+  return bf16 ? __uint_as_float((uint32_t)x[d] << 16) : (float)__builtin_bit_cast(_Float16, x[d]);
+}
 
 __device__ __forceinline__ float scale_at(const float* s, int mode, int hk, int d, int D) {
   return mode == PA_SCALE_PER_TENSOR ? s[0] : (mode == PA_SCALE_PER_CHANNEL ? s[hk * D + d] : 1.f);
@@ -54,6 +59,7 @@ __global__ __launch_bounds__(64) void insert_kernel(InsertParams p) {
   const int64_t slot = p.slot_mapping[i];
   if (slot < 0) return;          // padding rows carry slot -1
   const int64_t blk = slot / p.bs;
+  if (blk >= p.num_blocks) return;  // a slot past the cache is not written
   const int off = (int)(slot % p.bs);
   constexpr int BITS = Kv<KIND>::kBits;
   const int rb = p.D * BITS / 8;
@@ -61,23 +67,24 @@ __global__ __launch_bounds__(64) void insert_kernel(InsertParams p) {
   const size_t src = ((size_t)i * p.Hkv + hk) * p.D;
   for (int plane = 0; plane < 2; ++plane) {
     uint8_t* dst = (plane ? p.v_cache : p.k_cache) + row * rb;
-    const _Float16* x = (plane ? p.v : p.k) + src;
+    const uint16_t* x = (plane ? p.v : p.k) + src;
     const float* sc = plane ? p.v_scale : p.k_scale;
     const int mode = plane ? p.v_mode : p.k_mode;
-    if constexpr (KIND == PA_KV_F16) {
-      const uint16_t* xs = reinterpret_cast<const uint16_t*>(x);
+    const bool bf = p.in_bf16;
+    if constexpr (KIND == PA_KV_F16 || KIND == PA_KV_BF16) {
+      // the input bits unchanged (the input type matches the cache's)
       uint16_t* ds = reinterpret_cast<uint16_t*>(dst);
-      for (int d = threadIdx.x; d < p.D; d += 64) ds[d] = xs[d];
+      for (int d = threadIdx.x; d < p.D; d += 64) ds[d] = x[d];
     } else if constexpr (KIND == PA_KV_INT4) {
       for (int j = threadIdx.x; j < rb; j += 64) {
         const int d = 2 * j;
-        const int lo = enc_int((float)x[d] / scale_at(sc, mode, hk, d, p.D), 7.f);
-        const int hi = enc_int((float)x[d + 1] / scale_at(sc, mode, hk, d + 1, p.D), 7.f);
+        const int lo = enc_int(in_val(x, d, bf) / scale_at(sc, mode, hk, d, p.D), 7.f);
+        const int hi = enc_int(in_val(x, d + 1, bf) / scale_at(sc, mode, hk, d + 1, p.D), 7.f);
         dst[j] = (uint8_t)((lo & 15) | ((hi & 15) << 4));
       }
     } else {
       for (int d = threadIdx.x; d < p.D; d += 64) {
-        const float y = (float)x[d] / scale_at(sc, mode, hk, d, p.D);
+        const float y = in_val(x, d, bf) / scale_at(sc, mode, hk, d, p.D);
         dst[d] = KIND == PA_KV_E4M3 ? (uint8_t)enc_e4m3(y) : (uint8_t)(int8_t)enc_int(y, 127.f);
       }
     }
@@ -116,11 +123,14 @@ extern "C" pa_status kv_insert(const pa_insert_args* a, void* stream) {
   if (a->num_tokens < 0 || a->num_slots < 0 || a->num_kv_heads < 1 || a->head_dim < 2 ||
       a->block_size < 1 || a->num_blocks < 1 || (a->head_dim & 1))
     return fail(PA_ERR_INVALID_ARG, "kv_insert: bad sizes");
-  if (a->in_dtype != PA_DT_F16) return fail(PA_ERR_UNSUPPORTED, "kv_insert: in_dtype must be F16");
-  if (a->kv_kind == PA_KV_BF16) return fail(PA_ERR_UNSUPPORTED, "kv_insert: BF16 KV unsupported");
-  if (a->kv_kind == PA_KV_F16 &&
+  if (a->in_dtype != PA_DT_F16 && a->in_dtype != PA_DT_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "kv_insert: in_dtype must be F16 or BF16");
+  if ((a->kv_kind == PA_KV_F16 && a->in_dtype != PA_DT_F16) ||
+      (a->kv_kind == PA_KV_BF16 && a->in_dtype != PA_DT_BF16))
+    return fail(PA_ERR_UNSUPPORTED, "kv_insert: an F16 / BF16 cache takes input of its own type");
+  if ((a->kv_kind == PA_KV_F16 || a->kv_kind == PA_KV_BF16) &&
       (a->k_scale_mode != PA_SCALE_NONE || a->v_scale_mode != PA_SCALE_NONE))
-    return fail(PA_ERR_UNSUPPORTED, "kv_insert: F16 KV takes no scales");
+    return fail(PA_ERR_UNSUPPORTED, "kv_insert: F16 / BF16 KV takes no scales");
   const int64_t rows = a->num_tokens < a->num_slots ? a->num_tokens : a->num_slots;
   if (rows == 0) return PA_OK;
   if (!a->k_cache || !a->v_cache || !a->k || !a->v || !a->slot_mapping)
@@ -131,8 +141,10 @@ extern "C" pa_status kv_insert(const pa_insert_args* a, void* stream) {
   InsertParams p;
   p.k_cache = (uint8_t*)a->k_cache;
   p.v_cache = (uint8_t*)a->v_cache;
-  p.k = (const _Float16*)a->k;
-  p.v = (const _Float16*)a->v;
+  p.k = (const uint16_t*)a->k;
+  p.v = (const uint16_t*)a->v;
+  p.in_bf16 = a->in_dtype == PA_DT_BF16;
+  p.num_blocks = a->num_blocks;
   p.slot_mapping = a->slot_mapping;
   p.k_scale = a->k_scale;
   p.v_scale = a->v_scale;
@@ -147,6 +159,7 @@ extern "C" pa_status kv_insert(const pa_insert_args* a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   switch (a->kv_kind) {
     case PA_KV_F16: hipLaunchKernelGGL(insert_kernel<PA_KV_F16>, grid, dim3(64), 0, s, p); break;
+    case PA_KV_BF16: hipLaunchKernelGGL(insert_kernel<PA_KV_BF16>, grid, dim3(64), 0, s, p); break;
     case PA_KV_E4M3: hipLaunchKernelGGL(insert_kernel<PA_KV_E4M3>, grid, dim3(64), 0, s, p); break;
     case PA_KV_INT8: hipLaunchKernelGGL(insert_kernel<PA_KV_INT8>, grid, dim3(64), 0, s, p); break;
     case PA_KV_INT4: hipLaunchKernelGGL(insert_kernel<PA_KV_INT4>, grid, dim3(64), 0, s, p); break;
@@ -159,7 +172,6 @@ extern "C" pa_status pa_dequantize(pa_kv_kind kind, const void* codes, int64_t n
                                    const float* scale, pa_scale_mode mode, int64_t channels,
                                    float* out, void* stream) {
   if (!valid_kind(kind) || !valid_mode(mode)) return fail(PA_ERR_INVALID_ARG, "pa_dequantize: kind");
-  if (kind == PA_KV_BF16) return fail(PA_ERR_UNSUPPORTED, "pa_dequantize: BF16 unsupported");
   if (n < 0 || (mode == PA_SCALE_PER_CHANNEL && channels < 1))
     return fail(PA_ERR_INVALID_ARG, "pa_dequantize: bad sizes");
   const int64_t bits = kv_bits(kind);
@@ -173,6 +185,7 @@ extern "C" pa_status pa_dequantize(pa_kv_kind kind, const void* codes, int64_t n
   const uint32_t* c = (const uint32_t*)codes;
   switch (kind) {
     case PA_KV_F16: hipLaunchKernelGGL(dequant_kernel<PA_KV_F16>, grid, dim3(256), 0, s, c, ndw, scale, (int)mode, channels, out); break;
+    case PA_KV_BF16: hipLaunchKernelGGL(dequant_kernel<PA_KV_BF16>, grid, dim3(256), 0, s, c, ndw, scale, (int)mode, channels, out); break;
     case PA_KV_E4M3: hipLaunchKernelGGL(dequant_kernel<PA_KV_E4M3>, grid, dim3(256), 0, s, c, ndw, scale, (int)mode, channels, out); break;
     case PA_KV_INT8: hipLaunchKernelGGL(dequant_kernel<PA_KV_INT8>, grid, dim3(256), 0, s, c, ndw, scale, (int)mode, channels, out); break;
     case PA_KV_INT4: hipLaunchKernelGGL(dequant_kernel<PA_KV_INT4>, grid, dim3(256), 0, s, c, ndw, scale, (int)mode, channels, out); break;

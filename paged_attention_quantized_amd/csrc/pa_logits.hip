@@ -46,7 +46,49 @@ struct LogitsParams {
   int B, max_blocks, max_ctx, ngroups;
   int sfi;   // scale tail in the interleaved slot order
   int relu;  // rectifier between each head's dot and its weight
+  int epi;   // epilogue type of the head chain: PA_LOGITS_F32 / F16 / BF16
 };
+
+// fp32 value rounded to bf16 (nearest even), as an fp32
+__device__ __forceinline__ float round_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return x != x ? x : __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
+}
+
+// fp32 value rounded to the epilogue type (nearest even), as an fp32
+template <int EPI>
+__device__ __forceinline__ float epi_round(float x) {
+  if constexpr (EPI == PA_LOGITS_F16) return (float)(_Float16)x;
+  else if constexpr (EPI == PA_LOGITS_BF16) return round_bf16(x);
+  else return x;
+}
+
+// The weighted head chain of one token, heads in ascending order: acc =
+// fma(w_h, A(S_h), acc) in fp32, or with a reduced-precision epilogue the
+// weight and A(S_h) rounded to that type and every step's result rounded to
+// it too [FP4API, epi_dtype; the page does not define the arithmetic: the
+// reading taken is rounding at those three points]. A is the identity or the
+// rectifier.
+template <int EPI, int NTI, int HG>
+__device__ __forceinline__ float head_chain(const float (&s)[NTI][4][4], const float* wrow,
+                                            bool relu) {
+  float acc = 0.f;
+#pragma unroll
+  for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+    for (int rt = 0; rt < NTI; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = s[rt][tau][e];
+        if (relu) x = x > 0.f ? x : 0.f;
+        float f = fmaf(wrow[HG * tau + 4 * rt + e], epi_round<EPI>(x), acc);
+        // the fp32 result is a value of its own: the compiler would otherwise
+        // fuse the fma and the fp16 conversion into one rounding (v_fma_mix)
+        if constexpr (EPI != PA_LOGITS_F32) asm volatile("" : "+v"(f));
+        acc = epi_round<EPI>(f);
+      }
+  return acc;
+}
 
 // 4x4 transpose of (lane group, register): after it, register t of lane group
 // g holds what register g of lane group t held.
@@ -163,7 +205,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
       if (tid + 256 * k < QN) reinterpret_cast<u4*>(qlds)[tid + 256 * k] = qv[k];
     if (tid < NN * H) {
       sflds[tid] = sfv;
-      wlds[tid] = wv;
+      wlds[tid] = p.epi == PA_LOGITS_F16    ? epi_round<PA_LOGITS_F16>(wv)
+                  : p.epi == PA_LOGITS_BF16 ? epi_round<PA_LOGITS_BF16>(wv)
+                                            : wv;
     }
   }
   __syncthreads();
@@ -208,27 +252,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
       for (int rt = 0; rt < NTI; ++rt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) transpose4(s[rt][0][e], s[rt][1][e], s[rt][2][e], s[rt][3][e]);
+      // the weights are staged in LDS already rounded to the epilogue type
       const float* wrow = wlds + i * H;
-      float acc = 0.f;
-      if (p.relu) {
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-          for (int rt = 0; rt < NTI; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = s[rt][tau][e];
-              acc = fmaf(wrow[HG * tau + 4 * rt + e], x > 0.f ? x : 0.f, acc);
-            }
-      } else {
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-          for (int rt = 0; rt < NTI; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc = fmaf(wrow[HG * tau + 4 * rt + e], s[rt][tau][e], acc);
-      }
+      float acc;
+      if (p.epi == PA_LOGITS_F16)
+        acc = head_chain<PA_LOGITS_F16, NTI, HG>(s, wrow, p.relu);
+      else if (p.epi == PA_LOGITS_BF16)
+        acc = head_chain<PA_LOGITS_BF16, NTI, HG>(s, wrow, p.relu);
+      else if (p.relu)
+        acc = head_chain<PA_LOGITS_F32, NTI, HG>(s, wrow, true);
+      else
+        acc = head_chain<PA_LOGITS_F32, NTI, HG>(s, wrow, false);
       if (t < p.max_ctx) orow[(size_t)i * p.out_stride + t] = (OT)(t < L ? acc : -INFINITY);
     }
   }
@@ -269,15 +303,15 @@ LogitsFn pick_out(int format, int NN, int H) {
 
 using namespace pa;
 
+// The workspace only holds the PA_VALIDATE flags (unused otherwise: without
+// validation NULL, 0 is accepted).
 extern "C" size_t paged_mqa_logits_workspace_size(const pa_logits_args* a) {
   (void)a;
-  return 0;
+  return kValidateBytes;
 }
 
 extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!a) return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: args is NULL");
   if (a->batch < 0 || a->next_n < 1 || a->num_heads < 1 || a->head_dim < 1 ||
       a->block_size < 1 || a->max_blocks_per_seq < 1 || a->num_blocks < 1 ||
@@ -290,8 +324,9 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
   if (a->out_format != PA_LOGITS_F32 && a->out_format != PA_LOGITS_F16 &&
       a->out_format != PA_LOGITS_BF16)
     return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: unknown out_format");
-  if (a->epi_format != PA_LOGITS_F32)
-    return fail(PA_ERR_UNSUPPORTED, "paged_mqa_logits: only an fp32 epilogue is supported");
+  if (a->epi_format != PA_LOGITS_F32 && a->epi_format != PA_LOGITS_F16 &&
+      a->epi_format != PA_LOGITS_BF16)
+    return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: unknown epi_format");
   if (a->sf_interleaved != 0 && a->sf_interleaved != 1)
     return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: sf_interleaved must be 0 or 1");
   if (a->relu != 0 && a->relu != 1)
@@ -309,6 +344,17 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
   if (!a->out || !a->q || !a->sf_q || !a->kv_fused || !a->weights || !a->context_lens ||
       !a->block_table)
     return fail(PA_ERR_INVALID_ARG, "paged_mqa_logits: null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  if (validation_requested()) {
+    if (!workspace || workspace_bytes < kValidateBytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "paged_mqa_logits: PA_VALIDATE needs paged_mqa_logits_workspace_size() bytes "
+                  "of workspace");
+    pa_status st = validate_tables("paged_mqa_logits", a->block_table, a->context_lens, a->batch,
+                                   a->max_blocks_per_seq, a->max_context_len, a->block_size,
+                                   a->num_blocks, false, (int*)workspace, s);
+    if (st != PA_OK) return st;
+  }
   LogitsParams p;
   p.out = a->out;
   p.out_stride = a->out_row_stride;
@@ -320,11 +366,11 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
   p.block_table = a->block_table;
   p.sfi = a->sf_interleaved;
   p.relu = a->relu;
+  p.epi = a->epi_format;
   p.B = a->batch;
   p.max_blocks = a->max_blocks_per_seq;
   p.max_ctx = a->max_context_len;
   p.ngroups = (int)ceil_div(a->max_context_len, 4 * 64 * kLogitsBlocks);
-  hipStream_t s = (hipStream_t)stream;
   launch_timed(fn, dim3((unsigned)((int64_t)a->batch * p.ngroups)), dim3(256), s, p);
   return launch_status("paged_mqa_logits kernel");
 }

@@ -71,6 +71,21 @@ def test_host_validation(field, value, status):
     assert pa.load().pa_last_error().decode() != ""
 
 
+def test_bf16_kinds_accepted_on_host():
+    lib = pa.load()
+    for kw in (dict(q_dtype=1), dict(kv_kind=pa.KV_BF16, k_scale_mode=0, v_scale_mode=0)):
+        a = valid_args(**kw)
+        assert lib.paged_attn_workspace_size(ctypes.byref(a)) > 0
+    # a BF16 cache takes no scales
+    assert status_of(valid_args(kv_kind=pa.KV_BF16)) == 2
+
+
+def test_logits_workspace_holds_validation_flags():
+    lib = pa.load()
+    a = pa.LogitsArgs()
+    assert lib.paged_mqa_logits_workspace_size(ctypes.byref(a)) == 256
+
+
 def test_int4_small_head_dim_unsupported():
     a = valid_args(kv_kind=pa.KV_INT4, head_dim=64)
     assert status_of(a) == 2
@@ -89,17 +104,19 @@ def test_null_args():
 
 def test_plan_info_on_host():
     lib = pa.load()
-    info = (ctypes.c_int32 * 4)()
-    assert lib.pa_plan(ctypes.byref(valid_args()), None, 0, ctypes.cast(info, ctypes.c_void_p),
-                       None) == 0
-    split, nsplit, epu = info[0], info[1], info[2]
-    assert split % 16 == 0 and nsplit * split >= 4096 and epu % 8 == 0
-    assert epu >= split // 16
+    info = (ctypes.c_int32 * 8)()
+    assert lib.pa_plan(ctypes.byref(valid_args()), None, 0, None, None,
+                       ctypes.cast(info, ctypes.c_void_p), None) == 0
+    nwg, cap, ts, hpu, run_cost, nrb, rpb, hgroups = list(info)
+    # the decode shape: one row block of 4 rows, 8 KV heads per item, 16-token items
+    assert nwg >= 1 and (nrb, rpb) == (1, 4) and hpu * hgroups == 8 and ts % 16 == 0
+    assert cap == 64 * nrb * hgroups * -(-4096 // ts)
 
 
 def test_dequantize_validation():
     lib = pa.load()
     assert lib.pa_dequantize(9, None, 4, None, 0, 1, None, None) == 1
+    assert lib.pa_dequantize(pa.KV_BF16, None, 0, None, 0, 1, None, None) == 0
     assert lib.pa_dequantize(pa.KV_E4M3, None, 3, None, 0, 1, None, None) == 1  # partial dword
     assert lib.pa_dequantize(pa.KV_E4M3, None, 0, None, 0, 1, None, None) == 0  # empty: no work
 
@@ -115,6 +132,14 @@ def test_insert_validation():
     a.num_slots = 0
     a.k_scale = 0x1000
     assert lib.kv_insert(ctypes.byref(a), None) == 0  # nothing to insert: no launch
+    a.in_dtype = 1  # bf16 input into an E4M3 cache
+    assert lib.kv_insert(ctypes.byref(a), None) == 0
+    a.kv_kind, a.k_scale_mode, a.v_scale_mode = pa.KV_F16, 0, 0
+    assert lib.kv_insert(ctypes.byref(a), None) == 2  # F16 cache needs fp16 input
+    a.kv_kind = pa.KV_BF16
+    assert lib.kv_insert(ctypes.byref(a), None) == 0
+    a.in_dtype = 2
+    assert lib.kv_insert(ctypes.byref(a), None) == 2
 
 
 def test_struct_layouts_match_header(tmp_path):

@@ -73,6 +73,38 @@ def test_bf16_query_and_output(pa, idx):
     say(f"{case.name} bf16: {st}")
 
 
+def bf16_kv_cases():
+    return [
+        W.attn_case("bf16kv_decode", 1901, B=4, next_n=1, Hq=16, Hkv=4, D=128, bs=16,
+                    lens=[700, 33, 1, 250], kv_kind=W.KV_BF16, scale_mode=W.SCALE_NONE),
+        W.attn_case("bf16kv_verify", 1902, B=2, next_n=4, Hq=32, Hkv=4, D=64, bs=32,
+                    lens=[400, 9], kv_kind=W.KV_BF16, scale_mode=W.SCALE_NONE),
+        W.attn_case("bf16kv_prefill", 1903, B=2, next_n=40, Hq=16, Hkv=2, D=128, bs=32,
+                    lens=[300, 41], kv_kind=W.KV_BF16, scale_mode=W.SCALE_NONE),
+        W.attn_case("bf16kv_d256", 1904, B=2, next_n=2, Hq=4, Hkv=2, D=256, bs=16,
+                    lens=[129, 64], kv_kind=W.KV_BF16, scale_mode=W.SCALE_NONE),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(4))
+def test_bf16_kv_parity(pa, idx):
+    """BF16 caches (decode, verify, prefill layout, head_dim 256), with fp16 and
+    with bf16 queries, against the oracle's exact bf16 values; relocation
+    bit-identical."""
+    case = bf16_kv_cases()[idx]
+    for bf in (False, True):
+        say(f"bf16 kv {case.name} bf16 q={bf}")
+        d = DevAttn(case, bf16=bf)
+        out = d.run(pa)
+        ref, cond, vr = oracle_attn(case, conditioning=True, q=d.q.cpu() if bf else None)
+        st = compare_attn_conditioned(to_f64(out), ref, cond, vr, case.name,
+                                      "bf16" if bf else "f16")
+        say(f"{case.name}: {st}")
+    base = run_attn(pa, case)
+    got = run_attn(pa, W.relocate(case, 3))
+    assert np.array_equal(got.view(np.uint16), base.view(np.uint16))
+
+
 @pytest.mark.parametrize("idx", [0, 1, 3, 4])
 def test_relocation_and_unpaged_bit_identical(pa, idx):
     case = small_cases()[idx]
@@ -139,34 +171,76 @@ def test_worked_case_inf_times_zero(pa):
             compare_attn(got, oracle_attn(case), f"worked kind={kind} ks={ks}")
 
 
-def test_plan_probe(pa):
-    """The planner walks logical blocks in ascending order, covers [0, L)
-    exactly once per sequence, pads every unit to a multiple of 8 entries with
-    null (block 0, mask 0) entries, and never points a live entry at block 0."""
-    case = small_cases()[1]
+def plan_cases():
+    return [small_cases()[1], small_cases()[4], split_cases()[4], split_cases()[0],
+            W.attn_case("plan_prefill", 1801, B=2, next_n=40, Hq=16, Hkv=2, D=128, bs=32,
+                        lens=[500, 45], kv_kind=W.KV_E4M3, scale_mode=W.SCALE_PER_TENSOR)]
+
+
+def run_len_host(L, next_n, G, R, nrb, rpb, rb, causal):
+    """Tokens row block rb walks (its last row's causal limit), written out
+    from the causal rule: row r is query step r // G at position L - next_n + r // G."""
+    if not causal or nrb == 1:
+        return L
+    last = (min((rb + 1) * rpb, R) - 1) // G
+    return max(0, min(L, L - next_n + last + 1))
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_plan_probe(pa, idx):
+    """What the attention kernel walks (pa_plan runs its own range scan in
+    every workgroup): each (sequence, row block, head group) run's items cover
+    its visible tokens once, in ascending logical order; workgroup ranges are
+    contiguous in the global (sequence, row block, head group, position) order;
+    every item sits in its workgroup's slice of the cost line
+    [w * Q, (w + 1) * Q), Q = ceil(slots / workgroups), with run_cost slots
+    before each run; live items never read the null block; and the walk does
+    not depend on physical block ids (relocation changes only the block
+    column)."""
+    case = plan_cases()[idx]
     d = DevAttn(case)
-    say("plan probe")
-    entries, info = pa.pa_plan(d.bt, d.cl, case.max_context_len, q_shape=case.q.shape,
-                               k_cache_shape=case.k_cache.shape, kv_kind=case.kv_kind,
-                               k_scale_mode=case.k_scale_mode)
-    e = entries.cpu().numpy()
-    bs = case.block_size
-    assert info["entries_per_unit"] % 8 == 0
-    assert info["split_tokens"] % bs == 0
+    say(f"plan probe {case.name}")
+    items, seq_first, info = pa.pa_plan(d.bt, d.cl, case.max_context_len, q_shape=case.q.shape,
+                                        k_cache_shape=case.k_cache.shape, kv_kind=case.kv_kind,
+                                        k_scale_mode=case.k_scale_mode, causal=case.causal)
+    it = items.cpu().numpy()
+    sf = seq_first.cpu().numpy()
+    ts, nrb, rpb, hg_n, rc = (info["tokens_per_item"], info["row_blocks"],
+                              info["rows_per_block"], info["head_groups"], info["run_cost"])
+    G = case.num_q_heads // case.num_kv_heads
+    R = case.next_n * G
+    # expected items and cost-line slots, from the lengths alone
+    want, slots, cursor = [], [], 0
     for b in range(case.batch):
         L = int(case.context_lens[b])
-        seen = []
-        for s in range(info["nsplit"]):
-            for phys, lblk, mask in e[b, s]:
-                mask = int(np.uint32(mask))
-                if mask == 0:
-                    assert phys == 0
-                    continue
-                assert phys == case.block_table[b, lblk] and phys != 0
-                for j in range(bs):
-                    if mask >> j & 1:
-                        seen.append(lblk * bs + j)
-        assert seen == list(range(L))
+        assert sf[b] == cursor
+        for rb in range(nrb):
+            n = -(-run_len_host(L, case.next_n, G, R, nrb, rpb, rb, case.causal) // ts)
+            if n == 0:
+                continue
+            for hg in range(hg_n):
+                cursor += rc
+                for k in range(n):
+                    want.append((b, rb, hg, k * ts))
+                    slots.append(cursor)
+                    cursor += 1
+    assert sf[case.batch] == cursor
+    assert [tuple(x) for x in it[:, 1:5]] == want
+    q = max(1, -(-cursor // info["workgroups"]))
+    for (w, *_), slot in zip(it, slots):
+        assert w * q <= slot < (w + 1) * q
+    assert np.all(np.diff(it[:, 0]) >= 0)
+    bt = case.block_table
+    assert np.array_equal(it[:, 5], bt[it[:, 1], it[:, 4] // case.block_size])
+    assert np.all(it[:, 5] != 0)
+    other = W.relocate(case, 13)
+    d2 = DevAttn(other)
+    it2, sf2, _ = pa.pa_plan(d2.bt, d2.cl, case.max_context_len, q_shape=case.q.shape,
+                             k_cache_shape=case.k_cache.shape, kv_kind=case.kv_kind,
+                             k_scale_mode=case.k_scale_mode, causal=case.causal)
+    it2 = it2.cpu().numpy()
+    assert np.array_equal(it2[:, :5], it[:, :5]) and np.array_equal(sf2.cpu().numpy(), sf)
+    assert np.array_equal(it2[:, 5], other.block_table[it[:, 1], it[:, 4] // case.block_size])
 
 
 def test_workspace_and_args_errors(pa):

@@ -37,9 +37,55 @@ def test_dequantize_all_codes_bit_exact(pa, kind, mode):
         assert nan.sum() == 2 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
 
 
+def rtz_f16_of_bf16_bits(bits):
+    """fp16 value of bf16 bits converted toward zero (numpy/torch arithmetic):
+    the decode paged_attn_fwd applies to a BF16 cache."""
+    x = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out = np.array(x)
+    fin = np.isfinite(x)
+    a = np.abs(x[fin])
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -24)))
+    q = np.exp2(np.maximum(e, -14) - 10)  # fp16 spacing (subnormal below 2^-14)
+    r = np.trunc(a / q) * q
+    r = np.minimum(r, 65504.0)
+    out[fin] = np.copysign(r, x[fin])
+    return out
+
+
+@pytest.mark.parametrize("mode", [W.SCALE_NONE, W.SCALE_PER_TENSOR, W.SCALE_PER_CHANNEL])
+def test_dequantize_bf16_all_codes(pa, mode):
+    """Every bf16 bit pattern: equal to the oracle's exact value wherever fp16
+    holds it (magnitudes in [2^-14, 65504], zeros, infinities, NaN), and to the
+    toward-zero fp16 value elsewhere."""
+    rng = np.random.default_rng(4)
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    n = 65536
+    ch = 64
+    scale = np.exp(rng.uniform(-4, 4, ch)).astype(np.float32)
+    say(f"dequantize bf16 mode={mode}")
+    got = pa.pa_dequantize(W.KV_BF16, dev(codes.view(np.uint8)), n,
+                           dev(scale) if mode else None, mode=mode, channels=ch).cpu().numpy()
+    ref = oracle.dequantize(W.KV_BF16, codes.view(np.uint8), n, scale, mode, ch)
+    val = (codes.astype(np.uint32) << 16).view(np.float32)
+    a = np.abs(val)
+    exact = (a == 0) | ((a >= 2.0 ** -14) & (a <= 65504)) | np.isinf(val)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    m = exact & ~nan
+    assert np.array_equal(got[m].view(np.uint32), ref[m].view(np.uint32))
+    sc = np.ones(n, np.float32) if mode == 0 else (
+        np.full(n, scale[0], np.float32) if mode == 1 else scale[np.arange(n) % ch])
+    want = (rtz_f16_of_bf16_bits(codes).astype(np.float32) * sc)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
 def _insert_gpu(pa, case):
     kc, vc = dev(case.k_cache), dev(case.v_cache)
-    k, v = dev(case.k), dev(case.v)
+    if case.in_bf16:
+        k = dev(case.k.view(np.int16)).view(torch.bfloat16)
+        v = dev(case.v.view(np.int16)).view(torch.bfloat16)
+    else:
+        k, v = dev(case.k), dev(case.v)
     pa.kv_insert(kc, vc, k, v, dev(case.slot_mapping), kv_kind=case.kv_kind,
                  k_scale=None if case.k_scale is None else dev(case.k_scale),
                  v_scale=None if case.v_scale is None else dev(case.v_scale),
@@ -52,8 +98,37 @@ def _insert_oracle(case):
     kc, vc = case.k_cache.copy(), case.v_cache.copy()
     oracle.kv_insert(kc, vc, case.kv_kind, case.k, case.v, case.slot_mapping,
                      k_scale=case.k_scale, k_scale_mode=case.scale_mode, v_scale=case.v_scale,
-                     v_scale_mode=case.scale_mode, block_size=case.block_size)
+                     v_scale_mode=case.scale_mode, block_size=case.block_size,
+                     in_is_bf16=case.in_bf16)
     return kc, vc
+
+
+@pytest.mark.parametrize("kind,mode", [(W.KV_E4M3, W.SCALE_PER_TENSOR),
+                                       (W.KV_INT8, W.SCALE_PER_CHANNEL),
+                                       (W.KV_INT4, W.SCALE_PER_TENSOR),
+                                       (W.KV_BF16, W.SCALE_NONE)])
+def test_insert_bf16_input_bit_exact(pa, kind, mode):
+    """bf16 input rows (and a BF16 cache), with slotless rows, slot -1 rows and
+    rows whose slot lies past the cache: cache bytes equal the oracle's."""
+    case = W.insert_case(31 + kind, T=600, Hkv=2, D=128, bs=16, kv_kind=kind, scale_mode=mode,
+                         slotless_tail=5, neg_slots=3, value_scale=2.0, in_dtype="bf16",
+                         oob_slots=4)
+    say(f"insert bf16 kind={kind} mode={mode}")
+    gk, gv = _insert_gpu(pa, case)
+    ok, ov = _insert_oracle(case)
+    assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
+
+
+def test_insert_slot_past_cache_skipped(pa):
+    """A slot at or past num_blocks * block_size is not written (it would lie
+    outside the cache); the other rows land exactly as the oracle's."""
+    case = W.insert_case(77, T=300, Hkv=2, D=128, bs=16, kv_kind=W.KV_E4M3,
+                         scale_mode=W.SCALE_PER_TENSOR, oob_slots=7)
+    assert (case.slot_mapping >= case.num_blocks * case.block_size).sum() == 7
+    say("insert slots past the cache")
+    gk, gv = _insert_gpu(pa, case)
+    ok, ov = _insert_oracle(case)
+    assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
 
 
 @pytest.mark.parametrize("kind,mode", [(W.KV_E4M3, W.SCALE_PER_TENSOR),

@@ -171,10 +171,31 @@ def test_logits_relu(pa, idx):
     assert not np.array_equal(np.nan_to_num(got), np.nan_to_num(plain))
 
 
+@pytest.mark.parametrize("epi", ["f16", "bf16"])
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_logits_epilogue_types(pa, epi, fmt):
+    """fp16 / bf16 epilogues (epi_dtype): the head chain in that type, bit for
+    bit against the oracle's reading of it, for every output type."""
+    case = small_cases()[0]
+    say(f"logits epilogue {epi} out {fmt}")
+    got = run_gpu(pa, case, out_format=fmt, epi_dtype=TORCH_DT[epi])
+    ref = run_oracle(case, out_format=fmt, epi_format=epi)
+    if fmt == "f32":
+        assert_same(got, ref, f"epi {epi}")
+    else:
+        assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), (epi, fmt)
+
+
+def test_logits_epilogue_full_workload(pa):
+    """The full workload with an fp16 epilogue, every row bit-exact."""
+    case = W.mxfp4_logits()
+    say("full mxfp4 logits, fp16 epilogue")
+    got = run_gpu(pa, case, epi_dtype=torch.float16)
+    assert_same(got, run_oracle(case, epi_format="f16"), "full epi f16")
+
+
 def test_logits_format_errors(pa):
     case = small_cases()[0]
-    with pytest.raises(pa.PaError, match="UNSUPPORTED"):
-        run_gpu(pa, case, epi_dtype=torch.float16)
     out = torch.empty((case.batch * case.next_n, case.max_context_len), dtype=torch.float16,
                       device="cuda")
     with pytest.raises(pa.PaError, match="INVALID_ARG"):

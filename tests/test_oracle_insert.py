@@ -19,7 +19,8 @@ def run(case, lib):
     kc, vc = case.k_cache.copy(), case.v_cache.copy()
     oracle.kv_insert(kc, vc, case.kv_kind, case.k, case.v, case.slot_mapping,
                      k_scale=case.k_scale, k_scale_mode=case.scale_mode, v_scale=case.v_scale,
-                     v_scale_mode=case.scale_mode, block_size=case.block_size, lib=lib)
+                     v_scale_mode=case.scale_mode, block_size=case.block_size,
+                     in_is_bf16=case.in_bf16, lib=lib)
     return kc, vc
 
 
@@ -45,16 +46,18 @@ def check_case(case, lib):
     bs = case.block_size
     written = np.zeros(kc.shape[:2], bool)
     for cache, x, scale in ((kc, case.k, case.k_scale), (vc, case.v, case.v_scale)):
-        codes = None if case.kv_kind == W.KV_F16 else expected_codes(x, scale, case.kv_kind,
-                                                                     case.scale_mode)
+        codes = None if case.kv_kind in (W.KV_F16, W.KV_BF16) else expected_codes(
+            case.values(x), scale, case.kv_kind, case.scale_mode)
         for i in range(T):
             if i >= case.slot_mapping.shape[0] or case.slot_mapping[i] < 0:
                 continue
             s = int(case.slot_mapping[i])
             blk, off = s // bs, s % bs
+            if blk >= kc.shape[0]:
+                continue  # past the cache: skipped
             written[blk, off] = True
             row = cache[blk, off]
-            if case.kv_kind == W.KV_F16:
+            if case.kv_kind in (W.KV_F16, W.KV_BF16):
                 assert np.array_equal(row.view(np.uint16), x[i].view(np.uint16))
             elif case.kv_kind == W.KV_INT4:
                 dec = brute.decode_cache(row[None, None], W.KV_INT4, x.shape[-1])[0, 0]
@@ -109,7 +112,33 @@ def pin_round_trip_every_code(lib):
             assert np.array_equal(got.astype(np.int64), np.array(codes))
 
 
-ALL_PINS = [pin_insert_vs_library, pin_round_trip_every_code]
+def pin_bf16_input_and_cache(lib):
+    """bf16 input rows: quantized from their bf16 values (torch's own bf16),
+    or copied bit for bit into a BF16 cache."""
+    for kind, mode in ((W.KV_E4M3, W.SCALE_PER_TENSOR), (W.KV_INT8, W.SCALE_PER_CHANNEL),
+                       (W.KV_INT4, W.SCALE_PER_TENSOR), (W.KV_BF16, W.SCALE_NONE)):
+        case = W.insert_case(19, T=29, Hkv=2, D=32, bs=8, kv_kind=kind, scale_mode=mode,
+                             slotless_tail=3, neg_slots=2, value_scale=2.0, in_dtype="bf16")
+        check_case(case, lib)
+
+
+def pin_slot_past_cache_skipped(lib):
+    """A slot at or past num_blocks * block_size is skipped: the cache equals
+    the insert of the other rows alone."""
+    case = W.insert_case(23, T=40, Hkv=1, D=32, bs=8, kv_kind=W.KV_INT8,
+                         scale_mode=W.SCALE_PER_TENSOR, oob_slots=3)
+    bad = case.slot_mapping >= case.num_blocks * case.block_size
+    assert bad.sum() == 3
+    kc, vc = run(case, lib)
+    import dataclasses
+    clean = dataclasses.replace(case, slot_mapping=np.where(bad, -1, case.slot_mapping))
+    kc2, vc2 = run(clean, lib)
+    assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2)
+    check_case(case, lib)
+
+
+ALL_PINS = [pin_insert_vs_library, pin_round_trip_every_code, pin_bf16_input_and_cache,
+            pin_slot_past_cache_skipped]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)

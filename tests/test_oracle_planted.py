@@ -81,6 +81,8 @@ MUTATIONS = {
     "logits_tail_zero": ("orow[t] = -INFINITY;", "orow[t] = 0.0f;"),
     "logits_q_scale_byte": ("((qsf >> (8 * g)) & 0xFF)", "((qsf >> (8 * (3 - g))) & 0xFF)"),
     "insert_offset": ("int off = (int)(slot % bs);", "int off = (int)(slot % bs) ^ 1;"),
+    "insert_bf16_input_as_f16": ("return in_is_bf16 ? orc_bf16_to_f32(x[idx]) : orc_f16_to_f32(x[idx]);",
+                                 "return orc_f16_to_f32(x[idx]);"),
     "mx_scale_offset": ("int b = (e - 1) - 2 + 127;", "int b = (e - 1) - 1 + 127;"),
     "e2m1_ties_odd": ("float d = fabsf(a - orc_e2m1_to_f32((uint8_t)c));\n"
                       "    if (d < bestd || (d == bestd && (c & 1) == 0)) {",

@@ -458,7 +458,7 @@ def mxfp4_logits(seed=SEED_BASE + 4, B=32, max_len=32768) -> LogitsCase:
 
 @dataclasses.dataclass
 class InsertCase:
-    k: np.ndarray  # float16 [T, Hkv, D]
+    k: np.ndarray  # float16 [T, Hkv, D], or uint16 bf16 bits when in_bf16
     v: np.ndarray
     slot_mapping: np.ndarray  # int64 [num_slots]
     num_blocks: int
@@ -469,27 +469,46 @@ class InsertCase:
     scale_mode: int
     k_cache: np.ndarray  # prefilled destination, uint8 [num_blocks, bs, Hkv, row_bytes]
     v_cache: np.ndarray
+    in_bf16: bool = False
+
+    def values(self, x):
+        """float32 values of k or v."""
+        if self.in_bf16:
+            return (x.astype(np.uint32) << 16).view(np.float32)
+        return x.astype(np.float32)
 
 
 def insert_case(seed, *, T, Hkv, D, bs, kv_kind, scale_mode, slotless_tail=0, neg_slots=0,
-                value_scale=1.0) -> InsertCase:
-    """New tokens k, v [T, Hkv, D] ~ N(0, value_scale^2) as fp16, distinct
-    random slots in blocks 1.., the last `slotless_tail` rows without a slot
-    (num_slots = T - slotless_tail) and `neg_slots` rows with slot -1. The
-    destination caches are prefilled with NaN bytes (0xFF)."""
+                value_scale=1.0, in_dtype="f16", oob_slots=0) -> InsertCase:
+    """New tokens k, v [T, Hkv, D] ~ N(0, value_scale^2) as fp16 (or bf16
+    bits with in_dtype="bf16"), distinct random slots in blocks 1.., the last
+    `slotless_tail` rows without a slot (num_slots = T - slotless_tail),
+    `neg_slots` rows with slot -1 and `oob_slots` rows whose slot lies past the
+    cache. The destination caches are prefilled with NaN bytes (0xFF)."""
     rng = np.random.default_rng(seed)
     num_slots = T - slotless_tail
     nb = (T + bs - 1) // bs + 3
     slots = rng.choice(np.arange(bs, nb * bs), num_slots, replace=False).astype(np.int64)
     if neg_slots:
         slots[rng.choice(num_slots, neg_slots, replace=False)] = -1
-    k = (rng.standard_normal((T, Hkv, D), dtype=np.float32) * value_scale).astype(np.float16)
-    v = (rng.standard_normal((T, Hkv, D), dtype=np.float32) * value_scale).astype(np.float16)
+    if oob_slots:
+        pick = rng.choice(np.flatnonzero(slots >= 0), oob_slots, replace=False)
+        slots[pick] = nb * bs + rng.integers(0, 5 * bs, oob_slots)
+    kx = rng.standard_normal((T, Hkv, D), dtype=np.float32) * value_scale
+    vx = rng.standard_normal((T, Hkv, D), dtype=np.float32) * value_scale
+    if in_dtype == "bf16":
+        import torch
+        k = torch.from_numpy(kx).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        v = torch.from_numpy(vx).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    else:
+        k, v = kx.astype(np.float16), vx.astype(np.float16)
     k_scale = v_scale = None
+    kf = (k.astype(np.uint32) << 16).view(np.float32) if in_dtype == "bf16" else k.astype(np.float32)
+    vf = (v.astype(np.uint32) << 16).view(np.float32) if in_dtype == "bf16" else v.astype(np.float32)
     if scale_mode == SCALE_PER_TENSOR:
         lim = {KV_E4M3: 448.0, KV_INT8: 127.0, KV_INT4: 7.0}[kv_kind]
-        k_scale = np.array([np.abs(k.astype(np.float32)).max() / lim], np.float32)
-        v_scale = np.array([np.abs(v.astype(np.float32)).max() / lim], np.float32)
+        k_scale = np.array([np.abs(kf).max() / lim], np.float32)
+        v_scale = np.array([np.abs(vf).max() / lim], np.float32)
     elif scale_mode == SCALE_PER_CHANNEL:
         k_scale = np.exp(rng.uniform(-3, 1, (Hkv, D))).astype(np.float32)
         v_scale = np.exp(rng.uniform(-3, 1, (Hkv, D))).astype(np.float32)
@@ -498,7 +517,7 @@ def insert_case(seed, *, T, Hkv, D, bs, kv_kind, scale_mode, slotless_tail=0, ne
     vc = np.full((nb, bs, Hkv, rb), 0xFF, np.uint8)
     return InsertCase(k=k, v=v, slot_mapping=slots, num_blocks=nb, block_size=bs,
                       kv_kind=kv_kind, k_scale=k_scale, v_scale=v_scale, scale_mode=scale_mode,
-                      k_cache=kc, v_cache=vc)
+                      k_cache=kc, v_cache=vc, in_bf16=in_dtype == "bf16")
 
 
 @dataclasses.dataclass
