@@ -321,6 +321,41 @@ pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace, size_t work
                            void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* pa_topk_select [RELOC] [FP4API]                                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The top-k over indexer logits that gives each query row its token set
+ * [RELOC, Investigation: the selected token ids of a query row; Upstream
+ * check: top-k], joining paged_mqa_logits to paged_attn_sparse: for row
+ * r = b * next_n + i, sel[r, :] holds the ids of the k largest logits[r, t]
+ * over t < context_lens[b], in ascending id order, followed by -1 for the
+ * positions left when context_lens[b] < k. Equal logits (+0 and -0 alike) go
+ * to the lower token id, and NaN ranks below every number (the pages give no
+ * tie rule; this is the reading taken). The result is exact: index work,
+ * bit-identical to the oracle.
+ *
+ * Layouts: logits [>= batch * next_n, logits_row_stride] of logits_format
+ *          (fp32 / fp16 / bf16: the output formats of paged_mqa_logits);
+ *          context_lens [batch] int32, each in [0, logits_row_stride];
+ *          sel [batch * next_n, k] int32 (= [batch, next_n, k], the sel
+ *          argument of paged_attn_sparse with topk = k).
+ * One workgroup per row; no workspace.
+ */
+typedef struct pa_topk_args {
+  int32_t* sel;
+  const void* logits;
+  pa_logits_format logits_format;
+  int64_t logits_row_stride;
+  const int32_t* context_lens;
+  int32_t batch;
+  int32_t next_n;
+  int32_t k;
+} pa_topk_args;
+
+pa_status pa_topk_select(const pa_topk_args* a, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* kv_insert_mxfp4 [FP4API] [INSERT]                                         */
 /* ------------------------------------------------------------------------ */
 

@@ -93,6 +93,8 @@ def _bind(lib):
     lib.orc_sparse_plan.restype = i32
     lib.orc_mqa_logits.argtypes = [P, i64, P, P, P, P, P, P,
                                    i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.orc_topk_select.argtypes = [P, P, i32, i64, P, i32, i32, i32]
+    lib.orc_topk_select.restype = i32
     lib.orc_f32_to_bf16_array.argtypes = [P, P, i64]
     lib.orc_f32_to_bf16_array.restype = None
     lib.orc_f32_to_e2m1.argtypes = [f32]
@@ -327,6 +329,24 @@ def mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_contex
         lib.orc_f32_to_bf16_array(_ptr(out), _ptr(bits), out.size)
         return bits
     raise ValueError(f"unknown out_format {out_format!r}")
+
+
+def topk_select(logits, context_lens, next_n, k, *, fmt="f32", lib=None):
+    """Reference top-k selection (see orc_topk_select in oracle.c): logits
+    [B*next_n, stride] (float32, or uint16 bits of fp16 / bf16 with fmt "f16"
+    / "bf16"); returns int32 [B*next_n, k] token ids in ascending order, -1
+    padded."""
+    lib = lib or load()
+    lg = np.ascontiguousarray(logits)
+    cl = _c(context_lens, np.int32)
+    rows = cl.shape[0] * next_n
+    assert lg.shape[0] >= rows
+    sel = np.empty((rows, k), np.int32)
+    rc = lib.orc_topk_select(_ptr(sel), _ptr(lg), {"f32": 0, "f16": 1, "bf16": 2}[fmt],
+                             lg.shape[1], _ptr(cl), cl.shape[0], next_n, k)
+    if rc != 0:
+        raise ValueError(f"orc_topk_select failed with code {rc}")
+    return sel
 
 
 def kv_insert(k_cache, v_cache, kv_kind, k, v, slot_mapping, *, k_scale=None,

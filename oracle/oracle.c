@@ -747,6 +747,77 @@ int orc_mqa_logits(float* out, int64_t out_row_stride, const uint8_t* q, const i
   return 0;
 }
 
+/* ------------------------------------------------------------------ */
+/* Top-k token selection over logits [P3] [P5]                          */
+/* ------------------------------------------------------------------ */
+
+/* One logit of a row: fp32, fp16 (1) or bf16 (2) bits. */
+static float logit_value(const void* logits, int fmt, int64_t idx) {
+  if (fmt == 1) return orc_f16_to_f32(((const uint16_t*)logits)[idx]);
+  if (fmt == 2) return orc_bf16_to_f32(((const uint16_t*)logits)[idx]);
+  return ((const float*)logits)[idx];
+}
+
+typedef struct {
+  float v;
+  int32_t t;
+} orc_scored;
+
+/* Rank order of the selection: larger value first (equal values, -0 and +0
+ * included, tie), NaN after every number, then the lower token id. */
+static int rank_cmp(const void* pa, const void* pb) {
+  const orc_scored* a = (const orc_scored*)pa;
+  const orc_scored* b = (const orc_scored*)pb;
+  int an = isnan(a->v), bn = isnan(b->v);
+  if (an != bn) return an ? 1 : -1;
+  if (!an && a->v != b->v) return a->v > b->v ? -1 : 1;
+  return (a->t > b->t) - (a->t < b->t);
+}
+
+static int int_cmp(const void* pa, const void* pb) {
+  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  return (a > b) - (a < b);
+}
+
+/*
+ * sel[r, :] for row r = b * next_n + i: the ids of the k highest logits of
+ * row r among tokens t < context_lens[b] (the tokens the logits cover; the
+ * -inf tail past the length is not a candidate), in ascending id order, then
+ * -1 for the positions left when fewer than k tokens exist. This is the
+ * top-k over the indexer logits that gives each query row its token set
+ * [P3, Investigation: the selected token ids; Upstream check: top-k]. The
+ * pages give no tie rule; the reading taken: equal logits go to the lower
+ * token id, and NaN ranks below every number. Sorting is a library step
+ * (qsort) under that total order.
+ */
+int orc_topk_select(int32_t* sel, const void* logits, int fmt, int64_t row_stride,
+                    const int32_t* context_lens, int B, int next_n, int k) {
+  int rc = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int r = 0; r < B * next_n; ++r) {
+    int L = context_lens[r / next_n];
+    if (L < 0 || (int64_t)L > row_stride) {
+#pragma omp atomic write
+      rc = -2;
+      continue;
+    }
+    orc_scored* c = (orc_scored*)malloc(sizeof(orc_scored) * (size_t)(L > 0 ? L : 1));
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+    for (int t = 0; t < L; ++t) {
+      c[t].v = logit_value(logits, fmt, (int64_t)r * row_stride + t);
+      c[t].t = t;
+    }
+    qsort(c, (size_t)L, sizeof(orc_scored), rank_cmp);
+    int n = L < k ? L : k;
+    for (int j = 0; j < n; ++j) ids[j] = c[j].t;
+    qsort(ids, (size_t)n, sizeof(int32_t), int_cmp);
+    for (int j = 0; j < k; ++j) sel[(int64_t)r * k + j] = j < n ? ids[j] : -1;
+    free(c);
+    free(ids);
+  }
+  return rc;
+}
+
 /* fp32 -> bf16 bits of n values, round to nearest even (orc_f32_to_bf16). */
 void orc_f32_to_bf16_array(const float* x, uint16_t* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(x[i]);

@@ -60,6 +60,12 @@ class InsertArgs(ctypes.Structure):
                 ("k_scale_mode", _i32), ("v_scale", _vp), ("v_scale_mode", _i32)]
 
 
+class TopkArgs(ctypes.Structure):
+    _fields_ = [("sel", _vp), ("logits", _vp), ("logits_format", _i32),
+                ("logits_row_stride", _i64), ("context_lens", _vp), ("batch", _i32),
+                ("next_n", _i32), ("k", _i32)]
+
+
 class Mxfp4InsertArgs(ctypes.Structure):
     _fields_ = [("kv_fused", _vp), ("k", _vp), ("in_dtype", _i32), ("slot_mapping", _vp),
                 ("num_tokens", _i64), ("num_slots", _i64), ("head_dim", _i32),
@@ -78,7 +84,8 @@ _lib = None
 EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "paged_attn_fwd_noalloc",
            "paged_attn_noalloc_scratch_bytes", "pa_plan", "paged_attn_sparse",
            "paged_attn_sparse_workspace_size", "pa_sparse_plan", "paged_mqa_logits",
-           "paged_mqa_logits_workspace_size", "kv_insert", "kv_insert_mxfp4", "pa_dequantize",
+           "paged_mqa_logits_workspace_size", "pa_topk_select", "kv_insert", "kv_insert_mxfp4",
+           "pa_dequantize",
            "pa_last_error", "pa_set_profile_events"]
 
 
@@ -112,6 +119,8 @@ def load(path: str | None = None):
     lib.paged_mqa_logits.restype = _i32
     lib.paged_mqa_logits_workspace_size.argtypes = [ctypes.POINTER(LogitsArgs)]
     lib.paged_mqa_logits_workspace_size.restype = ctypes.c_size_t
+    lib.pa_topk_select.argtypes = [ctypes.POINTER(TopkArgs), _vp]
+    lib.pa_topk_select.restype = _i32
     lib.kv_insert.argtypes = [ctypes.POINTER(InsertArgs), _vp]
     lib.kv_insert.restype = _i32
     lib.kv_insert_mxfp4.argtypes = [ctypes.POINTER(Mxfp4InsertArgs), _vp]
@@ -458,6 +467,38 @@ def paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_
                                     workspace=workspace, stream=stream)
     call()
     return call.out
+
+
+# ---------------------------------------------------------------------------
+# top-k selection: logits -> per-row token ids for paged_attn_sparse
+# ---------------------------------------------------------------------------
+
+def prepare_topk_select(logits, context_lens, next_n, k, *, sel=None, stream=None):
+    """pa_topk_select with its argument struct built once; the result's .sel is
+    the output [B*next_n, k] int32 (see pa_topk_select in include/pa.h)."""
+    import torch
+    _need(logits, "logits", (torch.float32, torch.float16, torch.bfloat16), 2)
+    _need(context_lens, "context_lens", (torch.int32,), 1)
+    B = context_lens.shape[0]
+    if logits.shape[0] < B * next_n:
+        raise PaError(1, f"logits has {logits.shape[0]} rows, needs {B * next_n}")
+    if sel is None:
+        sel = torch.empty((B * next_n, k), dtype=torch.int32, device=logits.device)
+    _need(sel, "sel", (torch.int32,))
+    a = TopkArgs(sel=_ptr(sel), logits=_ptr(logits), logits_format=_logits_format(logits.dtype),
+                 logits_row_stride=logits.stride(0), context_lens=_ptr(context_lens), batch=B,
+                 next_n=int(next_n), k=int(k))
+    call = Prepared(load().pa_topk_select, a, (sel, logits, context_lens), _stream(stream))
+    call.sel = sel
+    return call
+
+
+def topk_select(logits, context_lens, next_n, k, *, sel=None, stream=None):
+    """Token ids of the k largest logits per row, ascending, -1 padded:
+    int32 [B*next_n, k], ready as paged_attn_sparse's sel (viewed [B, next_n, k])."""
+    call = prepare_topk_select(logits, context_lens, next_n, k, sel=sel, stream=stream)
+    call()
+    return call.sel
 
 
 # ---------------------------------------------------------------------------

@@ -144,4 +144,22 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
+// round trips): shifts by 1, 2, 4, 8 inside each row of 16 lanes (lanes whose
+// source falls outside the row read 0), then lane 15 of rows 0 and 2 is added
+// to rows 1 and 3, and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Value of lane `l` (wave-uniform) in every lane.
+__device__ __forceinline__ int lane_val(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+
 }  // namespace pa

@@ -146,7 +146,8 @@ def test_struct_layouts_match_header(tmp_path):
     """The binding's ctypes structs have the sizes and field offsets the C
     compiler gives the structs of include/pa.h."""
     structs = {"pa_attn_args": pa.AttnArgs, "pa_logits_args": pa.LogitsArgs,
-               "pa_insert_args": pa.InsertArgs, "pa_mxfp4_insert_args": pa.Mxfp4InsertArgs}
+               "pa_insert_args": pa.InsertArgs, "pa_mxfp4_insert_args": pa.Mxfp4InsertArgs,
+               "pa_topk_args": pa.TopkArgs}
     lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "pa.h"', "int main(void) {"]
     for cname, py in structs.items():
         lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from tests import (test_oracle_attn, test_oracle_insert, test_oracle_logits, test_oracle_mxfp4,
-                   test_oracle_sparse)
+                   test_oracle_sparse, test_oracle_topk)
 
 
 def pin_codec_e4m3(lib):
@@ -40,7 +40,7 @@ def pin_codec_round(lib):
 
 PINS = ([pin_codec_e4m3, pin_codec_round] + test_oracle_attn.ALL_PINS +
         test_oracle_logits.ALL_PINS + test_oracle_insert.ALL_PINS + test_oracle_mxfp4.ALL_PINS +
-        test_oracle_sparse.ALL_PINS)
+        test_oracle_sparse.ALL_PINS + test_oracle_topk.ALL_PINS)
 
 MUTATIONS = {
     "gqa_head_map": ("for (int h = hk * group; h < (hk + 1) * group; ++h) {\n        int64_t row",
@@ -102,6 +102,11 @@ MUTATIONS = {
                                "if (!vis[t] || s[t] < m) continue;"),
     "cond_sens_signed": ("vsens[d] += s[t] * fabs((double)vd[(int64_t)t * D + d] - orow[d]);",
                          "vsens[d] += s[t] * ((double)vd[(int64_t)t * D + d] - orow[d]);"),
+    "topk_ties_to_higher_id": ("return (a->t > b->t) - (a->t < b->t);",
+                               "return (a->t < b->t) - (a->t > b->t);"),
+    "topk_nan_first": ("if (an != bn) return an ? 1 : -1;", "if (an != bn) return an ? -1 : 1;"),
+    "topk_tail_candidates": ("for (int t = 0; t < L; ++t) {\n      c[t].v = logit_value(",
+                             "for (int t = 0; t < L; ++t) {\n      c[t].v = t + 1 == L ? 1e30f : logit_value("),
     "mx_sf_token_order": ("(int64_t)sf_slot_of_token(pos, bs, spi, sf_interleaved) * spi;",
                           "(int64_t)pos * spi;"),
 }
