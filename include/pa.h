@@ -454,14 +454,25 @@ pa_status kv_insert(const pa_insert_args* a, void* stream);
 pa_status pa_dequantize(pa_kv_kind kind, const void* codes, int64_t n, const float* scale,
                         pa_scale_mode mode, int64_t channels, float* out, void* stream);
 
+/*
+ * Benchmark probe: reads `bytes` (a multiple of 16) of device memory at `src`
+ * with 16-byte loads from `grid` workgroups of 256 threads, eight loads in
+ * flight per thread, and writes one word per workgroup to sink[0 .. grid) so
+ * the reads are live. Timing it gives the device's streaming-read rate.
+ */
+pa_status pa_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t grid,
+                        void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* pa_last_error(void);
 
 /*
  * Profiling hook for benchmarks: while set, every later paged_attn_fwd /
- * paged_mqa_logits call on the calling thread launches its dominant kernel
- * (the attention ring kernel, the logits kernel) with start_event and
- * stop_event attached to that kernel's dispatch (hipExtLaunchKernelGGL), so
+ * paged_attn_sparse / paged_mqa_logits / pa_topk_select / kv_insert_mxfp4 call
+ * on the calling thread launches its dominant kernel (the attention ring or
+ * prefill kernel, the logits kernel, the top-k kernel, the insert kernel)
+ * with start_event and stop_event attached to that kernel's dispatch
+ * (hipExtLaunchKernelGGL), so
  * the pair measures the kernel alone. Both are hipEvent_t handles owned by the
  * caller; pass NULL, NULL to clear. Returns PA_ERR_INVALID_ARG if exactly one
  * is NULL.

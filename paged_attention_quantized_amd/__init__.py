@@ -85,7 +85,7 @@ EXPORTS = ["paged_attn_fwd", "paged_attn_workspace_size", "paged_attn_fwd_noallo
            "paged_attn_noalloc_scratch_bytes", "pa_plan", "paged_attn_sparse",
            "paged_attn_sparse_workspace_size", "pa_sparse_plan", "paged_mqa_logits",
            "paged_mqa_logits_workspace_size", "pa_topk_select", "kv_insert", "kv_insert_mxfp4",
-           "pa_dequantize",
+           "pa_dequantize", "pa_read_probe",
            "pa_last_error", "pa_set_profile_events"]
 
 
@@ -127,6 +127,8 @@ def load(path: str | None = None):
     lib.kv_insert_mxfp4.restype = _i32
     lib.pa_dequantize.argtypes = [_i32, _vp, _i64, _vp, _i32, _i64, _vp, _vp]
     lib.pa_dequantize.restype = _i32
+    lib.pa_read_probe.argtypes = [_vp, _i64, _vp, _i32, _vp]
+    lib.pa_read_probe.restype = _i32
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_set_profile_events.argtypes = [_vp, _vp]

@@ -168,7 +168,6 @@ extern "C" pa_status pa_topk_select(const pa_topk_args* a, void* stream) {
   p.fmt = a->logits_format;
   p.next_n = a->next_n;
   p.k = a->k;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kTopkThreads), 0,
-                     (hipStream_t)stream, p);
+  launch_timed(topk_kernel, dim3((unsigned)rows), dim3(kTopkThreads), (hipStream_t)stream, p);
   return launch_status("pa_topk_select kernel");
 }
