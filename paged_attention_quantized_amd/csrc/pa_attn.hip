@@ -41,9 +41,10 @@
 //      row's causal limit are selected to p = 0 (never multiplied),
 //   3. V codes from LDS -> fp16, rows of invalid tokens zeroed by select
 //      [NULLPAD, Fix], O^T += V^T P^T with v_mfma_f32_16x16x16_f16.
-// At the end of each (sequence, head group) run inside its range a wave writes
-// its (m, l, c) and unnormalized O as a partial; the merge kernel combines the
-// partials of a (sequence, KV head) in workgroup order, then sub-tile order,
+// At the end of each (sequence, head group) run inside its range the waves of
+// a head fold their sub-tile states in LDS (sub-tile order) and the first
+// writes (m, l, c) and unnormalized O as the workgroup's partial; the merge
+// kernel combines the partials of a (sequence, KV head) in workgroup order
 // and applies v_scale / l.
 //
 // Query rows. Up to 32 rows per KV head (next_n x q heads per KV head) sit in
@@ -68,7 +69,7 @@
 namespace pa {
 
 // Combine the partials of each (sequence b, KV head hk, query row) in a fixed
-// order (workgroup, then sub-tile), which depends on logical positions only
+// order (workgroup order), which depends on logical positions only
 // [RELOC], and apply the V scale and 1/l. A row with no visible token is +0.
 // One thread per 4 output channels; the item ranges of the ring kernel follow
 // from the sequence starts it published.
@@ -98,13 +99,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
   const int nst = run_stages(p, L, rb);
   slot0 += hg * (nst + p.run_cost) + p.run_cost;
   const int i = r / p.G, h = hk * p.G + r % p.G;
-  const int nsub = p.wgmerge ? 1 : p.nsub;
   float m = -INFINITY, l = 0.f;
   f4 o = {0.f, 0.f, 0.f, 0.f};
   if (nst > 0) {
     const int w_first = slot0 / qc, w_last = (slot0 + nst - 1) / qc;
     const int run = (b * p.nrb + rb) * p.hgroups + hg;
-    const int nparts = (w_last - w_first + 1) * nsub;
+    const int nparts = w_last - w_first + 1;
     constexpr int U = 8;
     for (int k0 = 0; k0 < nparts; k0 += U) {
       f4 rec[U], x[U];
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p, int D) {
       for (int k = 0; k < U; ++k) {
         if (k0 + k < nparts) {
           const int part = k0 + k;
-          const size_t u = part_index(p, run, w_first + part / nsub, hl, part % nsub);
+          const size_t u = part_index(p, run, w_first + part, hl);
           rec[k] = p.ws_ml[u * p.rpb + rl];
           x[k] = *reinterpret_cast<const f4*>(p.ws_o + (u * p.rpb + rl) * D + d);
         } else {
@@ -460,11 +460,13 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
   if (sh->nw == 1 && ts > 2 * a->block_size)
     return fail(PA_ERR_UNSUPPORTED, "paged_attn: item spans more than two pages");
   sh->nwg = device_cus();
-  // Sub-tile states are merged inside the workgroup when one head's state (in
-  // the MFMA layout: 16*RT rows x D fp32, plus m and l) fits the LDS exchange
-  // buffer.
-  const int xch_per_head = sh->RT * (a->head_dim / 16) * 1024 + sh->RT * 512;
-  sh->wgmerge = (sh->nsub > 1 && xch_per_head <= kXchBytes) ? 1 : 0;
+  // Sub-tile states are merged inside the workgroup, one row tile of one head
+  // at a time (in the MFMA layout: 16 rows x D fp32, plus m and l, through
+  // the LDS exchange buffer), so every run leaves one partial per head and
+  // workgroup.
+  if (a->head_dim / 16 * 1024 + 512 > kXchBytes)
+    return fail(PA_ERR_UNSUPPORTED, "paged_attn: head_dim too large for the LDS exchange");
+  sh->wgmerge = sh->nsub > 1 ? 1 : 0;
   if (sh->prefill) sh->wgmerge = 1;  // one partial per group: the waves own disjoint rows
   // Cost of a run start in items, for the cost line: the first Q' loads wait
   // for every ring load in flight, the ring refills, the partial is written,
@@ -479,10 +481,9 @@ pa_status check_args(const pa_attn_args* a, Shape* sh, bool need_ptrs, int spars
     sh->run_cost = 2 + (sh->RT == 2 ? 10 : 0) +
                    (sh->wgmerge ? 4 + (sh->hpu * (sh->nsub - 1) + 1) / 2 : 0);
   // partial slots: one per (run, workgroup) pair a run can span, at most
-  // runs + workgroups of them, each with one partial per head (and per
-  // sub-tile when sub-tiles are not merged in the workgroup)
+  // runs + workgroups of them, each with one partial per head
   const int64_t slots = (int64_t)a->batch * sh->nrb * sh->hgroups + sh->nwg;
-  sh->parts = slots * (sh->wgmerge ? sh->hpu : sh->nw);
+  sh->parts = slots * sh->hpu;
   sh->ml_bytes = (size_t)round_up(sh->parts * sh->rpb * 16, 256);
   sh->o_bytes = (size_t)round_up(sh->parts * sh->rpb * a->head_dim * 4, 256);
   // sequence first slots, then the PA_VALIDATE flags

@@ -71,6 +71,7 @@ struct AttnParams {
   int nwg;                         // workgroups of the persistent grid
   int lbs, lts, lhpu;              // log2 of bs, ts, hpu (all powers of two)
   int wgmerge;                     // sub-tile states merged in the workgroup: one partial per head
+                                   // (always, when an item has several sub-tiles)
   int run_cost;                    // work split: items a run start costs (drain, q reload, partial)
   int k_scale_mode, v_scale_mode, causal;
   float softmax_scale;
@@ -763,34 +764,33 @@ __device__ __forceinline__ void compute_tile(const uint8_t* slot, const TileOffs
   }
 }
 
-// Exchange of a wave's softmax state through LDS, in the MFMA register layout
-// (lane-major), so the receiving wave of the same head combines element-wise:
-// o as [rt][q][lane] f4, then m and l as [rt][lane] floats.
+// Exchange of one row tile of a wave's softmax state through LDS, in the MFMA
+// register layout (lane-major), so the receiving wave of the same head
+// combines element-wise: o as [q][lane] f4, then m and l as [lane] floats
+// (D / 16 KiB + 512 bytes). One row tile at a time keeps the buffer small
+// enough for every head_dim and the live registers few.
 template <int KIND, int D, int RT, int QF>
-__device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, QF>& w, float* xbuf) {
+__device__ __forceinline__ void xch_put(const WaveState<KIND, D, RT, QF>& w, int rt, float* xbuf) {
   constexpr int DV = Geo<KIND, D>::DV;
   const int lane = threadIdx.x & 63;
   f4* xo = reinterpret_cast<f4*>(xbuf);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-    for (int q = 0; q < DV; ++q) xo[(rt * DV + q) * 64 + lane] = w.o[rt][q];
-    xbuf[RT * DV * 256 + rt * 64 + lane] = w.m_run[rt];
-    xbuf[RT * DV * 256 + (RT + rt) * 64 + lane] = w.l_acc[rt][0];
-  }
+  for (int q = 0; q < DV; ++q) xo[q * 64 + lane] = w.o[rt][q];
+  xbuf[DV * 256 + lane] = w.m_run[rt];
+  xbuf[DV * 256 + 64 + lane] = w.l_acc[rt][0];
 }
 
-// Combine the state in xbuf into w (w first, then xbuf: a fixed order).
+// Combine row tile rt of the state in xbuf into w (w first, then xbuf: a
+// fixed order).
 template <int KIND, int D, int RT, int QF>
-__device__ __forceinline__ void xch_merge(WaveState<KIND, D, RT, QF>& w, const float* xbuf,
+__device__ __forceinline__ void xch_merge(WaveState<KIND, D, RT, QF>& w, int rt, const float* xbuf,
                                           float c2) {
   constexpr int DV = Geo<KIND, D>::DV;
   const int lane = threadIdx.x & 63;
   const f4* xo = reinterpret_cast<const f4*>(xbuf);
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const float mb = xbuf[RT * DV * 256 + rt * 64 + lane];
-    const float lb = xbuf[RT * DV * 256 + (RT + rt) * 64 + lane];
+  {
+    const float mb = xbuf[DV * 256 + lane];
+    const float lb = xbuf[DV * 256 + 64 + lane];
     const float ma = w.m_run[rt];
     const float mn = fmaxf(ma, mb);
     const float a = ma == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ma - mn) * c2);
@@ -800,7 +800,7 @@ __device__ __forceinline__ void xch_merge(WaveState<KIND, D, RT, QF>& w, const f
     w.m_run[rt] = mn;
 #pragma unroll
     for (int q = 0; q < DV; ++q) {
-      w.o[rt][q] = w.o[rt][q] * a + xo[(rt * DV + q) * 64 + lane] * bw;
+      w.o[rt][q] = w.o[rt][q] * a + xo[q * 64 + lane] * bw;
       __builtin_amdgcn_sched_barrier(0);  // keep one f4 in flight: register pressure
     }
   }
@@ -814,11 +814,11 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Partial index of (run r, workgroup w, head-in-group hl, sub-tile st); run
+// Partial index of (run r, workgroup w, head-in-group hl); run
 // r = (b * nrb + rb) * hgroups + hg. Slot r + w is unique: a later workgroup only reaches
 // later runs, so (r, w) != (r', w') with r + w == r' + w' cannot both occur.
-__device__ __forceinline__ size_t part_index(const AttnParams& p, int r, int w, int hl, int st) {
-  return ((size_t)(r + w) * p.hpu + hl) * (p.wgmerge ? 1 : p.nsub) + st;
+__device__ __forceinline__ size_t part_index(const AttnParams& p, int r, int w, int hl) {
+  return (size_t)(r + w) * p.hpu + hl;
 }
 
 // Adds column (n + 8) mod 16 of a packed state to column n (row_ror:8): the
@@ -1111,22 +1111,21 @@ __global__ __launch_bounds__(64 * NWB) void attn_ring_kernel(
     item_next(p, lens, cp);
     if (j + 1 == nitems || cp.b != b || cp.hg != hg || cp.rb != rb) {
       const int run = (b * p.nrb + rb) * p.hgroups + hg;
-      if (p.wgmerge) {
-        // fold sub-tiles 1 .. nsub-1 of each head into sub-tile 0, in order
+      if (p.nsub > 1) {
+        // fold sub-tiles 1 .. nsub-1 of each head into sub-tile 0, in order,
+        // one row tile at a time
         for (int h = 0; h < p.hpu; ++h)
-          for (int s2 = 1; s2 < p.nsub; ++s2) {
-            if (hl == h && st == s2) xch_put<KIND, D, RT, QF>(w, xbuf);
-            lds_barrier();
-            if (hl == h && st == 0) xch_merge<KIND, D, RT, QF>(w, xbuf, c2);
-            lds_barrier();
-          }
-        if (st == 0)
-          write_partial<KIND, D, RT, QF>(p, part_index(p, run, blockIdx.x, hl, 0),
-                                           c2, w);
-      } else {
-        write_partial<KIND, D, RT, QF>(p, part_index(p, run, blockIdx.x, hl, st),
-                                         c2, w);
+          for (int s2 = 1; s2 < p.nsub; ++s2)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              if (hl == h && st == s2) xch_put<KIND, D, RT, QF>(w, rt, xbuf);
+              lds_barrier();
+              if (hl == h && st == 0) xch_merge<KIND, D, RT, QF>(w, rt, xbuf, c2);
+              lds_barrier();
+            }
       }
+      if (st == 0)
+        write_partial<KIND, D, RT, QF>(p, part_index(p, run, blockIdx.x, hl), c2, w);
       if (j + 1 < nitems)
         start_run<KIND, D, RT, QF>(p, cp.b, cp.rb, cp.hg * p.hpu + hl, cp.L, inv_m, sgn, w);
     }
@@ -1506,7 +1505,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void attn_prefill_kernel(
     if (j + 1 == nitems || cp.b != b || cp.hg != hg || cp.rb != rb) {
       const int run = (b * p.nrb + rb) * p.hgroups + hg;
       if (row0_of(rb) < p.R)
-        write_partial<KIND, D, 2, QF>(p, part_index(p, run, blockIdx.x, 0, 0), c2, w,
+        write_partial<KIND, D, 2, QF>(p, part_index(p, run, blockIdx.x, 0), c2, w,
                                         32 * wv);
       if (j + 1 < nitems)
         pf_start_run<KIND, D, QF>(p, cp.b, row0_of(cp.rb), cp.hg, cp.L, inv_m, sgn, w);
