@@ -342,22 +342,6 @@ int ilog2(int x) {  // x is a power of two
   return r;
 }
 
-// Compute units of the current device (the persistent grid size), cached per
-// device; threads may race to fill an entry, all with the same value.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 PrefillFn pick_prefill_fn(int kind, int D, bool fold) {
   switch (kind) {
     case PA_KV_F16: return pick_prefill_f16(D, fold);

@@ -1,5 +1,7 @@
-// pa_common.hip -- thread-local error state of libpa.
+// pa_common.hip -- thread-local error state of libpa, and device queries.
 #include <string.h>
+
+#include <atomic>
 
 #include "pa_host.hpp"
 
@@ -31,6 +33,22 @@ bool prof_events(hipEvent_t* start, hipEvent_t* stop) {
 void set_prof_events(void* start, void* stop) {
   g_prof_start = (hipEvent_t)start;
   g_prof_stop = (hipEvent_t)stop;
+}
+
+// Compute units of the current device (the persistent grid size), cached per
+// device; threads may race to fill an entry, all with the same value.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 pa_status launch_status(const char* what) {

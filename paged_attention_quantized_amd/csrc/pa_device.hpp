@@ -161,5 +161,33 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // Value of lane `l` (wave-uniform) in every lane.
 __device__ __forceinline__ int lane_val(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 
+// wave-uniform values, said so to the compiler (kept in SGPRs)
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uni64(uint64_t x) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32);
+}
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4,
+// scalar-base form): lane i of the wave writes lds + 16 * i, reading
+// sbase + voff; lds and sbase are wave-uniform. The load is issued through
+// inline asm so that the compiler does not treat the asynchronous LDS write as
+// something every later LDS read has to wait for (it would wait for the whole
+// ring); the ring's own vmcnt + barrier protocol orders writes and reads. The
+// asm sets M0 itself; nothing else in these kernels uses M0. An LDS DMA that
+// reads M0 right after a scalar write of M0 needs one wait state on gfx950
+// (the compiler puts an s_nop between the pair when it emits them itself), so
+// the asm carries it too.
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, const uint8_t* lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  // the base is uniform by construction; saying so keeps it in SGPRs
+  const uint64_t sb = uni64((uint64_t)(uintptr_t)sbase);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v),
+               "v"(voff), "s"(sb)
+               : "memory");
+}
+
+
+
 
 }  // namespace pa

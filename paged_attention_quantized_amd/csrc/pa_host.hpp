@@ -15,6 +15,9 @@ namespace pa {
 pa_status fail(pa_status st, const char* fmt, ...);
 void clear_error();
 pa_status launch_status(const char* what);
+// Compute units of the current device (persistent grids take one or a few
+// workgroups per unit).
+int device_cus();
 // Profiling events set by pa_set_profile_events (false if none).
 bool prof_events(hipEvent_t* start, hipEvent_t* stop);
 

@@ -8,13 +8,17 @@
 //      so a wave waits for one table lookup and one round of loads in all;
 //   2. S[h][t] = q_h . k_t with v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1,
 //      E8M0 scales per 32 channels, fp32 result; head_dim 128 is one MFMA);
-//      M rows are heads, N columns are tokens, and the heads of a row tile are
-//      laid out so that lane group g ends up holding heads [g*H/4, (g+1)*H/4);
+//      M rows are heads, N columns are tokens; row tile rt holds heads
+//      [16 rt, 16 rt + 16), so after its four token tiles lane group g holds
+//      heads 16 rt + 4 g .. 16 rt + 4 g + 3 of token 16 tau + j;
 //   3. a 4x4 transpose of (lane group, token tile) with permlane32/16 swaps
-//      moves all heads of one token into one lane;
-//   4. each lane runs the fp32 fma chain over heads in ascending order,
-//      weights[row, h] * S[h][t], and stores its token's logit (64 consecutive
-//      tokens per store instruction); tokens past the sequence get -inf.
+//      moves the row tile's 16 heads of one token into one lane;
+//   4. each lane continues the fp32 fma chain over those heads in ascending
+//      order, weights[row, h] * S[h][t] (weights read four at a time), one
+//      row tile after the other, so only one row tile's scores are live and a
+//      wave needs few registers (eight waves per SIMD hide the chain's
+//      latency); then it stores its token's logit (64 consecutive tokens per
+//      store instruction); tokens past the sequence get -inf.
 // Blocks past the sequence are never read; their columns are written as -inf.
 #include <math.h>
 
@@ -25,7 +29,7 @@
 #define LOGITS_NB 1
 #endif
 #ifndef LOGITS_WPE
-#define LOGITS_WPE 3
+#define LOGITS_WPE 8
 #endif
 
 namespace pa {
@@ -63,30 +67,30 @@ __device__ __forceinline__ float epi_round(float x) {
   else return x;
 }
 
-// The weighted head chain of one token, heads in ascending order: acc =
-// fma(w_h, A(S_h), acc) in fp32, or with a reduced-precision epilogue the
-// weight and A(S_h) rounded to that type and every step's result rounded to
-// it too [FP4API, epi_dtype; the page does not define the arithmetic: the
-// reading taken is rounding at those three points]. A is the identity or the
-// rectifier.
-template <int EPI, int NTI, int HG>
-__device__ __forceinline__ float head_chain(const float (&s)[NTI][4][4], const float* wrow,
-                                            bool relu) {
-  float acc = 0.f;
+// One row tile's 16 heads of the weighted head chain of one token, continuing
+// acc, heads in ascending order: acc = fma(w_h, A(S_h), acc) in fp32, or with
+// a reduced-precision epilogue the weight and A(S_h) rounded to that type and
+// every step's result rounded to it too [FP4API, epi_dtype; the page does not
+// define the arithmetic: the reading taken is rounding at those three points].
+// A is the identity or the rectifier. s[t][e] holds head 4 t + e of the tile,
+// wrow the tile's 16 weights (16-byte aligned: read four at a time).
+template <int EPI>
+__device__ __forceinline__ float head_chain16(const float (&s)[4][4], const float* wrow, bool relu,
+                                              float acc) {
 #pragma unroll
-  for (int tau = 0; tau < 4; ++tau)
+  for (int t = 0; t < 4; ++t) {
+    const f4 w = *reinterpret_cast<const f4*>(wrow + 4 * t);
 #pragma unroll
-    for (int rt = 0; rt < NTI; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = s[rt][tau][e];
-        if (relu) x = x > 0.f ? x : 0.f;
-        float f = fmaf(wrow[HG * tau + 4 * rt + e], epi_round<EPI>(x), acc);
-        // the fp32 result is a value of its own: the compiler would otherwise
-        // fuse the fma and the fp16 conversion into one rounding (v_fma_mix)
-        if constexpr (EPI != PA_LOGITS_F32) asm volatile("" : "+v"(f));
-        acc = epi_round<EPI>(f);
-      }
+    for (int e = 0; e < 4; ++e) {
+      float x = s[t][e];
+      if (relu) x = x > 0.f ? x : 0.f;
+      float f = fmaf(w[e], epi_round<EPI>(x), acc);
+      // the fp32 result is a value of its own: the compiler would otherwise
+      // fuse the fma and the fp16 conversion into one rounding (v_fma_mix)
+      if constexpr (EPI != PA_LOGITS_F32) asm volatile("" : "+v"(f));
+      acc = epi_round<EPI>(f);
+    }
+  }
   return acc;
 }
 
@@ -124,7 +128,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   constexpr int D = 128, BS = 64;
   constexpr int CH = NB * BS;  // tokens per chunk
   constexpr int NTI = H / 16;  // row tiles per query row
-  constexpr int HG = H / 4;    // heads per lane group after the MFMA
   constexpr int ROWB = D / 2;  // FP4 bytes per token
   constexpr int SFB = D / 32;  // scale bytes per token
   constexpr int BLK = BS * (ROWB + SFB);
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   static_assert(NN * H <= 256, "one scale word per thread");
   __shared__ __attribute__((aligned(16))) uint8_t qlds[NN * H * ROWB];
   __shared__ int32_t sflds[NN * H];
-  __shared__ float wlds[NN * H];
+  __shared__ __attribute__((aligned(16))) float wlds[NN * H];
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = blockIdx.x % p.ngroups, b = blockIdx.x / p.ngroups;
@@ -226,43 +229,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
     const int t = t_chunk + k * BS + lane;  // the token this lane stores
 #pragma unroll
     for (int i = 0; i < NN; ++i) {
-      float s[NTI][4][4];  // [rt][tau][e]
+      // the weights are staged in LDS already rounded to the epilogue type
+      const float* wrow = wlds + i * H;
+      float acc = 0.f;
 #pragma unroll
       for (int rt = 0; rt < NTI; ++rt) {
-        // A rows are heads: row j of row tile rt holds head HG*(j/4) + 4*rt + j%4,
-        // lane group g its channels [32g, 32g+32)
-        const int h = HG * (j >> 2) + 4 * rt + (j & 3);
+        // A rows are heads: row j of row tile rt holds head 16 rt + j, lane
+        // group g its channels [32g, 32g+32)
+        const int h = 16 * rt + j;
         const u4 v = *reinterpret_cast<const u4*>(qlds + (i * H + h) * ROWB + 16 * g);
         const i8v qa = i8v{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
         const int qs = (sflds[i * H + h] >> (8 * g)) & 0xFF;
+        float sc[4][4];  // [tau][e]
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           // B columns are tokens: column j of token tile tau is token 16*tau + j
           const u4 kv4 = kraw[k][tau];
           const i8v kb = i8v{(int)kv4[0], (int)kv4[1], (int)kv4[2], (int)kv4[3], 0, 0, 0, 0};
-          const f4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          const f4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               qa, kb, f4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, qs, 0, ks[k][tau]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[rt][tau][e] = acc[e];
+          for (int e = 0; e < 4; ++e) sc[tau][e] = c[e];
         }
+        // lane (j, g) holds heads 16 rt + 4 g + e of tokens 16 tau + j; after
+        // the transpose, sc[t][e] of lane (j, g) is head 16 rt + 4 t + e of
+        // token 16 g + j
+#pragma unroll
+        for (int e = 0; e < 4; ++e) transpose4(sc[0][e], sc[1][e], sc[2][e], sc[3][e]);
+        if (p.epi == PA_LOGITS_F16)
+          acc = head_chain16<PA_LOGITS_F16>(sc, wrow + 16 * rt, p.relu, acc);
+        else if (p.epi == PA_LOGITS_BF16)
+          acc = head_chain16<PA_LOGITS_BF16>(sc, wrow + 16 * rt, p.relu, acc);
+        else if (p.relu)
+          acc = head_chain16<PA_LOGITS_F32>(sc, wrow + 16 * rt, true, acc);
+        else
+          acc = head_chain16<PA_LOGITS_F32>(sc, wrow + 16 * rt, false, acc);
       }
-      // lane (j, g) holds heads HG*g + 4*rt + e of tokens 16*tau + j; transpose so
-      // that lane (j, g) holds heads HG*tau + 4*rt + e of token 16*g + j
-#pragma unroll
-      for (int rt = 0; rt < NTI; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) transpose4(s[rt][0][e], s[rt][1][e], s[rt][2][e], s[rt][3][e]);
-      // the weights are staged in LDS already rounded to the epilogue type
-      const float* wrow = wlds + i * H;
-      float acc;
-      if (p.epi == PA_LOGITS_F16)
-        acc = head_chain<PA_LOGITS_F16, NTI, HG>(s, wrow, p.relu);
-      else if (p.epi == PA_LOGITS_BF16)
-        acc = head_chain<PA_LOGITS_BF16, NTI, HG>(s, wrow, p.relu);
-      else if (p.relu)
-        acc = head_chain<PA_LOGITS_F32, NTI, HG>(s, wrow, true);
-      else
-        acc = head_chain<PA_LOGITS_F32, NTI, HG>(s, wrow, false);
       if (t < p.max_ctx) orow[(size_t)i * p.out_stride + t] = (OT)(t < L ? acc : -INFINITY);
     }
   }
