@@ -86,22 +86,31 @@ struct Kv<PA_KV_INT8> {
 };
 
 // INT4: eight signed nibbles per dword (element k at bits 4k..4k+3). Flipping
-// bit 3 of every nibble maps value v to v + 8 in [0, 15]; nibbles k and k+4 are
-// masked under the fp16 exponent of 1024 and 1032 is subtracted. Mask, flip
-// and exponent are one 3-input bitwise op, (s & 0x000F000F) ^ 0x64086408 (the
-// exponent bits are zero after the mask, so the xor sets them). The pairs come
-// out as (e0,e4), (e1,e5), (e2,e6), (e3,e7).
+// bit 3 of a nibble maps value v to u = v + 8 in [0, 15]. Nibbles k and k + 4
+// (k = 0, 2) are masked into bits 0-3 of each fp16 half under the exponent of
+// 1024, and 1032 is subtracted; nibbles k = 1, 3 are masked in place (bits
+// 4-7: the half reads 1024 + 16 u) and one fma takes x / 16 - 72 = u - 8 (every
+// step exact). Mask, flip and exponent are one 3-input bitwise op,
+// (s & mask) ^ (exponent | flip) (the exponent bits are zero after the mask,
+// so the xor sets them), and only the upper byte pair needs a shift: 9
+// instructions per 8 values. The pairs come out as (e0,e4), (e1,e5), (e2,e6),
+// (e3,e7).
 template <>
 struct Kv<PA_KV_INT4> {
   static constexpr int kBits = 4;
   static constexpr int kPairsPerDword = 4;
   __device__ static void decode(uint32_t w, h2* out) {
     const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      // truth table 0x6A: (a & b) ^ c, a = the shifted codes, b = mask, c = exponent | flip
-      out[k] = as_h2(__builtin_amdgcn_bitop3_b32(w >> (4 * k), 0x000F000Fu, 0x64086408u, 0x6A)) -
-               bias;
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t w8 = w >> 8;
+    // truth table 0x6A: (a & b) ^ c, a = the codes, b = mask, c = exponent | flip
+    out[0] = as_h2(__builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64086408u, 0x6A)) - bias;
+    out[1] = __builtin_elementwise_fma(
+        as_h2(__builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64806480u, 0x6A)), sixteenth, bias16);
+    out[2] = as_h2(__builtin_amdgcn_bitop3_b32(w8, 0x000F000Fu, 0x64086408u, 0x6A)) - bias;
+    out[3] = __builtin_elementwise_fma(
+        as_h2(__builtin_amdgcn_bitop3_b32(w8, 0x00F000F0u, 0x64806480u, 0x6A)), sixteenth, bias16);
   }
   // slot e of the 8 fp16 values produced from one dword holds element order(e)
   __device__ static constexpr int order(int e) { return (e >> 1) + 4 * (e & 1); }
