@@ -411,7 +411,7 @@ def _logits_args(out, q, sf_q, kv_fused, weights, context_lens, block_table, max
                  sf_vec_size, out_format=LOGITS_F32, epi_format=LOGITS_F32, sf_interleaved=False,
                  relu=False):
     B, next_n, H, Dh = q.shape
-    return LogitsArgs(out=_ptr(out), out_row_stride=out.stride(0) if out is not None else 0,
+    return LogitsArgs(out=_ptr(out), out_row_stride=_row_stride(out) if out is not None else 0,
                       q=_ptr(q), sf_q=_ptr(sf_q), kv_fused=_ptr(kv_fused), weights=_ptr(weights),
                       context_lens=_ptr(context_lens), block_table=_ptr(block_table), batch=B,
                       next_n=next_n, num_heads=H, head_dim=2 * Dh, block_size=kv_fused.shape[1],
@@ -475,6 +475,12 @@ def paged_mqa_logits(q, sf_q, kv_fused, weights, context_lens, block_table, max_
 # top-k selection: logits -> per-row token ids for paged_attn_sparse
 # ---------------------------------------------------------------------------
 
+def _row_stride(t):
+    """Elements between rows of a 2-D tensor (a tensor of one row may carry
+    any stride for its first dimension; its row length is used)."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
 def prepare_topk_select(logits, context_lens, next_n, k, *, sel=None, stream=None):
     """pa_topk_select with its argument struct built once; the result's .sel is
     the output [B*next_n, k] int32 (see pa_topk_select in include/pa.h)."""
@@ -488,7 +494,7 @@ def prepare_topk_select(logits, context_lens, next_n, k, *, sel=None, stream=Non
         sel = torch.empty((B * next_n, k), dtype=torch.int32, device=logits.device)
     _need(sel, "sel", (torch.int32,))
     a = TopkArgs(sel=_ptr(sel), logits=_ptr(logits), logits_format=_logits_format(logits.dtype),
-                 logits_row_stride=logits.stride(0), context_lens=_ptr(context_lens), batch=B,
+                 logits_row_stride=_row_stride(logits), context_lens=_ptr(context_lens), batch=B,
                  next_n=int(next_n), k=int(k))
     call = Prepared(load().pa_topk_select, a, (sel, logits, context_lens), _stream(stream))
     call.sel = sel

@@ -30,10 +30,38 @@ def cases():
     x = np.zeros((2, 1500), np.float32)
     x[1, ::2] = -0.0
     out.append(("all_equal_signed_zeros", x, np.array([1500, 1499], np.int32), 1, 77))
+    # a row stride that is not a multiple of 4 (the keys are read one at a time)
+    x = rng.standard_normal((4, 2999)).astype(np.float32)
+    out.append(("odd_stride", x, np.array([2999, 2500], np.int32), 2, 512))
+    # full-length rows of widely spread values (the candidate route)
+    x = (rng.standard_normal((3, 32768)) * 5000).astype(np.float32)
+    out.append(("wide_full", x, np.array([32768, 32767, 20001], np.int32), 1, 2048))
+    # long rows of one value: more keys share the pivot bins than the
+    # candidate lists hold (the radix route)
+    x = np.zeros((2, 20000), np.float32)
+    out.append(("all_equal_long", x, np.array([20000, 19000], np.int32), 1, 100))
+    out.append(("sample_miss", sample_miss_row(20000), np.array([20000], np.int32), 1, 2048))
     return out
 
 
-@pytest.mark.parametrize("idx", range(5))
+def sample_miss_row(L):
+    """One row whose large values sit only at ids the pivot route does not
+    sample: wave w of 16 owns ids [w c, (w + 1) c), c = round_up(ceil(L / 16),
+    256), and samples offset o = 256 u + 4 l + e when u and lane l have the
+    same parity and e = (l >> 4) & 3. The sample sees only small values, so
+    its pivots put almost every key above T and the row takes the radix
+    route."""
+    rng = np.random.default_rng(67)
+    c = ((L + 15) // 16 + 255) // 256 * 256
+    ids = np.arange(L)
+    o = ids % c
+    u, l, e = o // 256, (o % 256) // 4, o % 4
+    sampled = ((u & 1) == (l & 1)) & (e == ((l >> 4) & 3))
+    x = np.where(sampled, rng.random(L), 10.0 + rng.random(L)).astype(np.float32)
+    return x.reshape(1, L).copy()
+
+
+@pytest.mark.parametrize("idx", range(9))
 @pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
 def test_topk_bit_exact(pa, idx, fmt):
     name, x, lens, N, k = cases()[idx]
