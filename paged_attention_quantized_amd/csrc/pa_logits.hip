@@ -1,24 +1,25 @@
 // pa_logits.hip -- MXFP4 paged MQA logits on gfx950 [FP4API].
 //
-// Work unit = (sequence b, 256-token chunk), one wavefront. For the 64-token KV
-// blocks of the chunk that hold visible tokens:
-//   1. gather the blocks through block_table: each lane loads 16 FP4 bytes (32
-//      channels = one scale group) of one token and that group's UE8M0 byte.
-//      The loads of all blocks of the chunk are issued before the first MFMA,
-//      so a wave waits for one table lookup and one round of loads in all;
-//   2. S[h][t] = q_h . k_t with v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1,
-//      E8M0 scales per 32 channels, fp32 result; head_dim 128 is one MFMA);
-//      M rows are heads, N columns are tokens; row tile rt holds heads
-//      [16 rt, 16 rt + 16), so after its four token tiles lane group g holds
-//      heads 16 rt + 4 g .. 16 rt + 4 g + 3 of token 16 tau + j;
-//   3. a 4x4 transpose of (lane group, token tile) with permlane32/16 swaps
-//      moves the row tile's 16 heads of one token into one lane;
-//   4. each lane continues the fp32 fma chain over those heads in ascending
+// Work unit = (sequence b, 64-token block), one wavefront; a workgroup is
+// four consecutive blocks of one sequence. For a block that holds visible
+// tokens:
+//   1. gather it through block_table: lane l loads, for token tile tau (32
+//      tokens) and K half kh, the 16 FP4 bytes of token 32 tau + l % 32 at
+//      channels 64 kh + 32 (l / 32) .. + 32 (one scale group) and that group's
+//      UE8M0 byte. All loads are issued before the first MFMA;
+//   2. S = q . k with v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 x E2M1, E8M0
+//      scales per 32 channels, fp32 result; head_dim 128 is two MFMAs). A row
+//      rho of a 32-row tile is query row 2P + ((rho >> 2) & 1) of row pair P
+//      and head 16 ht + 4 (rho >> 3) + (rho & 3) of head tile ht; B columns
+//      are the 32 tokens of a token tile. The 32x32 result puts row
+//      8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32 in register r of lane
+//      l, so lane l holds heads 16 ht .. 16 ht + 15 of its own (query row
+//      2P + l / 32, token 32 tau + l % 32), head 16 ht + r in register r: no
+//      data moves between lanes;
+//   3. each lane continues the fp32 fma chain over those heads in ascending
 //      order, weights[row, h] * S[h][t] (weights read four at a time), one
-//      row tile after the other, so only one row tile's scores are live and a
-//      wave needs few registers (eight waves per SIMD hide the chain's
-//      latency); then it stores its token's logit (64 consecutive tokens per
-//      store instruction); tokens past the sequence get -inf.
+//      head tile after the other; then it stores its logit (32 consecutive
+//      tokens of one row per half-wave); tokens past the sequence get -inf.
 // Blocks past the sequence are never read; their columns are written as -inf.
 #include <math.h>
 
@@ -29,12 +30,13 @@
 #define LOGITS_NB 1
 #endif
 #ifndef LOGITS_WPE
-#define LOGITS_WPE 8
+#define LOGITS_WPE 6
 #endif
 
 namespace pa {
 
 typedef int i8v __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr int kLogitsBlocks = LOGITS_NB;  // 64-token blocks per wave
 
@@ -94,21 +96,6 @@ __device__ __forceinline__ float head_chain16(const float (&s)[4][4], const floa
   return acc;
 }
 
-// 4x4 transpose of (lane group, register): after it, register t of lane group
-// g holds what register g of lane group t held.
-__device__ __forceinline__ void transpose4(float& r0, float& r1, float& r2, float& r3) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(r0), __float_as_uint(r2), false,
-                                            false);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(r1), __float_as_uint(r3), false,
-                                            false);
-  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  r0 = __uint_as_float(c[0]);
-  r1 = __uint_as_float(c[1]);
-  r2 = __uint_as_float(d[0]);
-  r3 = __uint_as_float(d[1]);
-}
-
 // Keeps a loaded value where it is: the empty asm needs the value in a register
 // here, so the compiler can neither sink the load into a later branch nor
 // split the loads of a chunk into several waits.
@@ -137,7 +124,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   __shared__ __attribute__((aligned(16))) uint8_t qlds[NN * H * ROWB];
   __shared__ int32_t sflds[NN * H];
   __shared__ __attribute__((aligned(16))) float wlds[NN * H];
-  const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = blockIdx.x % p.ngroups, b = blockIdx.x / p.ngroups;
   const int L = p.context_lens[b];
@@ -153,7 +140,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   // column k, clamped to the last column inside max_context_len), the q rows of
   // the sequence (each thread QP 16-byte pieces), their scales and weights ----
   const int32_t* trow = p.block_table + (size_t)b * p.max_blocks + t_chunk / BS;
-  const int pg_lane = nblk > 0 ? trow[min(lane, nblk - 1)] : 0;
+  // (a wave with no visible block loads nothing: it only writes -inf columns)
+  const int pg_lane = nvis > 0 ? trow[min(lane, nblk - 1)] : 0;
   u4 qv[QP];
   int sfv = 0;
   float wv = 0.f;
@@ -168,9 +156,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
     }
   }
 
-  // ---- the FP4 rows and scale bytes of all blocks of the chunk. A block with
-  // no visible token takes the chunk's first block: its loads hit lines already
-  // in flight and are never used; a chunk with none reads nothing ----
+  // ---- the FP4 rows and scale bytes of all blocks of the chunk: piece
+  // 2 tau + kh of lane l is token 32 tau + l % 32, channels 64 kh + 32 (l / 32)
+  // .. + 32. A block with no visible token takes the chunk's first block: its
+  // loads hit lines already in flight and are never used; a chunk with none
+  // reads nothing ----
+  const int c32 = lane & 31, hw = lane >> 5;
   u4 kraw[NB][4];
   int ks[NB][4];
   if (nvis > 0) {
@@ -179,15 +170,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
       const int pg = __builtin_amdgcn_readlane(pg_lane, k < nvis ? k : 0);
       const uint8_t* blk = p.kv + (size_t)pg * BLK;
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        const int tok = 16 * tau + j;
+      for (int tau = 0; tau < 2; ++tau) {
+        const int tok = 32 * tau + c32;
         // scale slot of the token: token order, or the interleaved order in
         // which slot k holds token (k % SFB) * (BS / SFB) + k / SFB [FP4API,
-        // is_kv_sf_interleaved]; for tok = 16 tau + j that slot is 4 j + tau
+        // is_kv_sf_interleaved]: token 16 a + c sits in slot SFB c + a
         static_assert(SFB == 4 && BS / SFB == 16, "interleaved slot arithmetic");
-        const int slot = p.sfi ? SFB * j + tau : tok;
-        kraw[k][tau] = *reinterpret_cast<const u4*>(blk + tok * ROWB + 16 * g);
-        ks[k][tau] = blk[BS * ROWB + slot * SFB + g];
+        const int slot = p.sfi ? SFB * (tok & 15) + (tok >> 4) : tok;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          kraw[k][2 * tau + kh] = *reinterpret_cast<const u4*>(blk + tok * ROWB + 32 * kh + 16 * hw);
+          ks[k][2 * tau + kh] = blk[BS * ROWB + slot * SFB + 2 * kh + hw];
+        }
       }
     }
   }
@@ -223,49 +217,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
       pin(ks[k][tau]);
     }
 
+  // A rows of this lane: rho = l % 32 is query row 2P + ((rho >> 2) & 1) of the
+  // row pair and head 16 ht + 4 (rho >> 3) + (rho & 3)
+  const int a_s = (c32 >> 2) & 1, a_h = 4 * (c32 >> 3) + (c32 & 3);
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     if (k >= nvis) continue;
-    const int t = t_chunk + k * BS + lane;  // the token this lane stores
 #pragma unroll
-    for (int i = 0; i < NN; ++i) {
+    for (int P = 0; P < (NN + 1) / 2; ++P) {
+      const int row = 2 * P + hw;                  // the query row this lane chains
+      const int arow = min(2 * P + a_s, NN - 1);   // the query row of its A rows
       // the weights are staged in LDS already rounded to the epilogue type
-      const float* wrow = wlds + i * H;
-      float acc = 0.f;
+      const float* wrow = wlds + min(row, NN - 1) * H;
+      float acc[2] = {0.f, 0.f};
 #pragma unroll
-      for (int rt = 0; rt < NTI; ++rt) {
-        // A rows are heads: row j of row tile rt holds head 16 rt + j, lane
-        // group g its channels [32g, 32g+32)
-        const int h = 16 * rt + j;
-        const u4 v = *reinterpret_cast<const u4*>(qlds + (i * H + h) * ROWB + 16 * g);
-        const i8v qa = i8v{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-        const int qs = (sflds[i * H + h] >> (8 * g)) & 0xFF;
-        float sc[4][4];  // [tau][e]
+      for (int ht = 0; ht < NTI; ++ht) {
+        const int h = 16 * ht + a_h;
+        i8v qa[2];
+        int qs[2];
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-          // B columns are tokens: column j of token tile tau is token 16*tau + j
-          const u4 kv4 = kraw[k][tau];
-          const i8v kb = i8v{(int)kv4[0], (int)kv4[1], (int)kv4[2], (int)kv4[3], 0, 0, 0, 0};
-          const f4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              qa, kb, f4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, qs, 0, ks[k][tau]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sc[tau][e] = c[e];
+        for (int kh = 0; kh < 2; ++kh) {
+          const u4 v = *reinterpret_cast<const u4*>(qlds + (arow * H + h) * ROWB + 32 * kh + 16 * hw);
+          qa[kh] = i8v{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+          qs[kh] = (sflds[arow * H + h] >> (8 * (2 * kh + hw))) & 0xFF;
         }
-        // lane (j, g) holds heads 16 rt + 4 g + e of tokens 16 tau + j; after
-        // the transpose, sc[t][e] of lane (j, g) is head 16 rt + 4 t + e of
-        // token 16 g + j
 #pragma unroll
-        for (int e = 0; e < 4; ++e) transpose4(sc[0][e], sc[1][e], sc[2][e], sc[3][e]);
-        if (p.epi == PA_LOGITS_F16)
-          acc = head_chain16<PA_LOGITS_F16>(sc, wrow + 16 * rt, p.relu, acc);
-        else if (p.epi == PA_LOGITS_BF16)
-          acc = head_chain16<PA_LOGITS_BF16>(sc, wrow + 16 * rt, p.relu, acc);
-        else if (p.relu)
-          acc = head_chain16<PA_LOGITS_F32>(sc, wrow + 16 * rt, true, acc);
-        else
-          acc = head_chain16<PA_LOGITS_F32>(sc, wrow + 16 * rt, false, acc);
+        for (int tau = 0; tau < 2; ++tau) {
+          f16v c = {};
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const u4 kv4 = kraw[k][2 * tau + kh];
+            const i8v kb = i8v{(int)kv4[0], (int)kv4[1], (int)kv4[2], (int)kv4[3], 0, 0, 0, 0};
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[kh], kb, c, 4, 4, 0, qs[kh], 0,
+                                                                 ks[k][2 * tau + kh]);
+          }
+          // register 4 t + e holds head 16 ht + 4 t + e of this lane's (row, token)
+          float sc[4][4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[t][e] = c[4 * t + e];
+          if (p.epi == PA_LOGITS_F16)
+            acc[tau] = head_chain16<PA_LOGITS_F16>(sc, wrow + 16 * ht, p.relu, acc[tau]);
+          else if (p.epi == PA_LOGITS_BF16)
+            acc[tau] = head_chain16<PA_LOGITS_BF16>(sc, wrow + 16 * ht, p.relu, acc[tau]);
+          else if (p.relu)
+            acc[tau] = head_chain16<PA_LOGITS_F32>(sc, wrow + 16 * ht, true, acc[tau]);
+          else
+            acc[tau] = head_chain16<PA_LOGITS_F32>(sc, wrow + 16 * ht, false, acc[tau]);
+        }
       }
-      if (t < p.max_ctx) orow[(size_t)i * p.out_stride + t] = (OT)(t < L ? acc : -INFINITY);
+      if (row < NN) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          const int t = t_chunk + k * BS + 32 * tau + c32;
+          if (t < p.max_ctx) orow[(size_t)row * p.out_stride + t] = (OT)(t < L ? acc[tau] : -INFINITY);
+        }
+      }
     }
   }
 }
