@@ -1,6 +1,6 @@
 // pa_logits.hip -- MXFP4 paged MQA logits on gfx950 [FP4API].
 //
-// Work unit = (sequence b, 64-token block), one wavefront; a workgroup is
+// Work unit = (sequence b, 64-token block), one wavefront; a workgroup holds
 // four consecutive blocks of one sequence. For a block that holds visible
 // tokens:
 //   1. gather it through block_table: lane l loads, for token tile tau (32
@@ -29,6 +29,9 @@
 #ifndef LOGITS_NB
 #define LOGITS_NB 1
 #endif
+#ifndef LOGITS_WGW
+#define LOGITS_WGW 4
+#endif
 #ifndef LOGITS_WPE
 #define LOGITS_WPE 6
 #endif
@@ -39,6 +42,8 @@ typedef int i8v __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr int kLogitsBlocks = LOGITS_NB;  // 64-token blocks per wave
+constexpr int kLogitsWaves = LOGITS_WGW;  // waves per workgroup
+constexpr int kLogitsThreads = 64 * kLogitsWaves;
 
 struct LogitsParams {
   void* out;
@@ -104,13 +109,14 @@ __device__ __forceinline__ void pin(T& v) {
   asm volatile("" : "+v"(v));
 }
 
-// A workgroup is 4 waves over 4 consecutive chunks of one sequence; NB =
-// 64-token KV blocks per wave (chunk = 64*NB tokens). The q rows of the
-// sequence are staged once per workgroup in LDS.
+// A workgroup is kLogitsWaves waves over as many consecutive chunks of one
+// sequence (4: 2 and 8 measured within a few percent); NB = 64-token KV blocks
+// per wave (chunk = 64*NB tokens). The q rows of the sequence are staged once
+// per workgroup in LDS.
 // OT: output element type (float, _Float16 or __bf16; conversions round to
 // nearest even).
 template <int NN, int H, int NB, typename OT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE))) void logits_kernel(
+__global__ __launch_bounds__(kLogitsThreads) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE))) void logits_kernel(
     LogitsParams p) {
   constexpr int D = 128, BS = 64;
   constexpr int CH = NB * BS;  // tokens per chunk
@@ -119,8 +125,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   constexpr int SFB = D / 32;  // scale bytes per token
   constexpr int BLK = BS * (ROWB + SFB);
   constexpr int QN = NN * H * ROWB / 16;  // 16-byte q pieces of the sequence
-  constexpr int QP = (QN + 255) / 256;    // q pieces per thread
-  static_assert(NN * H <= 256, "one scale word per thread");
+  constexpr int T = kLogitsThreads;
+  constexpr int QP = (QN + T - 1) / T;           // q pieces per thread
+  constexpr int SP = (NN * H + T - 1) / T;       // scale words and weights per thread
   __shared__ __attribute__((aligned(16))) uint8_t qlds[NN * H * ROWB];
   __shared__ int32_t sflds[NN * H];
   __shared__ __attribute__((aligned(16))) float wlds[NN * H];
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = blockIdx.x % p.ngroups, b = blockIdx.x / p.ngroups;
   const int L = p.context_lens[b];
-  const int t_grp = grp * 4 * CH;
+  const int t_grp = grp * kLogitsWaves * CH;
   const int t_chunk = t_grp + wave * CH;
   const bool grp_live = t_grp < L;  // some wave of the workgroup reads KV
   // blocks of this chunk inside max_context_len, and those holding visible tokens
@@ -143,17 +150,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   // (a wave with no visible block loads nothing: it only writes -inf columns)
   const int pg_lane = nvis > 0 ? trow[min(lane, nblk - 1)] : 0;
   u4 qv[QP];
-  int sfv = 0;
-  float wv = 0.f;
+  int sfv[SP];
+  float wv[SP];
   if (grp_live) {
 #pragma unroll
     for (int k = 0; k < QP; ++k)
-      if (tid + 256 * k < QN)
-        qv[k] = reinterpret_cast<const u4*>(p.q + (size_t)b * NN * H * ROWB)[tid + 256 * k];
-    if (tid < NN * H) {
-      sfv = p.sf_q[(size_t)b * NN * H + tid];
-      wv = p.w[(size_t)b * NN * H + tid];
-    }
+      if (tid + T * k < QN)
+        qv[k] = reinterpret_cast<const u4*>(p.q + (size_t)b * NN * H * ROWB)[tid + T * k];
+#pragma unroll
+    for (int k = 0; k < SP; ++k)
+      if (tid + T * k < NN * H) {
+        sfv[k] = p.sf_q[(size_t)b * NN * H + tid + T * k];
+        wv[k] = p.w[(size_t)b * NN * H + tid + T * k];
+      }
   }
 
   // ---- the FP4 rows and scale bytes of all blocks of the chunk: piece
@@ -199,13 +208,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOGITS_WPE)
   if (grp_live) {
 #pragma unroll
     for (int k = 0; k < QP; ++k)
-      if (tid + 256 * k < QN) reinterpret_cast<u4*>(qlds)[tid + 256 * k] = qv[k];
-    if (tid < NN * H) {
-      sflds[tid] = sfv;
-      wlds[tid] = p.epi == PA_LOGITS_F16    ? epi_round<PA_LOGITS_F16>(wv)
-                  : p.epi == PA_LOGITS_BF16 ? epi_round<PA_LOGITS_BF16>(wv)
-                                            : wv;
-    }
+      if (tid + T * k < QN) reinterpret_cast<u4*>(qlds)[tid + T * k] = qv[k];
+#pragma unroll
+    for (int k = 0; k < SP; ++k)
+      if (tid + T * k < NN * H) {
+        sflds[tid + T * k] = sfv[k];
+        wlds[tid + T * k] = p.epi == PA_LOGITS_F16    ? epi_round<PA_LOGITS_F16>(wv[k])
+                            : p.epi == PA_LOGITS_BF16 ? epi_round<PA_LOGITS_BF16>(wv[k])
+                                                      : wv[k];
+      }
   }
   __syncthreads();
   if (nvis == 0) return;
@@ -380,7 +391,7 @@ extern "C" pa_status paged_mqa_logits(const pa_logits_args* a, void* workspace,
   p.B = a->batch;
   p.max_blocks = a->max_blocks_per_seq;
   p.max_ctx = a->max_context_len;
-  p.ngroups = (int)ceil_div(a->max_context_len, 4 * 64 * kLogitsBlocks);
-  launch_timed(fn, dim3((unsigned)((int64_t)a->batch * p.ngroups)), dim3(256), s, p);
+  p.ngroups = (int)ceil_div(a->max_context_len, kLogitsWaves * 64 * kLogitsBlocks);
+  launch_timed(fn, dim3((unsigned)((int64_t)a->batch * p.ngroups)), dim3(kLogitsThreads), s, p);
   return launch_status("paged_mqa_logits kernel");
 }
