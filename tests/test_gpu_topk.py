@@ -41,6 +41,23 @@ def cases():
     x = np.zeros((2, 20000), np.float32)
     out.append(("all_equal_long", x, np.array([20000, 19000], np.int32), 1, 100))
     out.append(("sample_miss", sample_miss_row(20000), np.array([20000], np.int32), 1, 2048))
+    # k one below the row length, and k at half of it
+    x = rng.standard_normal((2, 5000)).astype(np.float32)
+    out.append(("k_near_L", x, np.array([5000, 5000], np.int32), 1, 4999))
+    out.append(("k_half", x.copy(), np.array([5000, 4000], np.int32), 1, 2500))
+    # half of a long row NaN: the k-th key may be NaN's (key 0)
+    x = rng.standard_normal((2, 20000)).astype(np.float32)
+    x[:, rng.random(20000) < 0.5] = np.nan
+    out.append(("nan_half", x, np.array([20000, 20000], np.int32), 1, 12000))
+    # the k-th value is 0 with +0 and -0 mixed among many zeros
+    x = np.concatenate([np.abs(rng.standard_normal((2, 3000))), np.zeros((2, 9000)),
+                        -np.abs(rng.standard_normal((2, 3000)))], axis=1).astype(np.float32)
+    x[:, 3000:12000:2] = -0.0
+    x = x[:, rng.permutation(15000)].copy()
+    out.append(("zero_threshold", x, np.array([15000, 14999], np.int32), 1, 7000))
+    # values on a few levels spread over the whole row (ties at T across waves)
+    x = rng.integers(-3, 4, (2, 30000)).astype(np.float32) * 0.25
+    out.append(("few_levels_long", x, np.array([30000, 29999], np.int32), 1, 9000))
     return out
 
 
@@ -61,7 +78,7 @@ def sample_miss_row(L):
     return x.reshape(1, L).copy()
 
 
-@pytest.mark.parametrize("idx", range(9))
+@pytest.mark.parametrize("idx", range(14))
 @pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
 def test_topk_bit_exact(pa, idx, fmt):
     name, x, lens, N, k = cases()[idx]
