@@ -505,16 +505,26 @@ def cpu_baseline(bench, budget_s):
         cores = oracle.threads()
         n = max(1, min(bench.units, int(budget_s * (0.7 * cores if threads == 0 else 1) /
                                         max(t1, 1e-6))))
+        reps = 1
         if threads == 1 and n == 1:
             dt, frac = t1, frac1
         else:
             t = time.perf_counter()
             frac = bench.oracle_sample(n)
             dt = time.perf_counter() - t
-        legs[name] = {"value": round(frac * bench.alg_bytes / dt / 1e9, 4), "unit": "GB/s",
+            # the whole workload well inside the budget: repeat it, so the
+            # timing is not that of one short run
+            if n == bench.units and dt < budget_s / 4:
+                reps = 1 + int(budget_s / 4 / max(dt, 1e-6))
+                t = time.perf_counter()
+                for _ in range(reps - 1):
+                    bench.oracle_sample(n)
+                dt += time.perf_counter() - t
+        legs[name] = {"value": round(reps * frac * bench.alg_bytes / dt / 1e9, 4), "unit": "GB/s",
                       "cores": cores, "kind": "oracle",
                       "sample": f"first {n} of {bench.units} {bench.unit_name} "
-                                f"({100 * frac:.2f}% of one call's work) in {dt:.1f} s"}
+                                f"({100 * frac:.2f}% of one call's work)"
+                                + (f", {reps} times" if reps > 1 else "") + f" in {dt:.1f} s"}
     oracle.set_threads(0)
     out = dict(legs["all"])
     out["single_thread"] = legs["single"]
