@@ -584,7 +584,7 @@ def main():
                     help="run only the 1 GiB copy kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the single-GPU path has no collectives or sharding", file=sys.stderr)
         sys.exit(2)
 

@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1,  /* a null pointer, a negative or inconsistent size */
-  PA_ERR_UNSUPPORTED = 2,  /* valid, but a shape/kind this build has no kernel for */
+  PA_ERR_UNSUPPORTED = 2,  /* valid, but a shape/kind the library has no kernel for */
   PA_ERR_PRECONDITION = 3, /* a documented precondition checked on the host failed */
   PA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than *_workspace_size() */
   PA_ERR_HIP = 5           /* a HIP launch failed */
