@@ -1,7 +1,8 @@
 """The indexer-to-attention chain -- kv_insert_mxfp4 -> paged_mqa_logits ->
-pa_topk_select -> paged_attn_sparse -- captured once in a HIP graph and
-replayed several times: every replay reproduces the eager chain bit for bit
-(the inserted cache bytes, the logits, the ids and the attention output),
+pa_topk_select -> paged_attn_sparse, with a kv_insert into an E4M3 cache
+beside it -- captured once in a HIP graph and replayed several times: every
+replay reproduces the eager chain bit for bit (the inserted cache bytes of
+both inserts, the logits, the ids and the attention output),
 with eager runs of the chain between the replays. The eager chain's logits
 and ids are also checked against the oracle's chain."""
 import numpy as np
@@ -49,8 +50,16 @@ def test_chain_graph_replay_matches_eager(pa):
     lws = torch.empty(max(lws_n, 1), dtype=torch.uint8, device="cuda")
     sws_n = pa.paged_attn_sparse_workspace_size(d.q, d.k, d.bt, T, at.kv_kind, k)
     sws = torch.empty(max(sws_n, 1), dtype=torch.uint8, device="cuda")
+    fins = W.insert_case(7104, T=200, Hkv=2, D=128, bs=16, kv_kind=W.KV_E4M3,
+                         scale_mode=W.SCALE_PER_TENSOR, value_scale=2.0)
+    kc0, vc0 = dev(fins.k_cache), dev(fins.v_cache)
+    kc, vc = kc0.clone(), vc0.clone()
+    ik, iv, isl = dev(fins.k), dev(fins.v), dev(fins.slot_mapping)
+    iks, ivs = dev(fins.k_scale), dev(fins.v_scale)
 
     def chain():
+        pa.kv_insert(kc, vc, ik, iv, isl, kv_kind=fins.kv_kind, k_scale=iks, v_scale=ivs,
+                     k_scale_mode=fins.scale_mode, v_scale_mode=fins.scale_mode)
         pa.kv_insert_mxfp4(kv, keys, slots)
         pa.paged_mqa_logits(q, sfq, kv, w, lens, btd, T, out=logits, workspace=lws)
         pa.topk_select(logits, lens, 2, k, sel=sel)
@@ -58,6 +67,8 @@ def test_chain_graph_replay_matches_eager(pa):
                              kv_kind=at.kv_kind, k_scale=d.ks, v_scale=d.vs, workspace=sws)
 
     def reset():
+        kc.copy_(kc0)
+        vc.copy_(vc0)
         kv.copy_(kv0)
         logits.fill_(float("nan"))
         sel.fill_(-7)
@@ -66,7 +77,8 @@ def test_chain_graph_replay_matches_eager(pa):
     def snapshot():
         torch.cuda.synchronize()
         return (kv.cpu().numpy().copy(), logits.cpu().numpy().view(np.uint32).copy(),
-                sel.cpu().numpy().copy(), out.cpu().numpy().view(np.uint16).copy())
+                sel.cpu().numpy().copy(), out.cpu().numpy().view(np.uint16).copy(),
+                kc.cpu().numpy().copy(), vc.cpu().numpy().copy())
 
     say("graph chain: eager")
     reset()
@@ -78,6 +90,11 @@ def test_chain_graph_replay_matches_eager(pa):
     lo = oracle.mqa_logits(lg.q, lg.sf_q, kv_o, lg.weights, np.array([T], np.int32), bt, T)
     assert np.array_equal(ref[1], lo.view(np.uint32))
     assert np.array_equal(ref[2], oracle.topk_select(lo, np.array([T], np.int32), 2, k))
+    ok_, ov_ = fins.k_cache.copy(), fins.v_cache.copy()
+    oracle.kv_insert(ok_, ov_, fins.kv_kind, fins.k, fins.v, fins.slot_mapping,
+                     k_scale=fins.k_scale, k_scale_mode=fins.scale_mode, v_scale=fins.v_scale,
+                     v_scale_mode=fins.scale_mode, block_size=fins.block_size)
+    assert np.array_equal(ref[4], ok_) and np.array_equal(ref[5], ov_)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -87,7 +104,8 @@ def test_chain_graph_replay_matches_eager(pa):
         with torch.cuda.graph(g, stream=s):
             chain()
     torch.cuda.current_stream().wait_stream(s)
-    names = ("cache bytes", "logits", "ids", "attention output")
+    names = ("MXFP4 cache bytes", "logits", "ids", "attention output", "E4M3 K cache bytes",
+             "E4M3 V cache bytes")
     for r in range(4):
         reset()
         torch.cuda.synchronize()
